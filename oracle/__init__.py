@@ -1,0 +1,133 @@
+"""fp64 CPU oracle for absorbed MLA decode over a paged latent KV cache.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline
+leg of the benchmark are the only callers. The product path (the HIP library
+and its binding) never imports this package, and this package imports nothing
+from the product path.
+
+The arithmetic lives in ``mla_oracle.c`` (plain C, fp64, one sequential loop
+per (request, head), OpenMP across them). This module builds it with gcc and
+marshals numpy arrays through ctypes. See the C file's header for what is
+computed and which passage of each page it follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "mla_oracle.c")
+LIBRARY = os.path.join(_HERE, "liboracle_mla.so")
+
+D_K = 576   # key width: 512 kv_c + 64 rope
+D_V = 512   # value width: kv_c
+
+_lib_cache: dict[str, ctypes.CDLL] = {}
+
+
+def build(source: str = SOURCE, output: str = LIBRARY) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math) into a shared library."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", "-Wall",
+           "-o", output, source, "-lm"]
+    subprocess.run(cmd, check=True)
+    return output
+
+
+def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.oracle_mla_attend.argtypes = [vp, vp, i32, ctypes.c_float, vp, vp, i64, i64, i64,
+                                      i64, i64, ctypes.c_float, vp, vp, vp, i64, vp, vp]
+    lib.oracle_mla_attend.restype = i32
+    lib.oracle_lse_merge.argtypes = [vp, vp, i64, i64, vp, vp]
+    lib.oracle_lse_merge.restype = i32
+    lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_double.restype = ctypes.c_double
+    lib.oracle_bf16_to_double.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_double.restype = ctypes.c_double
+    return lib
+
+
+def load(path: str = LIBRARY) -> "Oracle":
+    """Load (building first if absent) the oracle library at ``path``."""
+    if path not in _lib_cache:
+        if not os.path.exists(path):
+            if path != LIBRARY:
+                raise FileNotFoundError(path)
+            build()
+        _lib_cache[path] = _bind(ctypes.CDLL(path))
+    return Oracle(_lib_cache[path])
+
+
+def _ptr(a: np.ndarray) -> ctypes.c_void_p:
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+class Oracle:
+    """Thin numpy front end over one loaded copy of the C oracle."""
+
+    def __init__(self, lib: ctypes.CDLL):
+        self.lib = lib
+
+    def attend(self, q_bits, kv, block_table, seq_lens, block_size, scale,
+               kv_fp8=False, kv_scale=1.0, req=None, tok_begin=None, tok_end=None):
+        """Exact attention of (request, token range) items.
+
+        q_bits      uint16 [B, H, 576]: bf16 bit patterns
+        kv          uint16 [NB, bs, 576] bf16 bits, or uint8 E4M3FN codes if kv_fp8
+        block_table int32 [B, max_blocks]; seq_lens int32 [B]
+        req         int32 [n] request of each item (default: every request)
+        tok_begin/end int64 [n] token range per item (default: whole request)
+        Returns (out float64 [n, H, 512], lse float64 [n, H]).
+        """
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kv = np.ascontiguousarray(kv, dtype=np.uint8 if kv_fp8 else np.uint16)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        batch, num_heads, dk = q_bits.shape
+        if dk != D_K or kv.shape[-1] != D_K or kv.shape[1] != block_size:
+            raise ValueError("shape mismatch")
+        if req is None:
+            req = np.arange(batch, dtype=np.int32)
+        req = np.ascontiguousarray(req, dtype=np.int32)
+        n = req.shape[0]
+        if tok_begin is None:
+            tok_begin = np.zeros(n, dtype=np.int64)
+        if tok_end is None:
+            tok_end = seq_lens[req].astype(np.int64)
+        tok_begin = np.ascontiguousarray(tok_begin, dtype=np.int64)
+        tok_end = np.ascontiguousarray(tok_end, dtype=np.int64)
+        out = np.empty((n, num_heads, D_V), dtype=np.float64)
+        lse = np.empty((n, num_heads), dtype=np.float64)
+        rc = self.lib.oracle_mla_attend(
+            _ptr(q_bits), _ptr(kv), int(bool(kv_fp8)), float(kv_scale), _ptr(block_table),
+            _ptr(seq_lens), batch, num_heads, block_size, block_table.shape[1], kv.shape[0],
+            float(scale), _ptr(req), _ptr(tok_begin), _ptr(tok_end), n, _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError(f"oracle_mla_attend failed with status {rc}")
+        return out, lse
+
+    def lse_merge(self, part_out, part_lse):
+        """Merge normalised partials [S, H, 512] / [S, H] of one request."""
+        part_out = np.ascontiguousarray(part_out, dtype=np.float64)
+        part_lse = np.ascontiguousarray(part_lse, dtype=np.float64)
+        n_parts, num_heads = part_lse.shape
+        out = np.empty((num_heads, D_V), dtype=np.float64)
+        lse = np.empty((num_heads,), dtype=np.float64)
+        rc = self.lib.oracle_lse_merge(_ptr(part_out), _ptr(part_lse), n_parts, num_heads,
+                                       _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError(f"oracle_lse_merge failed with status {rc}")
+        return out, lse
+
+    def e4m3_to_double(self, codes):
+        codes = np.asarray(codes, dtype=np.uint8)
+        return np.array([self.lib.oracle_e4m3_to_double(int(c)) for c in codes.ravel()],
+                        dtype=np.float64).reshape(codes.shape)
+
+    def bf16_to_double(self, bits):
+        bits = np.asarray(bits, dtype=np.uint16)
+        return np.array([self.lib.oracle_bf16_to_double(int(c)) for c in bits.ravel()],
+                        dtype=np.float64).reshape(bits.shape)

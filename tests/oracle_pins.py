@@ -1,0 +1,344 @@
+"""Pins that tie the fp64 oracle to facts outside itself.
+
+Each pin checks the oracle against something it does not share code with:
+a library routine (torch's float64 scaled_dot_product_attention and logsumexp,
+torch's float8_e4m3fn and bfloat16 decoders, numpy's logaddexp), a closed form
+of softmax attention, or an invariant the pages fix (split-then-merge equals
+unsplit; zero-padding heads to 128 leaves the real heads alone; a physical
+block permutation under a matching table changes nothing).
+
+The same pins run against deliberately broken copies of the oracle source in
+``test_oracle_mutants.py``; every plausible mistake must trip at least one.
+
+Run as a script (``python tests/oracle_pins.py --lib PATH``) to check one
+library build: exit status 0 if every pin holds, 1 otherwise.
+"""
+from __future__ import annotations
+
+import argparse
+import math
+import os
+import sys
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+TOL = 1e-12
+S = workloads.SCALE
+
+
+def _bf16(x: torch.Tensor) -> torch.Tensor:
+    return x.to(torch.bfloat16)
+
+
+def _bits(x: torch.Tensor) -> np.ndarray:
+    return x.contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def _paged_from_dense(dense_list, block_size, gen, extra_blocks=0, poison=True):
+    """Scatter dense per-request [N_b, 576] bf16 rows into a shuffled page pool."""
+    nblk = [(d.shape[0] + block_size - 1) // block_size for d in dense_list]
+    pool = sum(nblk) + extra_blocks
+    perm = torch.randperm(pool, generator=gen)
+    max_blocks = max(1, max(nblk))
+    table = torch.full((len(dense_list), max_blocks), -1, dtype=torch.int32)
+    kv = torch.full((pool, block_size, 576), float("nan"), dtype=torch.bfloat16)
+    if not poison:
+        kv = _bf16(torch.randn((pool, block_size, 576), generator=gen))
+    off = 0
+    for b, d in enumerate(dense_list):
+        for j in range(nblk[b]):
+            blk = int(perm[off + j])
+            table[b, j] = blk
+            rows = d[j * block_size:(j + 1) * block_size]
+            kv[blk, :rows.shape[0]] = rows
+        off += nblk[b]
+    seq = torch.tensor([d.shape[0] for d in dense_list], dtype=torch.int32)
+    return kv, table, seq
+
+
+def _sdpa64(q_bf16: torch.Tensor, k_bf16: torch.Tensor, scale: float):
+    """Library reference for one request: q [H, 576], k [N, 576] -> out [H, 512], lse [H]."""
+    q = q_bf16.to(torch.float64)[None, :, None, :]            # [1, H, 1, 576]
+    k = k_bf16.to(torch.float64)[None, None, :, :].expand(1, q.shape[1], -1, -1)
+    v = k[..., :512]
+    out = torch.nn.functional.scaled_dot_product_attention(q, k, v, scale=scale)[0, :, 0, :]
+    logits = scale * (q_bf16.to(torch.float64) @ k_bf16.to(torch.float64).T)
+    return out.numpy(), torch.logsumexp(logits, dim=-1).numpy()
+
+
+def _close(a, b, tol=TOL):
+    a, b = np.asarray(a), np.asarray(b)
+    return a.shape == b.shape and bool(np.all(np.abs(a - b) <= tol * (1 + np.abs(b))))
+
+
+# --------------------------------------------------------------------------- pins
+
+def pin_e4m3_decode(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = orc.e4m3_to_double(codes)
+    nan = np.isnan(ref)
+    assert (np.isnan(got) == nan).all(), "E4M3 NaN codes differ"
+    assert (got[~nan] == ref[~nan]).all(), "E4M3 decode differs from torch float8_e4m3fn"
+
+
+def pin_bf16_widen(orc):
+    gen = torch.Generator().manual_seed(11)
+    x = _bf16(torch.randn(4096, generator=gen) * 100)
+    got = orc.bf16_to_double(_bits(x))
+    assert (got == x.to(torch.float64).numpy()).all(), "bf16 widening differs from torch"
+
+
+def pin_sdpa_identity_table(orc):
+    """One request, pages in order: equals float64 SDPA with Eq=576, Ev=512."""
+    gen = torch.Generator().manual_seed(1)
+    H, N, bs = 5, 45, 16
+    q = _bf16(torch.randn((1, H, 576), generator=gen))
+    k = _bf16(torch.randn((N, 576), generator=gen))
+    nb = (N + bs - 1) // bs
+    kv = _bf16(torch.randn((nb * bs, 576), generator=gen))
+    kv[:N] = k
+    table = torch.arange(nb, dtype=torch.int32)[None]
+    out, lse = orc.attend(_bits(q), _bits(kv.view(nb, bs, 576)), table.numpy(),
+                          np.array([N], np.int32), bs, S)
+    ref_out, ref_lse = _sdpa64(q[0], k, S)
+    assert _close(out[0], ref_out), "out differs from float64 SDPA"
+    assert _close(lse[0], ref_lse), "lse differs from float64 logsumexp"
+
+
+def pin_sdpa_shuffled_pages(orc):
+    """Ragged requests scattered over shuffled pages (unused slots NaN) equal dense SDPA."""
+    gen = torch.Generator().manual_seed(2)
+    H = 3
+    for bs in (16, 32, 64):
+        lens = [1, 15, 16, 17, 70, 131]
+        dense = [_bf16(torch.randn((n, 576), generator=gen)) for n in lens]
+        kv, table, seq = _paged_from_dense(dense, bs, gen, extra_blocks=3)
+        q = _bf16(torch.randn((len(lens), H, 576), generator=gen))
+        out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+        for b in range(len(lens)):
+            ref_out, ref_lse = _sdpa64(q[b], dense[b], S)
+            assert _close(out[b], ref_out), f"paged out differs (bs={bs}, b={b})"
+            assert _close(lse[b], ref_lse), f"paged lse differs (bs={bs}, b={b})"
+
+
+def pin_closed_forms(orc):
+    gen = torch.Generator().manual_seed(3)
+    H, bs = 4, 16
+    # N = 1: out is the single value row, lse its logit.
+    q = _bf16(torch.randn((1, H, 576), generator=gen))
+    k = _bf16(torch.randn((1, 576), generator=gen))
+    kv, table, seq = _paged_from_dense([k], bs, gen)
+    out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+    v0 = k[0, :512].to(torch.float64).numpy()
+    x0 = S * (q[0].to(torch.float64) @ k[0].to(torch.float64)).numpy()
+    assert (out[0] == v0[None, :]).all(), "N=1: out must equal v_0 exactly"
+    assert _close(lse[0], x0), "N=1: lse must equal the logit"
+    # q = 0: uniform weights, out = mean of value rows, lse = ln N.
+    N = 29
+    k = _bf16(torch.randn((N, 576), generator=gen))
+    kv, table, seq = _paged_from_dense([k], bs, gen)
+    qz = torch.zeros((1, H, 576), dtype=torch.bfloat16)
+    out, lse = orc.attend(_bits(qz), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+    mean = k[:, :512].to(torch.float64).mean(0).numpy()
+    assert _close(out[0], np.broadcast_to(mean, (H, 512))), "q=0: out must be the mean row"
+    assert _close(lse[0], np.full(H, math.log(N))), "q=0: lse must be ln N"
+    # Equal kv_c rows (rope random): out = that row for any q.
+    c = _bf16(torch.randn((576,), generator=gen))
+    k = _bf16(torch.randn((N, 576), generator=gen))
+    k[:, :512] = c[:512]
+    kv, table, seq = _paged_from_dense([k], bs, gen)
+    q = _bf16(torch.randn((1, H, 576), generator=gen))
+    out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+    assert _close(out[0], np.broadcast_to(c[:512].to(torch.float64).numpy(), (H, 512))), \
+        "equal value rows: out must equal that row"
+    # All 576-wide rows equal: lse = x + ln N.
+    k = c[None, :].expand(N, 576).contiguous()
+    kv, table, seq = _paged_from_dense([k], bs, gen)
+    out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+    x = S * (q[0].to(torch.float64) @ c.to(torch.float64)).numpy()
+    assert _close(lse[0], x + math.log(N)), "equal rows: lse must be x + ln N"
+    # N = 2: out = sigmoid(x0 - x1) v0 + sigmoid(x1 - x0) v1.
+    k = _bf16(torch.randn((2, 576), generator=gen) * 0.3)
+    kv, table, seq = _paged_from_dense([k], bs, gen)
+    out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+    k64 = k.to(torch.float64).numpy()
+    x = S * (q[0].to(torch.float64).numpy() @ k64.T)            # [H, 2]
+    sig = 1.0 / (1.0 + np.exp(-(x[:, 0] - x[:, 1])))
+    ref = sig[:, None] * k64[0, :512] + (1 - sig)[:, None] * k64[1, :512]
+    assert _close(out[0], ref), "N=2 closed form"
+    assert _close(lse[0], np.logaddexp(x[:, 0], x[:, 1])), "N=2 lse = logaddexp(x0, x1)"
+
+
+def pin_empty_request(orc):
+    gen = torch.Generator().manual_seed(4)
+    q = _bf16(torch.randn((2, 2, 576), generator=gen))
+    k = _bf16(torch.randn((5, 576), generator=gen))
+    kv, table, _ = _paged_from_dense([k, k], 16, gen)
+    out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), np.array([0, 5], np.int32),
+                          16, S)
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all(), "empty request: out 0, lse -inf"
+    assert np.isfinite(lse[1]).all()
+
+
+def pin_split_merge(orc):
+    """Any partition into contiguous ranges, merged by LSE, equals the unsplit result."""
+    wl = workloads.make_workload(batch=3, num_heads=4, seq=("fixed", [1, 77, 200]),
+                                 block_size=16, seed=5, poison=True)
+    args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(),
+            wl.block_size, wl.scale)
+    full_out, full_lse = orc.attend(*args)
+    rng = np.random.default_rng(5)
+    for b in range(wl.batch):
+        n = int(wl.seq_lens[b])
+        for n_parts in (1, 2, 3, 7):
+            cuts = np.sort(rng.integers(0, n + 1, size=n_parts - 1))
+            edges = np.concatenate([[0], cuts, [n]]).astype(np.int64)
+            req = np.full(n_parts, b, np.int32)
+            po, pl = orc.attend(*args, req=req, tok_begin=edges[:-1], tok_end=edges[1:])
+            mo, ml = orc.lse_merge(po, pl)
+            assert _close(mo, full_out[b]), f"split-merge out (b={b}, parts={n_parts})"
+            assert _close(ml, full_lse[b]), f"split-merge lse (b={b}, parts={n_parts})"
+
+
+def pin_merge_closed_form(orc):
+    rng = np.random.default_rng(6)
+    po = rng.standard_normal((3, 2, 512))
+    pl = np.array([[0.5, -np.inf], [2.0, -np.inf], [-np.inf, -np.inf]])
+    out, lse = orc.lse_merge(po, pl)
+    w0, w1 = 1 / (1 + math.exp(1.5)), 1 / (1 + math.exp(-1.5))
+    assert _close(lse[0], np.logaddexp(0.5, 2.0)), "merge lse = logaddexp"
+    assert _close(out[0], w0 * po[0, 0] + w1 * po[1, 0]), "merge weights = softmax(lse)"
+    assert (out[1] == 0).all() and np.isneginf(lse[1]), "all-empty merge: out 0, lse -inf"
+
+
+def pin_rope_shift(orc):
+    """A rope vector shared by every key shifts all logits equally: out unchanged,
+    lse moves by scale * <q_rope, r>."""
+    gen = torch.Generator().manual_seed(7)
+    H, N, bs = 4, 50, 16
+    k = _bf16(torch.randn((N, 576), generator=gen))
+    r = _bf16(torch.randn((64,), generator=gen))
+    k0 = k.clone()
+    k0[:, 512:] = 0
+    k1 = k.clone()
+    k1[:, 512:] = r
+    q = _bf16(torch.randn((1, H, 576), generator=gen))
+    res = []
+    for kk in (k0, k1):
+        kv, table, seq = _paged_from_dense([kk], bs, torch.Generator().manual_seed(8))
+        res.append(orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S))
+    shift = S * (q[0, :, 512:].to(torch.float64) @ r.to(torch.float64)).numpy()
+    assert _close(res[1][0], res[0][0]), "shared rope vector must not change out"
+    assert _close(res[1][1][0], res[0][1][0] + shift), "shared rope vector shifts lse"
+
+
+def pin_head_padding(orc):
+    """Zero-padding heads to 128 leaves the real heads bitwise unchanged; the padded
+    heads give the uniform-weight closed form."""
+    wl = workloads.make_workload(batch=2, num_heads=16, seq=("fixed", [37, 130]),
+                                 block_size=16, seed=9)
+    args = (wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(), wl.block_size,
+            wl.scale)
+    out16, lse16 = orc.attend(wl.q_bits(), *args)
+    q128 = torch.zeros((2, 128, 576), dtype=torch.bfloat16)
+    q128[:, :16] = wl.q
+    out128, lse128 = orc.attend(_bits(q128), *args)
+    assert (out128[:, :16] == out16).all() and (lse128[:, :16] == lse16).all(), \
+        "padding heads changed the real heads"
+    for b in range(2):
+        n = int(wl.seq_lens[b])
+        rows = []
+        for t in range(n):
+            blk = int(wl.block_table[b, t // 16])
+            rows.append(wl.kv[blk, t % 16, :512].to(torch.float64).numpy())
+        mean = np.mean(rows, axis=0)
+        assert _close(out128[b, 16:], np.broadcast_to(mean, (112, 512))), "padded heads: mean"
+        assert _close(lse128[b, 16:], np.full(112, math.log(n))), "padded heads: ln N"
+
+
+def pin_block_permutation(orc):
+    """Permuting the physical pool under a matching table leaves results bitwise equal."""
+    wl = workloads.make_workload(batch=3, num_heads=4, seq=("fixed", [5, 64, 100]),
+                                 block_size=16, seed=10, pool_blocks=14)
+    out_a, lse_a = orc.attend(wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(),
+                              wl.seq_lens.numpy(), 16, wl.scale)
+    perm = torch.randperm(wl.num_blocks, generator=torch.Generator().manual_seed(10))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(wl.num_blocks)
+    kv_p = wl.kv[perm]                       # new block j holds old block perm[j]
+    table = wl.block_table.clone()
+    valid = table >= 0
+    table[valid] = inv[table[valid].long()].to(torch.int32)
+    out_b, lse_b = orc.attend(wl.q_bits(), _bits(kv_p), table.numpy(), wl.seq_lens.numpy(),
+                              16, wl.scale)
+    assert (out_a == out_b).all() and (lse_a == lse_b).all(), "block permutation changed results"
+
+
+def pin_batch_independence(orc):
+    wl = workloads.make_workload(batch=3, num_heads=4, seq=("fixed", [40, 64, 100]),
+                                 block_size=16, seed=12)
+    args = (wl.kv_bits(), wl.block_table.numpy(), wl.block_size, wl.scale)
+    out_a, lse_a = orc.attend(wl.q_bits(), args[0], args[1], wl.seq_lens.numpy(), *args[2:])
+    q2 = wl.q.clone()
+    q2[1:] = _bf16(torch.randn(q2[1:].shape, generator=torch.Generator().manual_seed(1)))
+    seq2 = wl.seq_lens.clone()
+    seq2[1:] = torch.tensor([3, 99], dtype=torch.int32)
+    out_b, lse_b = orc.attend(_bits(q2), args[0], args[1], seq2.numpy(), *args[2:])
+    assert (out_a[0] == out_b[0]).all() and (lse_a[0] == lse_b[0]).all(), \
+        "request 0 depends on other requests"
+
+
+def pin_fp8_dequant(orc):
+    """E4M3 cache with a per-tensor scale equals float64 SDPA on the dequantised rows."""
+    wl = workloads.make_workload(batch=2, num_heads=4, seq=("fixed", [20, 90]), block_size=16,
+                                 seed=13, kv_dtype="fp8")
+    out, lse = orc.attend(wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(),
+                          wl.seq_lens.numpy(), 16, wl.scale, kv_fp8=True,
+                          kv_scale=wl.kv_scale)
+    deq = wl.kv.view(torch.float8_e4m3fn).to(torch.float64) * wl.kv_scale
+    for b in range(2):
+        n = int(wl.seq_lens[b])
+        rows = torch.stack([deq[int(wl.block_table[b, t // 16]), t % 16] for t in range(n)])
+        q = wl.q[b].to(torch.float64)[None, :, None, :]
+        kk = rows[None, None].expand(1, 4, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            q, kk, kk[..., :512], scale=wl.scale)[0, :, 0].numpy()
+        ref_lse = torch.logsumexp(wl.scale * (wl.q[b].to(torch.float64) @ rows.T), -1).numpy()
+        assert _close(out[b], ref), f"fp8 out differs from SDPA on dequantised rows (b={b})"
+        assert _close(lse[b], ref_lse), f"fp8 lse differs (b={b})"
+
+
+PINS = [pin_e4m3_decode, pin_bf16_widen, pin_sdpa_identity_table, pin_sdpa_shuffled_pages,
+        pin_closed_forms, pin_empty_request, pin_split_merge, pin_merge_closed_form,
+        pin_rope_shift, pin_head_padding, pin_block_permutation, pin_batch_independence,
+        pin_fp8_dequant]
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--lib", required=True)
+    args = ap.parse_args(argv)
+    import oracle
+    orc = oracle.load(args.lib)
+    failed = []
+    for pin in PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError) as e:
+            failed.append(f"{pin.__name__}: {e}")
+    for f in failed:
+        print("FAIL", f)
+    print(f"{len(PINS) - len(failed)}/{len(PINS)} pins hold")
+    return 1 if failed else 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,62 @@
+"""Plant plausible mistakes in a copy of the oracle source; the pins must catch each.
+
+Every mutant is compiled from a textual edit of ``oracle/mla_oracle.c`` into a
+temporary library and checked by ``oracle_pins.py`` in a child process (so a
+mutant that crashes cannot take the test run down). A mutant passes every pin
+only if the pins are blind to that mistake, which fails this test.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+# (name, text in mla_oracle.c, replacement)
+MUTANTS = [
+    ("slot_index_swapped", "* block_size +\n                    t % block_size;\n      load_token(kv_cache, kv_fp8, kvs, row, k);\n      double dot",
+     "* block_size +\n                    (t + 1) % block_size;\n      load_token(kv_cache, kv_fp8, kvs, row, k);\n      double dot"),
+    ("page_index_off_by_one", "block_table[b * max_blocks + t / block_size] * block_size +\n                    t % block_size;\n      load_token(kv_cache, kv_fp8, kvs, row, k);\n      double wt",
+     "block_table[b * max_blocks + (t + 1) / block_size] * block_size +\n                    t % block_size;\n      load_token(kv_cache, kv_fp8, kvs, row, k);\n      double wt"),
+    ("rope_dropped", "for (int d = 0; d < ORACLE_D; ++d) dot += qv[d] * k[d];",
+     "for (int d = 0; d < ORACLE_DV; ++d) dot += qv[d] * k[d];"),
+    ("values_from_rope_side", "o[d] += wt * k[d];", "o[d] += wt * k[d + 64];"),
+    ("scale_dropped", "x[t - t0] = s * dot;", "x[t - t0] = dot;"),
+    ("weight_sign", "exp(x[t - t0] - m)", "exp(m - x[t - t0])"),
+    ("lse_log2", "lse[i * num_heads + h] = m + log(l);", "lse[i * num_heads + h] = m + log2(l);"),
+    ("lse_missing_max", "lse[i * num_heads + h] = m + log(l);", "lse[i * num_heads + h] = log(l);"),
+    ("no_normalise", "for (int d = 0; d < ORACLE_DV; ++d) o[d] /= l;", ""),
+    ("q_head_batch_transposed", "q[(b * num_heads + h) * ORACLE_D + d]",
+     "q[((h % batch) * num_heads + (b % num_heads)) * ORACLE_D + d]"),
+    ("e4m3_bias", "exponent - 7);", "exponent - 8);"),
+    ("e4m3_subnormal", "ldexp((double)mantissa / 8.0, -6)", "ldexp((double)mantissa / 8.0, -7)"),
+    ("kv_scale_dropped", "oracle_e4m3_to_double(p[d]) * kv_scale;", "oracle_e4m3_to_double(p[d]);"),
+    ("merge_weight_sign", "double w = exp(ls - M);", "double w = exp(M - ls);"),
+    ("merge_unnormalised", "for (int d = 0; d < ORACLE_DV; ++d) o[d] /= wsum;", ""),
+    ("tail_overread", "int64_t t1 = tok_end[i] > n ? n : tok_end[i];\n    double* o",
+     "int64_t t1 = tok_end[i] > n ? n : tok_end[i];\n    if (t1 == n && t1 % block_size) t1 = (t1 / block_size + 1) * block_size;\n    double* o"),
+]
+
+
+def test_mutant_list_applies():
+    src = open(oracle.SOURCE).read()
+    for name, old, _ in MUTANTS:
+        assert src.count(old) >= 1, f"mutant {name} no longer matches the oracle source"
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(tmp_path, name, old, new):
+    src = open(oracle.SOURCE).read()
+    assert old in src
+    mutated = src.replace(old, new, 1)
+    c_path = tmp_path / f"{name}.c"
+    c_path.write_text(mutated)
+    lib = tmp_path / f"lib{name}.so"
+    oracle.build(str(c_path), str(lib))
+    env = dict(os.environ, OMP_NUM_THREADS="2")
+    r = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), "--lib", str(lib)],
+                       capture_output=True, text=True, timeout=300, env=env)
+    assert r.returncode != 0, f"no pin caught mutant {name}:\n{r.stdout}\n{r.stderr}"
