@@ -1,0 +1,236 @@
+"""Benchmark of absorbed MLA paged-KV decode on one MI355X.
+
+One step = one mla_decode call (split plan + attention + LSE combine) over the
+whole synthetic batch, inputs already resident in HBM. Default workload: the
+DeepSeek-R1 one-GPU share at 8-way tensor parallelism (batch 512, 16 heads,
+seq_lens U[1024, 3072], block 32, bf16 cache), the configuration the headline
+metric is quoted on.
+
+Prints ONE JSON line: µs per call (value), the attention kernel's achieved
+algorithmic HBM bandwidth against the 8 TB/s peak (roofline), and the fp64
+CPU oracle timed on a bounded sample of the same workload (cpu_baseline).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
+PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}
+MALL_BYTES = 256 << 20          # memory-side cache; smaller pools are rotated
+ROTATE_MIN_BYTES = 1 << 30
+KERNEL_SOURCES = [os.path.join(ROOT, "mla_paged_attention_amd", "csrc", f)
+                  for f in ("mla_kernels.hip", "mla_internal.h")]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+D_K, D_V = 576, 512
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(wl) -> int:
+    """Bytes a decode call must move at least once: the cache rows of every
+    token, q, out, lse, the used block-table entries and seq_lens."""
+    e_kv = 1 if wl.kv_dtype == "fp8" else 2
+    n_tok = wl.total_tokens
+    nblk = sum((int(n) + wl.block_size - 1) // wl.block_size for n in wl.seq_lens)
+    b, h = wl.batch, wl.num_heads
+    return (n_tok * D_K * e_kv + b * h * D_K * 2 + b * h * D_V * 2 + b * h * 4 + nblk * 4
+            + b * 4)
+
+
+def algorithmic_flops(wl) -> int:
+    """Logits (2 * 576) and P.V (2 * 512) multiply-adds per head and token."""
+    return 2 * (D_K + D_V) * wl.num_heads * wl.total_tokens
+
+
+def cpu_baseline(wl, target_s: float) -> dict:
+    """Time the fp64 oracle on a bounded prefix of the requests."""
+    import numpy as np
+
+    import oracle
+    orc = oracle.load()
+    lens = wl.seq_lens.numpy().astype(np.int64)
+    args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(),
+            wl.block_size, wl.scale)
+    kw = dict(kv_fp8=wl.kv_dtype == "fp8", kv_scale=wl.kv_scale)
+    n_probe = min(wl.batch, 4)
+    t0 = time.perf_counter()
+    orc.attend(*args, req=np.arange(n_probe, dtype=np.int32), **kw)
+    probe = time.perf_counter() - t0
+    per_tok = probe / max(1, lens[:n_probe].sum())
+    want_tok = target_s / max(per_tok, 1e-12)
+    n_req = int(np.searchsorted(np.cumsum(lens), want_tok) + 1)
+    n_req = max(n_probe, min(wl.batch, n_req))
+    t0 = time.perf_counter()
+    orc.attend(*args, req=np.arange(n_req, dtype=np.int32), **kw)
+    dt = time.perf_counter() - t0
+    tok = int(lens[:n_req].sum())
+    full_s = dt * wl.total_tokens / tok
+    threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
+    return {"value": round(full_s * 1e6, 1), "unit": "us/call", "cores": threads,
+            "kind": "oracle",
+            "sample": (f"first {n_req} of {wl.batch} requests ({tok} of {wl.total_tokens} "
+                       f"tokens, all heads) in {dt:.2f} s, scaled to the whole batch"),
+            "tokens_per_s": round(tok / dt, 1)}
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="r1tp8")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the decode path "
+                                   "has no multi-GPU mode (heads shard across GPUs with no "
+                                   "exchange inside attention)", "n_gpus": args.gpus}))
+        return 2
+
+    import torch
+
+    import mla_paged_attention_amd as mla
+    import workloads
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        return 1
+    mla.library()  # fail loudly now if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    log(f"generating workload {args.config}")
+    wl = workloads.make_config(args.config)
+    cfg = workloads.CONFIGS[args.config]
+    pool_bytes = wl.kv.numel() * wl.kv.element_size()
+    copies = 1 if pool_bytes >= 2 * MALL_BYTES else max(4, math.ceil(ROTATE_MIN_BYTES / pool_bytes))
+    q, bt, sl = wl.q.to(dev), wl.block_table.to(dev), wl.seq_lens.to(dev)
+    kvs = [wl.kv.to(dev) for _ in range(copies)]
+    out = torch.empty((wl.batch, wl.num_heads, D_V), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((wl.batch, wl.num_heads), dtype=torch.float32, device=dev)
+    nbytes = mla.get_workspace_size(wl.batch, wl.num_heads, wl.max_blocks * wl.block_size,
+                                    args.num_splits, 0)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"tokens={wl.total_tokens} pool={pool_bytes / 2**20:.0f} MiB copies={copies} "
+        f"workspace={nbytes / 2**20:.1f} MiB")
+
+    def call(i, events=None):
+        mla.decode(q, kvs[i % copies], bt, sl, scale=wl.scale, num_splits=args.num_splits,
+                   kv_scale=wl.kv_scale, out=out, lse=lse, workspace=ws, stream=stream,
+                   events=events)
+
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+    log(f"warmup done ({args.warmup} calls)")
+
+    # Timed region 1: K plain calls.
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        call(i)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    log(f"timed {args.steps} calls: {ms_per_step * 1e3:.1f} us/call (wall {wall * 1e3 / args.steps:.1f})")
+
+    # Timed region 2: K calls with HIP events around each kernel (same stream).
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for row in evs:
+        for e in row:
+            e.record(stream)  # create the underlying HIP events
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        call(i, events=evs[i])
+    torch.cuda.synchronize()
+    attn_ms = [r[1].elapsed_time(r[2]) for r in evs]
+    plan_ms = [r[0].elapsed_time(r[1]) for r in evs]
+    comb_ms = [r[2].elapsed_time(r[3]) for r in evs]
+    tot_ms = [r[0].elapsed_time(r[3]) for r in evs]
+    attn_avg = statistics.fmean(attn_ms)
+    log(f"attention kernel {attn_avg * 1e3:.1f} us avg, plan {statistics.fmean(plan_ms) * 1e3:.1f},"
+        f" combine {statistics.fmean(comb_ms) * 1e3:.1f}")
+
+    alg_bytes = algorithmic_bytes(wl)
+    alg_flops = algorithmic_flops(wl)
+    achieved = alg_bytes / (attn_avg * 1e-3) / 1e9
+    mfma_peak = PEAK_MFMA_TFLOPS["fp8" if wl.kv_dtype == "fp8" else "bf16"]
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        entry = t.get(args.config)
+        if entry and entry.get("kernel_hash") == kernel_source_hash():
+            traffic = entry.get("bytes_per_launch")
+
+    result = {
+        "metric": "MLA decode us/call + achieved HBM GB/s & MFMA % at bs=512, 16 heads",
+        "value": round(ms_per_step * 1e3, 2),
+        "unit": "us/call",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8" if wl.kv_dtype == "fp8" else "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.config, "batch": wl.batch, "num_heads": wl.num_heads,
+                   "seq_lens": list(cfg["seq"]) if cfg["seq"][0] != "fixed" else
+                   sorted(set(cfg["seq"][1])), "total_tokens": wl.total_tokens,
+                   "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
+                   "num_splits": args.num_splits or "auto", "parallelism": "single-gpu"},
+        "tokens_per_s": round(wl.total_tokens / (ms_per_step * 1e-3), 1),
+        "hbm_GBps_algorithmic": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "mfma_pct": round(100 * alg_flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak, 2),
+        "kernels_us": {"plan": round(statistics.fmean(plan_ms) * 1e3, 2),
+                       "attention": round(attn_avg * 1e3, 2),
+                       "combine": round(statistics.fmean(comb_ms) * 1e3, 2),
+                       "call_with_events": round(statistics.fmean(tot_ms) * 1e3, 2),
+                       "attention_p10_p90": [round(sorted(attn_ms)[len(attn_ms) // 10] * 1e3, 2),
+                                             round(sorted(attn_ms)[(9 * len(attn_ms)) // 10] * 1e3, 2)]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
+                     "traffic": traffic, "kernel": "mla::attn_kernel<0>",
+                     "algorithmic_bytes_per_launch": alg_bytes,
+                     "mfma_frac": round(alg_flops / (attn_avg * 1e-3) / 1e12 / mfma_peak, 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the fp64 oracle on a sample")
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

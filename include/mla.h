@@ -1,0 +1,182 @@
+/*
+ * mla.h -- C ABI of libmla_mi355x.so: absorbed Multi-head Latent Attention
+ * (MLA) decode over a paged latent KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. One query token per request (PR #20769 "SM100 Cutlass
+ * MLA decode with unrestricted num_heads (< 128) for DeepSeek TP", review of
+ * ensure_size: max_query_len = 1, batch_size = num_decodes). Every cached
+ * token is a 576-wide latent row: columns 0..511 are kv_c, 512..575 the rope
+ * part. For request b with N = seq_lens[b] tokens and head h:
+ *
+ *     x_t      = scale * <q[b][h][0:576], K_t[0:576]>         t < N
+ *     out[b][h] = sum_t exp(x_t) K_t[0:512] / sum_t exp(x_t)   (V = kv_c)
+ *     lse[b][h] = ln(sum_t exp(x_t))                           (natural log)
+ *
+ * where K_t is row (t mod block_size) of physical block
+ * block_table[b][t / block_size] (paged cache: PR #21078 "Flashinfer MLA
+ * (trtllm-gen) decode kernel integration", E2E command --block-size 32).
+ * The KV length is split across workgroups and the normalised partials are
+ * merged by log-sum-exp (PR #20769, summary of changes: split KV across
+ * multiple blocks/SMs plus a reduction kernel that combines the results).
+ * Any head count 1..128 is accepted (PR #20769: num_heads below 128 is what
+ * lets tensor parallelism shard heads); no padding to 128 is required.
+ *
+ * Conventions shared by every entry point:
+ *  - All data pointers are caller-owned DEVICE memory on the current HIP
+ *    device. The library never allocates, frees, or retains pointers, and
+ *    keeps no mutable global state (PR #20769 review: a module-global
+ *    workspace is not thread-safe; the workspace is per caller).
+ *  - Every call enqueues on `stream` (a hipStream_t; NULL = the null stream)
+ *    and returns without synchronising. A returned MLA_OK covers argument
+ *    validation and launch only.
+ *  - Arguments are validated before any HIP call, so every MLA_ERR_INVALID_ARG
+ *    path is observable on a machine without a GPU. Then: no usable device ->
+ *    MLA_ERR_NO_DEVICE; a device other than gfx950 -> MLA_ERR_UNSUPPORTED
+ *    (every symbol is always exported; PR #20769 timeline: an undefined
+ *    workspace-size symbol broke import on other GPUs).
+ *  - Unsupported configurations are reported, never silently changed.
+ *  - No C++ exception crosses this boundary.
+ */
+#ifndef MLA_MI355X_H
+#define MLA_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MLA_HEAD_DIM_K 576   /* key width: 512 kv_c + 64 rope */
+#define MLA_HEAD_DIM_V 512   /* value width: kv_c */
+#define MLA_MAX_HEADS 128
+#define MLA_MAX_FORCED_SPLITS 16
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, out-of-range size */
+  MLA_ERR_UNSUPPORTED = -2,        /* valid request this build does not serve */
+  MLA_ERR_WORKSPACE_TOO_SMALL = -3,
+  MLA_ERR_NO_DEVICE = -4,
+  MLA_ERR_HIP = -5                 /* a HIP runtime call or launch failed */
+} mla_status_t;
+
+typedef enum {
+  MLA_KV_BF16 = 0,
+  MLA_KV_FP8_E4M3 = 1  /* OCP E4M3FN codes times one per-tensor fp32 scale */
+} mla_kv_dtype_t;
+
+/*
+ * Workspace bytes that mla_decode needs (the analogue of the workspace-size
+ * query with four 64-bit arguments in PR #20769, workspace sizing snippet).
+ * Pure host arithmetic: no HIP call, works without a GPU.
+ *
+ *  batch        number of decode requests (>= 0)
+ *  num_heads    1..128
+ *  max_seq_len  upper bound on any seq_len; mla_decode itself checks against
+ *               max_blocks_per_seq * block_size, so pass that product
+ *  num_splits   0 = automatic scheduling; 1..16 = that many splits per request
+ *  num_cus      compute units to plan for; <= 0 means 256 (MI355X)
+ *
+ * Returns 0 when an argument is out of range.
+ */
+size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_len,
+                              int64_t num_splits, int64_t num_cus);
+
+/*
+ * mla_decode: out, lse <- attention of q over the paged cache (formula above).
+ *
+ *  q            [batch][num_heads][576] bf16, contiguous, 16-byte aligned
+ *  kv_cache     [num_blocks][block_size][576] bf16 (MLA_KV_BF16) or uint8
+ *               E4M3FN codes (MLA_KV_FP8_E4M3), contiguous, 16-byte aligned
+ *  block_table  [batch][max_blocks_per_seq] int32 physical block ids; entries
+ *               past ceil(seq_lens[b] / block_size) are never read
+ *  seq_lens     [batch] int32, 0 <= seq_lens[b] <= max_blocks_per_seq *
+ *               block_size. A request with seq_len 0 gets out = 0,
+ *               lse = -inf. Lengths beyond the table capacity are clamped to
+ *               it, and block ids outside [0, num_blocks) are skipped (their
+ *               tokens contribute nothing): the result of such a request is
+ *               then not meaningful, but nothing outside the cache is read.
+ *  out          [batch][num_heads][512] bf16 (fp32 accumulation, round to
+ *               nearest even), 16-byte aligned, fully overwritten
+ *  lse          [batch][num_heads] fp32 natural-log LSE of the scaled logits,
+ *               or NULL if not wanted
+ *  scale        logit scale applied to q.k (finite)
+ *  num_heads    1..128
+ *  block_size   16, 32, 64 or 128 tokens per physical block
+ *  num_splits   0 = automatic: the KV of all requests is cut into balanced
+ *               contiguous ranges, one per workgroup slot on the device, so
+ *               every CU is busy even at batch 1; a request cut into several
+ *               ranges is merged by the LSE combine. 1..16 = every request is
+ *               cut into exactly that many near-equal token ranges (some may
+ *               be empty), merged the same way.
+ *  batch        number of requests (0 is a no-op)
+ *  max_blocks_per_seq  row length of block_table (>= 1)
+ *  num_blocks   number of physical blocks in kv_cache (>= 1)
+ *  kv_dtype     mla_kv_dtype_t
+ *  kv_scale     per-tensor dequantisation scale: exactly 1.0 for MLA_KV_BF16,
+ *               finite and > 0 for MLA_KV_FP8_E4M3. In the fp8 path q is
+ *               quantised to E4M3 inside the kernel, one scale per (request,
+ *               head) row, and both products run on fp8 matrix cores.
+ *  workspace    caller-owned device scratch of at least workspace_bytes,
+ *               256-byte aligned, needing no initialisation; distinct
+ *               concurrent calls need distinct workspaces
+ *  workspace_bytes  >= mla_get_workspace_size(batch, num_heads,
+ *               max_blocks_per_seq * block_size, num_splits, <device CUs>)
+ *               in forced mode; in automatic mode a smaller workspace is
+ *               accepted down to what one partition per CU needs, and fewer
+ *               partitions are used (results are unchanged)
+ *  stream       hipStream_t to enqueue on
+ */
+mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, void* out, float* lse, float scale,
+                        int32_t num_heads, int32_t block_size, int32_t num_splits,
+                        int32_t batch, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        int32_t kv_dtype, float kv_scale, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_profiled: exactly mla_decode, and additionally records the four
+ * caller-created hipEvent_t handles in events[0..3] on `stream`: before the
+ * split-plan kernel, before the attention kernel, after the attention kernel
+ * and after the combine kernel. Used to time the attention kernel alone.
+ * events must be non-NULL with four non-NULL entries.
+ */
+mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 void* out, float* lse, float scale, int32_t num_heads,
+                                 int32_t block_size, int32_t num_splits, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t kv_dtype, float kv_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * mla_combine: merge normalised split partials by log-sum-exp (PR #20769,
+ * summary of changes: the reduction kernel that combines split-KV results).
+ *
+ *  partial_out  [total_rows][num_heads][512] fp32, each row already divided
+ *               by its own softmax denominator, 16-byte aligned
+ *  partial_lse  [total_rows][num_heads] fp32 natural-log LSE; -inf marks an
+ *               empty split (weight 0, its partial_out is not read)
+ *  split_indptr [batch + 1] int32, non-decreasing, split_indptr[0] = 0:
+ *               request b owns rows split_indptr[b] .. split_indptr[b+1]-1
+ *  out          [batch][num_heads][512] bf16: sum_s w_s o_s / sum_s w_s with
+ *               w_s = exp(lse_s - max_s lse_s); a request with no row or only
+ *               empty rows gets out = 0, lse = -inf
+ *  lse          [batch][num_heads] fp32 = max + ln(sum_s w_s), or NULL
+ */
+mla_status_t mla_combine(const float* partial_out, const float* partial_lse,
+                         const int32_t* split_indptr, void* out, float* lse, int32_t batch,
+                         int32_t num_heads, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* mla_status_string(int32_t status);
+
+/* ABI revision of this header; bumped on any signature change. */
+int32_t mla_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_MI355X_H */

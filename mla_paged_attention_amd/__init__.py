@@ -1,0 +1,32 @@
+"""Absorbed Multi-head Latent Attention decode over a paged latent KV cache,
+native to AMD Instinct MI355X (gfx950).
+
+The computation lives in ``libmla_mi355x.so`` (hand-written HIP kernels behind
+the C ABI declared in ``include/mla.h``); this package is its ctypes binding.
+Build the library with ``python -m mla_paged_attention_amd.build``.
+"""
+from ._binding import (  # noqa: F401
+    BLOCK_SIZES,
+    EXPORTED_SYMBOLS,
+    HEAD_DIM_K,
+    HEAD_DIM_V,
+    LIBRARY_PATH,
+    MAX_FORCED_SPLITS,
+    MAX_HEADS,
+    MLA_ERR_HIP,
+    MLA_ERR_INVALID_ARG,
+    MLA_ERR_NO_DEVICE,
+    MLA_ERR_UNSUPPORTED,
+    MLA_ERR_WORKSPACE_TOO_SMALL,
+    MLA_KV_BF16,
+    MLA_KV_FP8_E4M3,
+    MLA_OK,
+    MLAError,
+    abi_version,
+    combine,
+    decode,
+    get_workspace_size,
+    library,
+    status_string,
+    workspace_for,
+)

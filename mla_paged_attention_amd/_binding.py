@@ -1,0 +1,215 @@
+"""ctypes binding of libmla_mi355x.so (the C ABI in include/mla.h).
+
+Argument marshalling only: shapes and dtypes are checked against the same
+constants the header defines, torch supplies device memory and the current
+HIP stream, and every step of the computation runs in the library's kernels.
+There is no fallback: if the library is missing or the device is not gfx950
+the call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIBRARY_PATH = os.path.join(HERE, "libmla_mi355x.so")
+
+HEAD_DIM_K = 576
+HEAD_DIM_V = 512
+MAX_HEADS = 128
+MAX_FORCED_SPLITS = 16
+BLOCK_SIZES = (16, 32, 64, 128)
+
+MLA_OK = 0
+MLA_ERR_INVALID_ARG = -1
+MLA_ERR_UNSUPPORTED = -2
+MLA_ERR_WORKSPACE_TOO_SMALL = -3
+MLA_ERR_NO_DEVICE = -4
+MLA_ERR_HIP = -5
+
+MLA_KV_BF16 = 0
+MLA_KV_FP8_E4M3 = 1
+
+EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_decode", "mla_decode_profiled",
+                    "mla_combine", "mla_status_string", "mla_abi_version")
+
+_lib = None
+_lock = threading.Lock()
+
+
+class MLAError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+
+
+def _bind(lib: ctypes.CDLL) -> None:
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.mla_get_workspace_size.argtypes = [i64, i64, i64, i64, i64]
+    lib.mla_get_workspace_size.restype = sz
+    decode_args = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz,
+                   vp]
+    lib.mla_decode.argtypes = decode_args
+    lib.mla_decode.restype = i32
+    lib.mla_decode_profiled.argtypes = decode_args + [ctypes.POINTER(vp)]
+    lib.mla_decode_profiled.restype = i32
+    lib.mla_combine.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp]
+    lib.mla_combine.restype = i32
+    lib.mla_status_string.argtypes = [i32]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_abi_version.argtypes = []
+    lib.mla_abi_version.restype = i32
+
+
+def library() -> ctypes.CDLL:
+    """Load the in-tree library once (torch is imported first so that both
+    share the one HIP runtime already mapped under the same soname)."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIBRARY_PATH):
+                raise RuntimeError(
+                    f"{LIBRARY_PATH} is not built; run `python -m mla_paged_attention_amd.build`")
+            lib = ctypes.CDLL(LIBRARY_PATH)
+            _bind(lib)
+            _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return library().mla_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return int(library().mla_abi_version())
+
+
+def get_workspace_size(batch: int, num_heads: int, max_seq_len: int, num_splits: int = 0,
+                       num_cus: int = 0) -> int:
+    return int(library().mla_get_workspace_size(batch, num_heads, max_seq_len, num_splits,
+                                                num_cus))
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+_workspaces: dict = {}
+
+
+def workspace_for(device: torch.device, stream, nbytes: int) -> torch.Tensor:
+    """Per (device, stream) uninitialised workspace, grown on demand. Calls on
+    one stream are ordered, so reusing the buffer between them is safe."""
+    key = (device.index, stream.cuda_stream if stream is not None else
+           torch.cuda.current_stream(device).cuda_stream)
+    buf = _workspaces.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _workspaces[key] = buf
+    return buf
+
+
+def _kv_dtype(kv: torch.Tensor) -> int:
+    if kv.dtype == torch.bfloat16:
+        return MLA_KV_BF16
+    if kv.dtype in (torch.uint8, torch.float8_e4m3fn):
+        return MLA_KV_FP8_E4M3
+    raise TypeError(f"kv_cache dtype {kv.dtype} is not bf16 or E4M3 (uint8/float8_e4m3fn)")
+
+
+def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+           seq_lens: torch.Tensor, *, scale: float, num_splits: int = 0, kv_scale: float = 1.0,
+           out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
+           workspace: torch.Tensor | None = None, stream=None, events=None):
+    """Absorbed MLA decode over a paged cache (see include/mla.h, mla_decode).
+
+    q [B, H, 576] bf16; kv_cache [num_blocks, block_size, 576] bf16 or E4M3
+    (uint8 / float8_e4m3fn) with per-tensor kv_scale; block_table [B, max_blocks]
+    int32; seq_lens [B] int32. Returns (out [B, H, 512] bf16, lse [B, H] fp32 or
+    None). `events`: four torch.cuda.Event(enable_timing=True) to record around
+    the split plan, attention and combine kernels (mla_decode_profiled).
+    """
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise ValueError("q must be [batch, num_heads, 576] bf16")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != HEAD_DIM_K:
+        raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
+    kv_dtype = _kv_dtype(kv_cache)
+    batch, num_heads, _ = q.shape
+    num_blocks, block_size, _ = kv_cache.shape
+    if block_table.dim() != 2 or block_table.shape[0] != batch or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be [batch, max_blocks] int32")
+    if seq_lens.shape != (batch,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be [batch] int32")
+    dev = q.device
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if out is None:
+        out = torch.empty((batch, num_heads, HEAD_DIM_V), dtype=torch.bfloat16, device=dev)
+    if lse is True:
+        lse = torch.empty((batch, num_heads), dtype=torch.float32, device=dev)
+    elif lse is False:
+        lse = None
+    max_blocks = block_table.shape[1]
+    need = get_workspace_size(batch, num_heads, max_blocks * block_size, num_splits, 0)
+    if workspace is None:
+        workspace = workspace_for(dev, stream, need)
+    args = (_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+            float(scale), num_heads, block_size, num_splits, batch, max_blocks, num_blocks,
+            kv_dtype, float(kv_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream))
+    lib = library()
+    if events is None:
+        st = lib.mla_decode(*args)
+    else:
+        arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib.mla_decode_profiled(*args, arr)
+    if st != MLA_OK:
+        raise MLAError(st, "mla_decode")
+    return out, lse
+
+
+def combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, split_indptr: torch.Tensor,
+            *, out: torch.Tensor | None = None, lse: torch.Tensor | bool | None = True,
+            stream=None):
+    """LSE merge of split partials (see include/mla.h, mla_combine).
+
+    partial_out [rows, H, 512] fp32; partial_lse [rows, H] fp32 (-inf = empty);
+    split_indptr [B + 1] int32. Returns (out [B, H, 512] bf16, lse [B, H] or None).
+    """
+    if partial_out.dim() != 3 or partial_out.shape[2] != HEAD_DIM_V or \
+            partial_out.dtype != torch.float32:
+        raise ValueError("partial_out must be [rows, num_heads, 512] fp32")
+    rows, num_heads, _ = partial_out.shape
+    if partial_lse.shape != (rows, num_heads) or partial_lse.dtype != torch.float32:
+        raise ValueError("partial_lse must be [rows, num_heads] fp32")
+    if split_indptr.dim() != 1 or split_indptr.dtype != torch.int32:
+        raise ValueError("split_indptr must be [batch + 1] int32")
+    batch = split_indptr.shape[0] - 1
+    dev = partial_out.device
+    for name, t in (("partial_out", partial_out), ("partial_lse", partial_lse),
+                    ("split_indptr", split_indptr)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if out is None:
+        out = torch.empty((batch, num_heads, HEAD_DIM_V), dtype=torch.bfloat16, device=dev)
+    if lse is True:
+        lse = torch.empty((batch, num_heads), dtype=torch.float32, device=dev)
+    elif lse is False:
+        lse = None
+    st = library().mla_combine(_ptr(partial_out), _ptr(partial_lse), _ptr(split_indptr),
+                               _ptr(out), _ptr(lse), batch, num_heads, _stream_handle(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_combine")
+    return out, lse

@@ -1,0 +1,49 @@
+"""Build libmla_mi355x.so in-tree with hipcc for gfx950.
+
+The library is plain C ABI (include/mla.h); the Python binding loads it with
+ctypes. Run ``python -m mla_paged_attention_amd.build`` or call ``build()``.
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+SOURCES = [os.path.join(CSRC, "mla_kernels.hip"), os.path.join(CSRC, "mla_api.hip")]
+LIBRARY = os.path.join(HERE, "libmla_mi355x.so")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+FLAGS = [
+    "--offload-arch=gfx950",
+    "-O3",
+    "-std=c++17",
+    "-fPIC",
+    "-shared",
+    "-Wall",
+    # Keep hipcc from forming packed fp32 instructions.
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    tmp = LIBRARY + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-o", tmp, *SOURCES]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    noise = "is not a recognized feature for this target"
+    msgs = [ln for ln in (r.stdout + r.stderr).splitlines() if noise not in ln]
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    if verbose and msgs:
+        print("\n".join(msgs))
+    os.replace(tmp, LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

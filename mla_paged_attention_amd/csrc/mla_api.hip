@@ -1,0 +1,288 @@
+// mla_api.hip -- the C ABI declared in include/mla.h: argument validation,
+// workspace sizing, device checks and kernel dispatch. No allocation, no
+// host synchronisation, no exceptions across the boundary.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+#include <mutex>
+#include <string.h>
+
+#include "../../include/mla.h"
+#include "mla_internal.h"
+
+namespace {
+
+using mla::WorkspaceLayout;
+
+constexpr int64_t kDefaultCus = 256;  // MI355X
+constexpr int kMaxDevices = 64;
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int bs_log2_of(int32_t bs) {
+  switch (bs) {
+    case 16: return 4;
+    case 32: return 5;
+    case 64: return 6;
+    case 128: return 7;
+    default: return -1;
+  }
+}
+
+// Partial rows the automatic plan may need with at most `parts` partitions:
+// every cut inside a request adds one piece, and a split request of p pieces
+// holds p rows, so at most 2 * (parts - 1) rows; never more than
+// batch * min(parts, units of the longest request).
+int64_t auto_rows(int64_t batch, int64_t parts, int64_t max_seq_len) {
+  if (parts <= 1 || batch <= 0) return 0;
+  int64_t units = (max_seq_len + mla::kUnit - 1) / mla::kUnit;
+  if (units < 1) units = 1;
+  int64_t per_req = parts < units ? parts : units;
+  if (per_req <= 1) return 0;
+  int64_t a = 2 * (parts - 1), b = batch * per_req;
+  return a < b ? a : b;
+}
+
+int64_t forced_rows(int64_t batch, int64_t splits) { return splits > 1 ? batch * splits : 0; }
+
+struct DeviceInfo {
+  bool valid = false;
+  bool gfx950 = false;
+  int cus = 0;
+};
+
+std::mutex g_dev_mutex;
+DeviceInfo g_dev[kMaxDevices];  // immutable device properties, filled once per device
+
+mla_status_t query_device(DeviceInfo* info) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLA_ERR_NO_DEVICE;
+  if (dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (!g_dev[dev].valid) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return MLA_ERR_NO_DEVICE;
+    DeviceInfo d;
+    d.valid = true;
+    d.gfx950 = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    d.cus = prop.multiProcessorCount;
+    g_dev[dev] = d;
+  }
+  *info = g_dev[dev];
+  return MLA_OK;
+}
+
+struct DecodeArgs {
+  const void* q;
+  const void* kv_cache;
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  void* out;
+  float* lse;
+  float scale;
+  int32_t num_heads, block_size, num_splits, batch, max_blocks, num_blocks, kv_dtype;
+  float kv_scale;
+  void* workspace;
+  size_t workspace_bytes;
+  hipStream_t stream;
+};
+
+mla_status_t validate_decode(const DecodeArgs& a) {
+  if (a.batch < 0) return MLA_ERR_INVALID_ARG;
+  if (a.num_heads < 1 || a.num_heads > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (bs_log2_of(a.block_size) < 0) return MLA_ERR_INVALID_ARG;
+  if (a.num_splits < 0 || a.num_splits > MLA_MAX_FORCED_SPLITS) return MLA_ERR_INVALID_ARG;
+  if (a.max_blocks < 1 || a.num_blocks < 1) return MLA_ERR_INVALID_ARG;
+  if (int64_t(a.max_blocks) * a.block_size > INT32_MAX / 2) return MLA_ERR_INVALID_ARG;
+  if (int64_t(a.num_blocks) * a.block_size * MLA_HEAD_DIM_K > (int64_t(1) << 46))
+    return MLA_ERR_INVALID_ARG;
+  if (!isfinite(a.scale)) return MLA_ERR_INVALID_ARG;
+  if (a.kv_dtype == MLA_KV_BF16) {
+    if (a.kv_scale != 1.0f) return MLA_ERR_INVALID_ARG;
+  } else if (a.kv_dtype == MLA_KV_FP8_E4M3) {
+    if (!(isfinite(a.kv_scale) && a.kv_scale > 0.f)) return MLA_ERR_INVALID_ARG;
+  } else {
+    return MLA_ERR_INVALID_ARG;
+  }
+  if (a.batch == 0) return MLA_OK;
+  if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out || !a.workspace)
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned(a.q, 16) || !aligned(a.kv_cache, 16) || !aligned(a.out, 16) ||
+      !aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) || !aligned(a.workspace, 256))
+    return MLA_ERR_INVALID_ARG;
+  if (a.lse && !aligned(a.lse, 4)) return MLA_ERR_INVALID_ARG;
+  // Metadata alone must fit whatever the mode.
+  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.num_heads, 0).total)
+    return MLA_ERR_WORKSPACE_TOO_SMALL;
+  if (a.num_splits > 0) {
+    WorkspaceLayout w =
+        mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits));
+    if (a.workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  return MLA_OK;
+}
+
+mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
+  mla_status_t st = validate_decode(a);
+  if (st != MLA_OK) return st;
+  if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
+    return MLA_ERR_INVALID_ARG;
+  DeviceInfo dev;
+  st = query_device(&dev);
+  if (st != MLA_OK) return st;
+  if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
+  if (a.batch == 0) return MLA_OK;
+
+  const int64_t cap = int64_t(a.max_blocks) * a.block_size;
+  WorkspaceLayout w;
+  int64_t max_parts = 0;
+  if (a.num_splits > 0) {
+    w = mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits));
+  } else {
+    // Largest partition count whose partial rows fit the given workspace.
+    max_parts = mla::max_partitions(dev.cus, a.num_heads);
+    while (max_parts > 1 &&
+           mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, max_parts, cap)).total >
+               a.workspace_bytes)
+      max_parts = max_parts * 3 / 4;
+    w = mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, max_parts, cap));
+    if (w.total > a.workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
+  }
+  uint8_t* ws = static_cast<uint8_t*>(a.workspace);
+  int32_t* header = reinterpret_cast<int32_t*>(ws + w.header);
+  int32_t* cum = reinterpret_cast<int32_t*>(ws + w.cum);
+  int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + w.row_ptr);
+  float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
+  float* part_out = reinterpret_cast<float*>(ws + w.part_out);
+
+  hipStream_t s = a.stream;
+  auto rec = [&](int i) -> bool {
+    return !events || hipEventRecord(static_cast<hipEvent_t>(events[i]), s) == hipSuccess;
+  };
+
+  if (!rec(0)) return MLA_ERR_HIP;
+  if (mla::launch_plan(a.seq_lens, a.batch, int32_t(cap), a.num_splits, int32_t(max_parts),
+                       header, cum, row_ptr, s) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (!rec(1)) return MLA_ERR_HIP;
+
+  mla::AttnArgs args;
+  args.q = static_cast<const uint16_t*>(a.q);
+  args.kv = static_cast<const uint8_t*>(a.kv_cache);
+  args.block_table = a.block_table;
+  args.seq_lens = a.seq_lens;
+  args.out = static_cast<uint16_t*>(a.out);
+  args.lse = a.lse;
+  args.part_out = part_out;
+  args.part_lse = part_lse;
+  args.header = header;
+  args.cum = cum;
+  args.row_ptr = row_ptr;
+  args.scale_log2 = a.scale * 1.4426950408889634f;
+  args.kv_scale = a.kv_scale;
+  args.num_heads = a.num_heads;
+  args.batch = a.batch;
+  args.max_blocks = a.max_blocks;
+  args.num_blocks = a.num_blocks;
+  args.bs_log2 = bs_log2_of(a.block_size);
+  args.cap_tokens = int32_t(cap);
+  args.num_splits = a.num_splits;
+  args.head_tiles = mla::head_tiles(a.num_heads);
+  int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
+  int64_t parts_launched = (parts + 7) / 8 * 8;
+  if (parts_launched * args.head_tiles > INT32_MAX) return MLA_ERR_INVALID_ARG;
+  hipError_t e = mla::launch_attention(args, a.kv_dtype == MLA_KV_FP8_E4M3, int32_t(parts_launched), s);
+  if (e == hipErrorNotSupported) return MLA_ERR_UNSUPPORTED;
+  if (e != hipSuccess) return MLA_ERR_HIP;
+  if (!rec(2)) return MLA_ERR_HIP;
+
+  const bool need_combine = a.num_splits > 1 || (a.num_splits == 0 && max_parts > 1);
+  if (need_combine) {
+    if (mla::launch_combine(part_out, part_lse, row_ptr, static_cast<uint16_t*>(a.out), a.lse,
+                            a.batch, a.num_heads, 0, s) != hipSuccess)
+      return MLA_ERR_HIP;
+  }
+  if (!rec(3)) return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_len,
+                              int64_t num_splits, int64_t num_cus) {
+  if (batch < 0 || batch > INT32_MAX / 2) return 0;
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS) return 0;
+  if (max_seq_len < 0 || max_seq_len > INT32_MAX / 2) return 0;
+  if (num_splits < 0 || num_splits > MLA_MAX_FORCED_SPLITS) return 0;
+  if (num_cus <= 0) num_cus = kDefaultCus;
+  int64_t rows = num_splits > 0
+                     ? forced_rows(batch, num_splits)
+                     : auto_rows(batch, mla::max_partitions(num_cus, num_heads), max_seq_len);
+  return mla::workspace_layout(batch, num_heads, rows).total;
+}
+
+mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
+                        const int32_t* seq_lens, void* out, float* lse, float scale,
+                        int32_t num_heads, int32_t block_size, int32_t num_splits,
+                        int32_t batch, int32_t max_blocks_per_seq, int32_t num_blocks,
+                        int32_t kv_dtype, float kv_scale, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, block_size,
+               num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype, kv_scale,
+               workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  return run_decode(a, nullptr);
+}
+
+mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
+                                 const int32_t* block_table, const int32_t* seq_lens,
+                                 void* out, float* lse, float scale, int32_t num_heads,
+                                 int32_t block_size, int32_t num_splits, int32_t batch,
+                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t kv_dtype, float kv_scale, void* workspace,
+                                 size_t workspace_bytes, void* stream, void* const* events) {
+  if (!events) return MLA_ERR_INVALID_ARG;
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, block_size,
+               num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype, kv_scale,
+               workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  return run_decode(a, events);
+}
+
+mla_status_t mla_combine(const float* partial_out, const float* partial_lse,
+                         const int32_t* split_indptr, void* out, float* lse, int32_t batch,
+                         int32_t num_heads, void* stream) {
+  if (batch < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (batch > 0) {
+    if (!partial_out || !partial_lse || !split_indptr || !out) return MLA_ERR_INVALID_ARG;
+    if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(split_indptr, 4) ||
+        !aligned(out, 16) || (lse && !aligned(lse, 4)))
+      return MLA_ERR_INVALID_ARG;
+  }
+  DeviceInfo dev;
+  mla_status_t st = query_device(&dev);
+  if (st != MLA_OK) return st;
+  if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
+  if (batch == 0) return MLA_OK;
+  if (mla::launch_combine(partial_out, partial_lse, split_indptr, static_cast<uint16_t*>(out),
+                          lse, batch, num_heads, 1, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+const char* mla_status_string(int32_t status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_WORKSPACE_TOO_SMALL: return "MLA_ERR_WORKSPACE_TOO_SMALL";
+    case MLA_ERR_NO_DEVICE: return "MLA_ERR_NO_DEVICE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+int32_t mla_abi_version(void) { return 1; }
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// mla_internal.h -- launch interface between the C-ABI layer (mla_api.hip) and
+// the gfx950 kernels (mla_kernels.hip). Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kDK = 576;        // key width (512 kv_c + 64 rope)
+constexpr int kDV = 512;        // value width (kv_c)
+constexpr int kUnit = 16;       // tokens per scheduling unit = MFMA tile rows
+constexpr int kHeadTile = 16;   // heads per workgroup (MFMA tile columns)
+constexpr int kWaves = 4;       // waves per attention workgroup
+constexpr int kThreads = 64 * kWaves;
+constexpr int kOverheadUnits = 1;   // per-request fixed cost in the balanced plan
+constexpr int kMinPartUnits = 4;    // smallest partition: one unit per wave
+constexpr int kPlanThreads = 1024;
+
+// Workspace layout. Offsets are 256-byte aligned.
+struct WorkspaceLayout {
+  size_t header;    // int32[64]: [0] partitions used, [1] cost units per partition
+  size_t cum;       // int32[batch + 1]: exclusive prefix of per-request costs
+  size_t row_ptr;   // int32[batch + 1]: first partial row of each request
+  size_t part_lse;  // float[rows][num_heads]
+  size_t part_out;  // float[rows][num_heads][512]
+  size_t total;
+  int64_t rows;
+};
+
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_t rows) {
+  WorkspaceLayout w;
+  size_t off = 0;
+  w.header = off;
+  off += 256;
+  w.cum = off;
+  off += align256(size_t(batch + 1) * 4);
+  w.row_ptr = off;
+  off += align256(size_t(batch + 1) * 4);
+  w.part_lse = off;
+  off += align256(size_t(rows) * size_t(num_heads) * 4);
+  w.part_out = off;
+  off += align256(size_t(rows) * size_t(num_heads) * kDV * 4);
+  w.total = off;
+  w.rows = rows;
+  return w;
+}
+
+inline int head_tiles(int num_heads) { return (num_heads + kHeadTile - 1) / kHeadTile; }
+
+// Upper bound on balanced partitions for a device with `num_cus` CUs: one
+// attention workgroup per CU at a time, shared by the head tiles.
+inline int64_t max_partitions(int64_t num_cus, int64_t num_heads) {
+  int64_t g = num_cus / head_tiles(int(num_heads));
+  return g < 8 ? 8 : g;
+}
+
+struct AttnArgs {
+  const uint16_t* q;         // [B][H][576] bf16 bits
+  const uint8_t* kv;         // [NB][bs][576] bf16 or e4m3 bytes
+  const int32_t* block_table;
+  const int32_t* seq_lens;
+  uint16_t* out;             // [B][H][512] bf16 bits
+  float* lse;                // [B][H] or null
+  float* part_out;
+  float* part_lse;
+  const int32_t* header;
+  const int32_t* cum;
+  const int32_t* row_ptr;
+  float scale_log2;          // logit scale * log2(e)
+  float kv_scale;            // fp8 dequantisation scale (1 for bf16)
+  int32_t num_heads;
+  int32_t batch;
+  int32_t max_blocks;
+  int32_t num_blocks;
+  int32_t bs_log2;
+  int32_t cap_tokens;        // max_blocks * block_size
+  int32_t num_splits;        // 0 = balanced plan
+  int32_t head_tiles;
+};
+
+hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
+                       int32_t num_splits, int32_t max_parts, int32_t* header, int32_t* cum,
+                       int32_t* row_ptr, hipStream_t stream);
+
+// kv_fp8: 0 = bf16 cache, 1 = E4M3 cache. `parts_launched` is a multiple of 8.
+hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_launched,
+                            hipStream_t stream);
+
+hipError_t launch_combine(const float* part_out, const float* part_lse,
+                          const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
+                          int32_t num_heads, int zero_empty, hipStream_t stream);
+
+}  // namespace mla

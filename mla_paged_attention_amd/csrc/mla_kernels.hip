@@ -1,0 +1,510 @@
+// mla_kernels.hip -- gfx950 (CDNA4) kernels for absorbed MLA decode over a
+// paged latent KV cache.
+//
+// Three kernels run per decode call, all on the caller's stream:
+//
+//  1. plan_kernel: from device seq_lens, the split plan. In balanced mode the
+//     KV of all requests is laid end to end in 16-token units (plus a fixed
+//     per-request overhead) and cut into equal contiguous partitions, one per
+//     attention workgroup slot on the device; a request that straddles a cut
+//     becomes several pieces. In forced mode every request is cut into
+//     num_splits near-equal pieces. The plan stays on the device, so the host
+//     never synchronises. (PR #20769 "SM100 Cutlass MLA decode with
+//     unrestricted num_heads (< 128) for DeepSeek TP", summary of changes: a
+//     tile scheduler and splitting KV across multiple blocks/SMs.)
+//
+//  2. attn_kernel: one workgroup per (partition, 16-head tile). Its four
+//     waves take the 16-token units of a piece round robin. For each unit a
+//     wave loads the 16 cached rows (contiguous: a unit never straddles a
+//     page because block sizes are multiples of 16) straight from HBM into
+//     registers, computes the 16x16 logit tile on bf16 MFMA, updates an fp32
+//     online softmax, and accumulates P.V on MFMA into a 16x512 fp32 tile.
+//     The four waves' states are merged through LDS; a one-piece request is
+//     written as the final bf16 output and LSE, a piece of a split request
+//     as a normalised fp32 partial plus its LSE.
+//
+//  3. combine_kernel: log-sum-exp merge of the partial rows of each split
+//     request (PR #20769, summary of changes: the reduction kernel that
+//     combines split-KV results).
+//
+// Operand layouts of v_mfma_f32_16x16x32_bf16 / v_mfma_f32_16x16x16_bf16
+// used below (lane l, c = l % 16, g = l / 16): A[i][k] lives in lane with
+// i = c and k in the g-th group of k slots; B[k][j] in lane with j = c and
+// the same k slots; D[i][j] in lane with j = c, i = 4g + r, r = 0..3. Only
+// the symmetry between the k-slot maps of A and B is relied on.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "mla_internal.h"
+
+namespace mla {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kRowBytes = kDK * 2;       // one bf16 cache row: 1152 bytes
+constexpr int kQChunks = kDK / 32;       // 18 k-steps of 32 features
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kFrameSlack = 8.f;  // log2 headroom of the accumulation frame
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ unsigned short bf16_bits(float x) {
+  __bf16 h = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(unsigned short, h);
+}
+
+// ----------------------------------------------------------------------------
+// Block-wide exclusive scan over kPlanThreads threads.
+__device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    int t = __shfl_up(inc, d);
+    if (lane >= d) inc += t;
+  }
+  if (lane == 63) s_wave[wave] = inc;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < kPlanThreads / 64 ? s_wave[lane] : 0;
+    int winc = w;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      int t = __shfl_up(winc, d);
+      if (lane >= d) winc += t;
+    }
+    if (lane < kPlanThreads / 64) s_wave[16 + lane] = winc - w;
+    if (lane == kPlanThreads / 64 - 1) s_wave[32] = winc;
+  }
+  __syncthreads();
+  int res = s_wave[16 + wave] + inc - v;
+  *total = s_wave[32];
+  __syncthreads();
+  return res;
+}
+
+__device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
+
+__device__ __forceinline__ int units_of(int n) {
+  int u = (n + kUnit - 1) / kUnit;
+  return u < 1 ? 1 : u;  // an empty request still owns one (empty) unit
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* seq_lens, int32_t batch,
+                                                            int32_t cap_tokens, int32_t num_splits,
+                                                            int32_t max_parts, int32_t* header,
+                                                            int32_t* cum, int32_t* row_ptr) {
+  __shared__ int s_wave[40];
+  const int tid = threadIdx.x;
+  if (num_splits > 0) {
+    for (int b = tid; b <= batch; b += kPlanThreads) row_ptr[b] = num_splits > 1 ? b * num_splits : 0;
+    if (tid == 0) {
+      header[0] = batch * num_splits;
+      header[1] = 0;
+    }
+    return;
+  }
+  // Pass 1: exclusive prefix of cost = overhead + units.
+  int carry = 0;
+  for (int base = 0; base < batch; base += kPlanThreads) {
+    int b = base + tid;
+    int cost = b < batch ? kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens)) : 0;
+    int tot;
+    int ex = block_exclusive_scan(cost, s_wave, &tot);
+    if (b < batch) cum[b] = carry + ex;
+    carry += tot;
+  }
+  const int total = carry;
+  if (tid == 0) cum[batch] = total;
+  int part = (total + max_parts - 1) / max_parts;
+  if (part < kMinPartUnits) part = kMinPartUnits;
+  const int parts = (total + part - 1) / part;
+  // Pass 2: pieces per request and partial rows (requests with one piece need none).
+  carry = 0;
+  int rcarry = 0;
+  for (int base = 0; base < batch; base += kPlanThreads) {
+    int b = base + tid;
+    int cost = b < batch ? kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens)) : 0;
+    int tot;
+    int ex = block_exclusive_scan(cost, s_wave, &tot);
+    int rows = 0;
+    if (b < batch) {
+      int c0 = carry + ex;
+      int first = (c0 + kOverheadUnits) / part;
+      int last = (c0 + cost - 1) / part;
+      int pieces = last - first + 1;
+      rows = pieces > 1 ? pieces : 0;
+    }
+    carry += tot;
+    int rtot;
+    int rex = block_exclusive_scan(rows, s_wave, &rtot);
+    if (b < batch) row_ptr[b] = rcarry + rex;
+    rcarry += rtot;
+  }
+  if (tid == 0) {
+    row_ptr[batch] = rcarry;
+    header[0] = parts;
+    header[1] = part;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// Attention.
+
+constexpr int kQRowDwords = kDK / 2 + 4;  // 1152 B row + 16 B pad: rows start 4 banks apart
+
+struct AttnSmem {
+  float o[kWaves][kHeadTile][kDV];       // per-wave scaled accumulators (merge)
+  float m[kWaves][kHeadTile];            // per-wave running max (log2 domain)
+  float l[kWaves][kHeadTile];            // per-wave softmax denominators
+  uint32_t q[kHeadTile][kQRowDwords];    // q tile of the current piece (bf16 pairs)
+};
+
+// Process one piece: tokens of units [u0, u1) of request b, heads of tile ht.
+// piece = index of this piece within the request, pieces = how many it has.
+template <int KV_FP8>
+__device__ void attend_piece(const AttnArgs& a, AttnSmem& sm, int b, int ht, int u0, int u1,
+                             int piece, int pieces) {
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int H = a.num_heads;
+  const int h0 = ht * kHeadTile;
+  const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
+
+  // Stage the 16 x 576 q tile (contiguous in HBM) in LDS; heads >= H are 0.
+  {
+    const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + h0) * kDK);
+    for (int i = tid; i < kHeadTile * (kDK / 8); i += kThreads) {
+      const int row = i / (kDK / 8), ch = i - row * (kDK / 8);
+      u32x4_t v = h0 + row < H ? qsrc[i] : u32x4_t{0, 0, 0, 0};
+      *reinterpret_cast<u32x4_t*>(&sm.q[row][ch * 4]) = v;
+    }
+  }
+  __syncthreads();
+  // B operand of the logit MFMA: head c, features 32 s + 8 g .. + 7.
+  const uint32_t* qrow = &sm.q[c][4 * g];
+
+  // Accumulation frames (log2 domain). The register accumulator holds
+  // sum_t 2^(x_t - m_ref) v_t for the tokens seen since its last flush; the
+  // wave's LDS slot sm.o[wave] holds the earlier tokens in frame m_lds. The
+  // register accumulator is never rescaled in place: when a head's max rises
+  // more than kFrameSlack above m_ref, the accumulator is folded into the LDS
+  // slot (rescaling only the LDS copy) and restarted from zero in the new
+  // frame. Weights 2^(x - m_ref) therefore stay below 2^kFrameSlack.
+  f32x4_t acc[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = -INFINITY;  // frame of head c (same value in all 4 lane groups)
+  float l_run = 0.f;        // this lane's share of the denominator of head c, frame m_ref
+  float m_lds[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // LDS frame, heads 4g + r
+
+  // Fold acc (frame m_ref) into the LDS slot, which moves to frame m_ref.
+  auto flush = [&]() {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mr = __shfl(m_ref, 4 * g + r);
+      const bool fresh = m_lds[r] == -INFINITY;
+      const float f = fresh ? 0.f : fast_exp2(m_lds[r] - mr);
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta) {
+        float* dst = &sm.o[wave][4 * g + r][128 * beta + 8 * c];
+        f32x4_t lo = f32x4_t{acc[beta * 8 + 0][r], acc[beta * 8 + 1][r], acc[beta * 8 + 2][r],
+                             acc[beta * 8 + 3][r]};
+        f32x4_t hi = f32x4_t{acc[beta * 8 + 4][r], acc[beta * 8 + 5][r], acc[beta * 8 + 6][r],
+                             acc[beta * 8 + 7][r]};
+        if (!fresh) {
+          lo += *reinterpret_cast<const f32x4_t*>(dst) * f;
+          hi += *reinterpret_cast<const f32x4_t*>(dst + 4) * f;
+        }
+        *reinterpret_cast<f32x4_t*>(dst) = lo;
+        *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
+      }
+      m_lds[r] = mr;
+    }
+  };
+
+  const int bs_mask = (1 << a.bs_log2) - 1;
+  const int u_end = min(u1, (n + kUnit - 1) / kUnit);
+  for (int u = u0 + wave; u < u_end; u += kWaves) {
+    const int t0 = u * kUnit;
+    int nvalid = min(kUnit, n - t0);
+    int blk = a.block_table[size_t(b) * a.max_blocks + (t0 >> a.bs_log2)];
+    if (blk < 0 || blk >= a.num_blocks) {  // never read outside the cache
+      blk = 0;
+      nvalid = 0;
+    }
+    const uint8_t* base =
+        a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowBytes;
+
+    // K operand: lane holds token c, features 32 s + 8 g .. + 7.
+    u32x4_t kf[kQChunks];
+    {
+      const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(base + c * kRowBytes) + g;
+#pragma unroll
+      for (int s = 0; s < kQChunks; ++s) kf[s] = kp[4 * s];
+    }
+    // V rows for P.V: lane holds tokens 4 g + r, features 128 beta + 8 c .. + 7.
+    u32x4_t vf[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const u32x4_t* vp = reinterpret_cast<const u32x4_t*>(base + (4 * g + r) * kRowBytes) + c;
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta) vf[beta][r] = vp[16 * beta];
+    }
+
+    // Logits: S^T[token][head] = K . q^T; lane gets tokens 4 g + r of head c.
+    f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kQChunks; ++s) {
+      const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(qrow + 16 * s);
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s]),
+                                                   __builtin_bit_cast(bf16x8_t, qv), sc, 0, 0,
+                                                   0);
+    }
+    float x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (4 * g + r < nvalid) ? sc[r] * a.scale_log2 : -INFINITY;
+
+    // Online softmax (fp32, log2 domain) with a lazily moved frame.
+    float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, __shfl_xor(mt, 32));
+    if (__ballot(mt > m_ref + kFrameSlack) != 0ull) {  // wave-uniform, rare after warm-up
+      if (__ballot(m_ref != -INFINITY) != 0ull) flush();
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const float m_new = fmaxf(m_ref, mt);
+      l_run *= m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+      m_ref = m_new;
+    }
+    const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_use);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+
+    // P as the A operand: head c, tokens 4 g .. 4 g + 3 (already in place).
+    s16x4_t pa;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pa[r] = (short)bf16_bits(p[r]);
+
+    // Masked tokens must contribute exactly 0 even if their bytes are NaN.
+    if (nvalid < kUnit) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const unsigned keep = (4 * g + r < nvalid) ? 0xffffffffu : 0u;
+#pragma unroll
+        for (int beta = 0; beta < 4; ++beta) vf[beta][r] &= keep;
+      }
+    }
+
+    // P.V: for each feature e of the lane's 8, gather the 4 tokens' values
+    // into one B operand (a 4x8 -> 8x4 transpose of 16-bit values).
+#pragma unroll
+    for (int beta = 0; beta < 4; ++beta) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const unsigned d0 = vf[beta][0][i], d1 = vf[beta][1][i];
+        const unsigned d2 = vf[beta][2][i], d3 = vf[beta][3][i];
+        u32x2_t ve = u32x2_t{(d0 & 0xffffu) | (d1 << 16), (d2 & 0xffffu) | (d3 << 16)};
+        u32x2_t vo = u32x2_t{(d0 >> 16) | (d1 & 0xffff0000u), (d2 >> 16) | (d3 & 0xffff0000u)};
+        acc[beta * 8 + 2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            pa, __builtin_bit_cast(s16x4_t, ve), acc[beta * 8 + 2 * i], 0, 0, 0);
+        acc[beta * 8 + 2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+            pa, __builtin_bit_cast(s16x4_t, vo), acc[beta * 8 + 2 * i + 1], 0, 0, 0);
+      }
+    }
+  }
+
+  // ---- merge the four waves through LDS ----
+  // Final fold: the wave's whole sum now sits in sm.o[wave], frame m_ref.
+  flush();
+  float l_c = l_run + __shfl_xor(l_run, 16);
+  l_c += __shfl_xor(l_c, 32);
+  if (g == 0) {
+    sm.m[wave][c] = m_ref;
+    sm.l[wave][c] = l_c;
+  }
+  __syncthreads();
+  {
+    const bool final_out = pieces == 1;
+    const int row = final_out ? 0 : a.row_ptr[b] + piece;
+#pragma unroll
+    for (int j = 0; j < (kHeadTile * kDV / 4) / kThreads; ++j) {
+      const int qi = j * kThreads + tid;
+      const int hh = qi >> 7;           // 128 four-wide chunks per head
+      const int d = (qi & 127) << 2;
+      const int h = h0 + hh;
+      if (h >= H) continue;
+      float M = fmaxf(fmaxf(sm.m[0][hh], sm.m[1][hh]), fmaxf(sm.m[2][hh], sm.m[3][hh]));
+      float L = 0.f;
+      f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm.m[w][hh];
+        if (mw == -INFINITY) continue;  // this wave saw no token of the piece
+        const float f = fast_exp2(mw - M);
+        L += sm.l[w][hh] * f;
+        sum += *reinterpret_cast<const f32x4_t*>(&sm.o[w][hh][d]) * f;
+      }
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      const float lse_v = L > 0.f ? (M + __log2f(L)) * kLn2 : -INFINITY;
+      sum *= inv;
+      if (final_out) {
+        u32x2_t pk;
+        pk[0] = unsigned(bf16_bits(sum[0])) | (unsigned(bf16_bits(sum[1])) << 16);
+        pk[1] = unsigned(bf16_bits(sum[2])) | (unsigned(bf16_bits(sum[3])) << 16);
+        *reinterpret_cast<u32x2_t*>(a.out + (size_t(b) * H + h) * kDV + d) = pk;
+        if (d == 0 && a.lse) a.lse[size_t(b) * H + h] = lse_v;
+      } else {
+        *reinterpret_cast<f32x4_t*>(a.part_out + (size_t(row) * H + h) * kDV + d) = sum;
+        if (d == 0) a.part_lse[size_t(row) * H + h] = lse_v;
+      }
+    }
+  }
+  __syncthreads();  // LDS is reused by the next piece
+}
+
+template <int KV_FP8>
+__global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem sm;
+  // Workgroups are dispatched to the 8 XCDs round robin. Give the head tiles
+  // of one partition the same XCD (shared L2) and adjacent dispatch slots.
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int ht = slot % a.head_tiles;
+  const int part = (slot / a.head_tiles) * 8 + xcd;
+
+  // Walk the pieces of this partition: one piece in forced mode, every
+  // request overlapping the partition's cost range in balanced mode.
+  int b, end = 0, P = 1;
+  if (a.num_splits > 0) {
+    if (part >= a.batch * a.num_splits) return;
+    b = part / a.num_splits;
+  } else {
+    const int parts = a.header[0];
+    P = a.header[1];
+    if (part >= parts) return;
+    const int start = part * P;
+    end = start + P;
+    int lo = 0, hi = a.batch - 1;  // first request whose cost range reaches past start
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a.cum[mid + 1] > start)
+        hi = mid;
+      else
+        lo = mid + 1;
+    }
+    b = lo;
+  }
+  for (;;) {
+    int u0, u1, piece, pieces;
+    bool last;
+    if (a.num_splits > 0) {
+      // Forced split k of request b; an empty split still writes its
+      // (zero, -inf) partial because the combine reads every row.
+      const int S = a.num_splits, k = part - b * S;
+      const int nu = (clamp_len(a.seq_lens[b], a.cap_tokens) + kUnit - 1) / kUnit;
+      u0 = int((long long)k * nu / S);
+      u1 = int((long long)(k + 1) * nu / S);
+      piece = k;
+      pieces = S;
+      last = true;
+    } else {
+      const int ub = a.cum[b] + kOverheadUnits;  // cost position of the request's first unit
+      if (ub >= end) return;
+      const int ue = a.cum[b + 1];
+      const int p0 = max(ub, part * P), p1 = min(ue, end);
+      if (p0 >= p1) return;
+      u0 = p0 - ub;
+      u1 = p1 - ub;
+      piece = p0 / P - ub / P;
+      pieces = (ue - 1) / P - ub / P + 1;
+      last = ue >= end || b + 1 >= a.batch;
+    }
+    attend_piece<KV_FP8>(a, sm, b, ht, u0, u1, piece, pieces);
+    if (last) return;
+    ++b;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// LSE combine: one workgroup per (request, 16-head tile).
+__global__ void __launch_bounds__(256) combine_kernel(const float* part_out, const float* part_lse,
+                                                      const int32_t* row_ptr, uint16_t* out,
+                                                      float* lse, int32_t batch, int32_t H,
+                                                      int32_t tiles, int zero_empty) {
+  const int b = blockIdx.x / tiles, ht = blockIdx.x - (blockIdx.x / tiles) * tiles;
+  const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
+  if (nr <= 0 && !zero_empty) return;
+  const int tid = threadIdx.x;
+  const int h = ht * kHeadTile + (tid >> 4);
+  if (h >= H) return;
+  const int sub = tid & 15;
+  float M = -INFINITY;
+  for (int s = 0; s < nr; ++s) M = fmaxf(M, part_lse[size_t(r0 + s) * H + h]);
+  f32x4_t acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float W = 0.f;
+  if (M != -INFINITY) {
+    for (int s = 0; s < nr; ++s) {
+      const float ls = part_lse[size_t(r0 + s) * H + h];
+      if (ls == -INFINITY) continue;
+      const float w = fast_exp2((ls - M) * kLog2e);
+      W += w;
+      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s) * H + h) * kDV);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] += w * src[i * 16 + sub];
+    }
+  }
+  const float inv = W > 0.f ? 1.f / W : 0.f;
+  uint16_t* dst = out + (size_t(b) * H + h) * kDV;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f32x4_t v = acc[i] * inv;
+    u32x2_t pk;
+    pk[0] = unsigned(bf16_bits(v[0])) | (unsigned(bf16_bits(v[1])) << 16);
+    pk[1] = unsigned(bf16_bits(v[2])) | (unsigned(bf16_bits(v[3])) << 16);
+    *reinterpret_cast<u32x2_t*>(dst + (i * 16 + sub) * 4) = pk;
+  }
+  if (sub == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
+}
+
+// ----------------------------------------------------------------------------
+// Host-side launchers.
+
+hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
+                       int32_t num_splits, int32_t max_parts, int32_t* header, int32_t* cum,
+                       int32_t* row_ptr, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch,
+                     cap_tokens, num_splits, max_parts, header, cum, row_ptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_launched,
+                            hipStream_t stream) {
+  dim3 grid(unsigned(parts_launched) * unsigned(args.head_tiles));
+  if (kv_fp8) return hipErrorNotSupported;
+  hipLaunchKernelGGL(attn_kernel<0>, grid, dim3(kThreads), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* part_out, const float* part_lse,
+                          const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
+                          int32_t num_heads, int zero_empty, hipStream_t stream) {
+  const int tiles = head_tiles(num_heads);
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(batch) * unsigned(tiles)), dim3(256), 0, stream,
+                     part_out, part_lse, row_ptr, out, lse, batch, num_heads, tiles, zero_empty);
+  return hipGetLastError();
+}
+
+}  // namespace mla

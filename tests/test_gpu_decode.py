@@ -1,0 +1,223 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every case draws seeded inputs from workloads.py, runs mla_decode on cuda:0
+and the oracle on the host, and compares element by element at the stated
+tolerances (bf16 cache: out 1e-2 + 1e-2|ref|, lse 1e-3 absolute; fp8 cache:
+2e-2 + 2e-2|ref| for both, against the oracle fed the dequantised cache and
+the unquantised bf16 q). Full-size configurations compare a sample of
+requests (all heads) and check that every output is finite.
+"""
+import numpy as np
+import pytest
+import torch
+
+import mla_paged_attention_amd as mla
+import workloads
+from gpu_helpers import compare, run_gpu, run_oracle, to_device, to_np
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+def _check(orc, wl, num_splits=0, req=None, what=""):
+    out, lse = to_np(*run_gpu(wl, num_splits))
+    ref_out, ref_lse = run_oracle(orc, wl, req)
+    if req is not None:
+        out, lse = out[req], lse[req]
+    return compare(out, lse, ref_out, ref_lse, wl.kv_dtype, what or wl.name)
+
+
+@pytest.mark.parametrize("num_splits", [1, 2, 0, 3, 7, 16])
+@pytest.mark.parametrize("poison", [False, True])
+def test_tiny(orc, num_splits, poison):
+    wl = workloads.make_config("tiny", poison=poison)
+    _check(orc, wl, num_splits, what=f"tiny splits={num_splits} poison={poison}")
+
+
+@pytest.mark.parametrize("block_size", [16, 32, 64, 128])
+@pytest.mark.parametrize("num_heads", [1, 5, 16, 20, 128])
+def test_ragged_edges(orc, block_size, num_heads):
+    lens = [0, 1, 15, 16, 17, 31, 33, 64, 129, 700]
+    wl = workloads.make_workload(batch=len(lens), num_heads=num_heads, seq=("fixed", lens),
+                                 block_size=block_size, seed=100 + block_size + num_heads,
+                                 pool_blocks=None, poison=True)
+    for s in (0, 1, 4):
+        _check(orc, wl, s, what=f"edges bs={block_size} H={num_heads} splits={s}")
+
+
+@pytest.mark.parametrize("name", ["v2lite-1", "v2lite-8", "v2lite-64"])
+def test_v2lite(orc, name):
+    wl = workloads.make_config(name)
+    _check(orc, wl, 0)
+
+
+def test_v2lite8_poisoned(orc):
+    wl = workloads.make_config("v2lite-8", poison=True)
+    _check(orc, wl, 0, what="v2lite-8 poisoned")
+
+
+def _sample(wl, k, seed):
+    rng = np.random.default_rng(seed)
+    lens = wl.seq_lens.numpy()
+    pick = set(rng.choice(wl.batch, size=min(k, wl.batch), replace=False).tolist())
+    pick.add(int(np.argmax(lens)))
+    pick.add(int(np.argmin(lens)))
+    pick.add(0)
+    pick.add(wl.batch - 1)
+    return np.array(sorted(pick), dtype=np.int32)
+
+
+def test_r1tp8_sampled(orc):
+    wl = workloads.make_config("r1tp8")
+    _check(orc, wl, 0, req=_sample(wl, 28, 4), what="r1tp8 (sampled)")
+
+
+def test_fullhead_sampled(orc):
+    wl = workloads.make_config("fullhead")
+    _check(orc, wl, 0, req=_sample(wl, 4, 5), what="fullhead (sampled)")
+
+
+def test_fp8_sampled(orc):
+    wl = workloads.make_config("fp8")
+    _check(orc, wl, 0, req=_sample(wl, 3, 6), what="fp8 (sampled)")
+
+
+@pytest.mark.parametrize("num_splits", [0, 1, 5])
+def test_fp8_small(orc, num_splits):
+    wl = workloads.make_workload(batch=5, num_heads=20, seq=("fixed", [1, 17, 100, 513, 2000]),
+                                 block_size=64, seed=61, kv_dtype="fp8", poison=True)
+    _check(orc, wl, num_splits, what=f"fp8 small splits={num_splits}")
+
+
+# ---------------------------------------------------------------- invariants
+
+def test_block_permutation_bitwise():
+    wl = workloads.make_workload(batch=6, num_heads=16, seq=("fixed", [5, 64, 100, 333, 1000, 47]),
+                                 block_size=32, seed=21, pool_blocks=70)
+    out_a, lse_a = run_gpu(wl, 0)
+    perm = torch.randperm(wl.num_blocks, generator=torch.Generator().manual_seed(3))
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(wl.num_blocks)
+    wl.kv = wl.kv[perm].contiguous()
+    valid = wl.block_table >= 0
+    wl.block_table[valid] = inv[wl.block_table[valid].long()].to(torch.int32)
+    out_b, lse_b = run_gpu(wl, 0)
+    assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+
+
+def test_batch_independence_bitwise():
+    # Request 0 keeps its piece boundaries when the others change only in content.
+    wl = workloads.make_workload(batch=4, num_heads=16, seq=("fixed", [700, 300, 900, 50]),
+                                 block_size=64, seed=22)
+    out_a, lse_a = run_gpu(wl, 1)
+    wl.q[1:] = torch.randn(wl.q[1:].shape, generator=torch.Generator().manual_seed(9)).to(
+        torch.bfloat16)
+    wl.seq_lens[1:] = torch.tensor([3, 17, 640], dtype=torch.int32)
+    out_b, lse_b = run_gpu(wl, 1)
+    assert torch.equal(out_a[0], out_b[0]) and torch.equal(lse_a[0], lse_b[0])
+
+
+@pytest.mark.parametrize("num_splits", [0, 3])
+def test_determinism_bitwise(num_splits):
+    wl = workloads.make_config("v2lite-8")
+    dev = to_device(wl)
+    out_a, lse_a = run_gpu(wl, num_splits, dev)
+    out_a, lse_a = out_a.clone(), lse_a.clone()
+    for _ in range(3):
+        out_b, lse_b = run_gpu(wl, num_splits, dev)
+        assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
+
+
+def test_head_padding_to_128(orc):
+    wl = workloads.make_config("tiny")
+    out16, lse16 = to_np(*run_gpu(wl, 0))
+    q128 = torch.zeros((wl.batch, 128, 576), dtype=torch.bfloat16)
+    q128[:, :16] = wl.q
+    wl128 = workloads.Workload(name="tiny-pad128", q=q128, kv=wl.kv,
+                               block_table=wl.block_table, seq_lens=wl.seq_lens,
+                               block_size=wl.block_size, kv_dtype=wl.kv_dtype,
+                               kv_scale=wl.kv_scale)
+    out128, lse128 = to_np(*run_gpu(wl128, 0))
+    ref_out, ref_lse = run_oracle(orc, wl128)
+    compare(out128, lse128, ref_out, ref_lse, what="tiny padded to 128 heads")
+    # Real heads: the same per-head arithmetic, so bitwise equal to the 16-head run.
+    assert np.array_equal(out128[:, :16], out16) and np.array_equal(lse128[:, :16], lse16)
+    # Padded heads (q = 0): the mean of the value rows and ln N.
+    for b in range(wl.batch):
+        n = int(wl.seq_lens[b])
+        np.testing.assert_allclose(lse128[b, 16:], np.log(n), atol=1e-3)
+
+
+def test_split_counts_agree(orc):
+    wl = workloads.make_workload(batch=3, num_heads=16, seq=("fixed", [2000, 37, 4097]),
+                                 block_size=64, seed=23, poison=True)
+    ref_out, ref_lse = run_oracle(orc, wl)
+    for s in range(0, 17):
+        out, lse = to_np(*run_gpu(wl, s))
+        compare(out, lse, ref_out, ref_lse, what=f"splits={s}")
+
+
+def test_small_workspace_auto_mode(orc):
+    wl = workloads.make_config("v2lite-8")
+    meta = mla.get_workspace_size(wl.batch, wl.num_heads, 0, 1, 0)
+    full = mla.get_workspace_size(wl.batch, wl.num_heads, wl.max_blocks * wl.block_size, 0, 0)
+    ref_out, ref_lse = run_oracle(orc, wl)
+    for nbytes in (meta, (meta + full) // 2, full):
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        out, lse = to_np(*run_gpu(wl, 0, workspace=ws))
+        compare(out, lse, ref_out, ref_lse, what=f"auto with {nbytes} B workspace")
+
+
+def test_forced_workspace_too_small():
+    wl = workloads.make_config("tiny")
+    ws = torch.empty(mla.get_workspace_size(wl.batch, wl.num_heads, 0, 1, 0), dtype=torch.uint8,
+                     device="cuda:0")
+    with pytest.raises(mla.MLAError) as e:
+        run_gpu(wl, 4, workspace=ws)
+    assert e.value.status == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_batch_zero():
+    q = torch.empty((0, 16, 576), dtype=torch.bfloat16, device="cuda:0")
+    kv = torch.zeros((1, 16, 576), dtype=torch.bfloat16, device="cuda:0")
+    bt = torch.zeros((0, 1), dtype=torch.int32, device="cuda:0")
+    sl = torch.zeros((0,), dtype=torch.int32, device="cuda:0")
+    out, lse = mla.decode(q, kv, bt, sl, scale=0.1)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 16, 512)
+
+
+@pytest.mark.parametrize("name", ["v2lite-64", "r1tp8", "fullhead", "fp8"])
+def test_full_size_finite(name):
+    wl = workloads.make_config(name)
+    out, lse = run_gpu(wl, 0)
+    assert torch.isfinite(out.float()).all() and torch.isfinite(lse).all()
+    # softmax weights sum to one, so |out| never exceeds the largest |value|
+    vmax = wl.kv.float().abs().max() if wl.kv_dtype == "bf16" else \
+        wl.kv.view(torch.float8_e4m3fn).float().abs().max() * wl.kv_scale
+    assert float(out.float().abs().max()) <= float(vmax) * 1.01
+
+
+# ---------------------------------------------------------------- combine
+
+def test_combine_matches_oracle_merge(orc):
+    gen = torch.Generator().manual_seed(31)
+    H = 20
+    counts = [0, 1, 2, 5, 16, 3]
+    indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(indptr[-1])
+    part_out = torch.randn((rows, H, 512), generator=gen, dtype=torch.float32)
+    part_lse = (torch.randn((rows, H), generator=gen, dtype=torch.float32) * 5)
+    part_lse[3, :4] = -float("inf")           # some empty splits
+    part_lse[indptr[3]:indptr[4], 7] = -float("inf")  # a request-head with only empty splits
+    out, lse = mla.combine(part_out.cuda(), part_lse.cuda(), torch.from_numpy(indptr).cuda())
+    torch.cuda.synchronize()
+    out, lse = to_np(out, lse)
+    for b in range(len(counts)):
+        r0, r1 = indptr[b], indptr[b + 1]
+        ref_out, ref_lse = orc.lse_merge(part_out[r0:r1].double().numpy(),
+                                         part_lse[r0:r1].double().numpy())
+        if r1 == r0:
+            ref_out = np.zeros((H, 512))
+            ref_lse = np.full(H, -np.inf)
+        compare(out[b], lse[b], ref_out, ref_lse, what=f"combine request {b}")
