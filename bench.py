@@ -31,7 +31,7 @@ MALL_BYTES = 256 << 20          # memory-side cache; smaller pools are rotated
 ROTATE_MIN_BYTES = 1 << 30
 KERNEL_SOURCES = [os.path.join(ROOT, "mla_paged_attention_amd", "csrc", f)
                   for f in ("mla_kernels.hip", "mla_internal.h")]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+PROFILES = os.path.join(ROOT, "profiles")
 D_K, D_V = 576, 512
 
 
@@ -45,6 +45,24 @@ def kernel_source_hash() -> str:
         with open(p, "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def measured_traffic(config: str, khash: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summaries (FETCH_SIZE + WRITE_SIZE, calibrated against a plain copy), or
+    None if none was taken for this workload with the current kernel source."""
+    if not os.path.isdir(PROFILES):
+        return None
+    for name in sorted(os.listdir(PROFILES)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(PROFILES, name)) as f:
+            for line in f:
+                if line.startswith("traffic_line:"):
+                    _, cfg, h, nbytes = line.split()
+                    if cfg == config and h == khash:
+                        return int(nbytes)
+    return None
 
 
 def algorithmic_bytes(wl) -> int:
@@ -94,6 +112,30 @@ def cpu_baseline(wl, target_s: float) -> dict:
             "tokens_per_s": round(tok / dt, 1)}
 
 
+def calib_copy(torch, dev, nbytes: int, reps: int) -> int:
+    """Plain copies (read n + write n bytes per launch) and sums (read n bytes)
+    of known size: the reference for scaling FETCH_SIZE / WRITE_SIZE counters
+    and the practically reachable HBM bandwidth."""
+    src = torch.randn(nbytes // 4, device=dev)
+    dst = torch.empty_like(src)
+    res = {"calib_bytes_per_launch": nbytes, "reps": reps}
+    for name, fn, moved in (("copy", lambda: dst.copy_(src), 2 * nbytes),
+                            ("sum", lambda: src.sum(), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        res[f"{name}_us"] = round(ms * 1e3, 2)
+        res[f"{name}_GBps"] = round(moved / (ms * 1e-3) / 1e9, 1)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -103,6 +145,9 @@ def main(argv=None) -> int:
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="instead of decoding, run plain device copies and reductions of "
+                         "MIB MiB (HBM counter calibration and practical bandwidth)")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -120,8 +165,10 @@ def main(argv=None) -> int:
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}))
         return 1
-    mla.library()  # fail loudly now if the HIP library is missing
     dev = torch.device("cuda:0")
+    if args.calib_copy:
+        return calib_copy(torch, dev, args.calib_copy << 20, max(args.steps, 1))
+    mla.library()  # fail loudly now if the HIP library is missing
 
     log(f"generating workload {args.config}")
     wl = workloads.make_config(args.config)
@@ -183,14 +230,7 @@ def main(argv=None) -> int:
     alg_flops = algorithmic_flops(wl)
     achieved = alg_bytes / (attn_avg * 1e-3) / 1e9
     mfma_peak = PEAK_MFMA_TFLOPS["fp8" if wl.kv_dtype == "fp8" else "bf16"]
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        entry = t.get(args.config)
-        if entry and entry.get("kernel_hash") == kernel_source_hash():
-            traffic = entry.get("bytes_per_launch")
-
+    traffic = measured_traffic(args.config, kernel_source_hash())
     result = {
         "metric": "MLA decode us/call + achieved HBM GB/s & MFMA % at bs=512, 16 heads",
         "value": round(ms_per_step * 1e3, 2),
