@@ -260,7 +260,7 @@ def main(argv=None) -> int:
                                              round(sorted(attn_ms)[(9 * len(attn_ms)) // 10] * 1e3, 2)]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4),
-                     "traffic": traffic, "kernel": "mla::attn_kernel<0>",
+                     "traffic": traffic, "kernel": "mla::attn_kernel<%d>" % int(wl.kv_dtype == "fp8"),
                      "algorithmic_bytes_per_launch": alg_bytes,
                      "mfma_frac": round(alg_flops / (attn_avg * 1e-3) / 1e12 / mfma_peak, 4)},
         "cpu_baseline": None,

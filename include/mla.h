@@ -116,8 +116,11 @@ size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_
  *  kv_dtype     mla_kv_dtype_t
  *  kv_scale     per-tensor dequantisation scale: exactly 1.0 for MLA_KV_BF16,
  *               finite and > 0 for MLA_KV_FP8_E4M3. In the fp8 path q is
- *               quantised to E4M3 inside the kernel, one scale per (request,
- *               head) row, and both products run on fp8 matrix cores.
+ *               quantised inside the kernel into two E4M3 rows per (request,
+ *               head) (the rounded row and its scaled rounding residual, each
+ *               with its own amax / 448 scale), P * 2^8 is carried the same
+ *               way as two E4M3 terms, and both products run on fp8 matrix
+ *               cores.
  *  workspace    caller-owned device scratch of at least workspace_bytes,
  *               256-byte aligned, needing no initialisation; distinct
  *               concurrent calls need distinct workspaces

@@ -1,0 +1,182 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load on a machine without a GPU, export every entry point
+include/mla.h declares, agree with the Python binding on every constant, and
+reject bad arguments before making any HIP call (so these paths are testable
+here). With valid arguments and no device it reports MLA_ERR_NO_DEVICE.
+No kernel is ever launched from this file: on a machine with a GPU the
+checks that would reach the device are skipped.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+import mla_paged_attention_amd as mla
+from mla_paged_attention_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla.h")
+HAS_GPU = torch.cuda.is_available()
+
+FAKE = 0x100000  # 256-byte aligned, never dereferenced (validation or no device)
+
+
+def header_text():
+    with open(HEADER) as f:
+        return f.read()
+
+
+def declared_functions():
+    return sorted(set(re.findall(r"^\s*[\w\s\*]*?\b(mla_\w+)\s*\(", header_text(), re.M)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(B.EXPORTED_SYMBOLS)
+
+
+def test_every_declared_symbol_is_exported():
+    lib = mla.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", mla.LIBRARY_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mla_\w+)", out))
+    for name in declared_functions():
+        assert name in exported, f"{name} declared in mla.h but not exported"
+        assert getattr(lib, name) is not None
+
+
+def test_constants_match_header():
+    text = header_text()
+    defines = dict(re.findall(r"#define (MLA_\w+) (\d+)", text))
+    assert int(defines["MLA_HEAD_DIM_K"]) == mla.HEAD_DIM_K == 576
+    assert int(defines["MLA_HEAD_DIM_V"]) == mla.HEAD_DIM_V == 512
+    assert int(defines["MLA_MAX_HEADS"]) == mla.MAX_HEADS == 128
+    assert int(defines["MLA_MAX_FORCED_SPLITS"]) == mla.MAX_FORCED_SPLITS == 16
+    enums = dict((k, int(v)) for k, v in re.findall(r"(MLA_\w+) = (-?\d+)", text))
+    for name in ("MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED",
+                 "MLA_ERR_WORKSPACE_TOO_SMALL", "MLA_ERR_NO_DEVICE", "MLA_ERR_HIP",
+                 "MLA_KV_BF16", "MLA_KV_FP8_E4M3"):
+        assert enums[name] == getattr(mla, name), name
+
+
+def test_status_strings_and_version():
+    for code in (0, -1, -2, -3, -4, -5):
+        s = mla.status_string(code)
+        assert s.startswith("MLA_") and "UNKNOWN" not in s
+    assert mla.status_string(7) == "MLA_ERR_UNKNOWN"
+    assert mla.abi_version() == 1
+
+
+# ------------------------------------------------------------------ workspace size
+
+def _layout(batch, heads, rows):
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    return 256 + 2 * a((batch + 1) * 4) + a(rows * heads * 4) + a(rows * heads * 512 * 4)
+
+
+def test_workspace_size_forced_mode():
+    for batch, heads, splits in ((1, 16, 1), (7, 20, 2), (512, 16, 16), (128, 128, 16)):
+        rows = batch * splits if splits > 1 else 0
+        assert mla.get_workspace_size(batch, heads, 4096, splits, 0) == _layout(batch, heads, rows)
+
+
+def test_workspace_size_auto_mode():
+    # 256 CUs, 16 heads: up to 256 partitions -> at most 2 * 255 partial rows.
+    assert mla.get_workspace_size(512, 16, 3072, 0, 0) == _layout(512, 16, 510)
+    assert mla.get_workspace_size(512, 16, 3072, 0, 256) == _layout(512, 16, 510)
+    # 128 heads: 8 head tiles share a CU, 32 partitions.
+    assert mla.get_workspace_size(128, 128, 32768, 0, 0) == _layout(128, 128, 62)
+    # Never more rows than every request split into one piece per 16-token unit.
+    assert mla.get_workspace_size(2, 16, 32, 0, 0) == _layout(2, 16, 4)
+    assert mla.get_workspace_size(2, 16, 16, 0, 0) == _layout(2, 16, 0)
+
+
+@pytest.mark.parametrize("args", [(-1, 16, 10, 0, 0), (1, 0, 10, 0, 0), (1, 129, 10, 0, 0),
+                                  (1, 16, -1, 0, 0), (1, 16, 10, -1, 0), (1, 16, 10, 17, 0)])
+def test_workspace_size_rejects(args):
+    assert mla.get_workspace_size(*args) == 0
+
+
+# ------------------------------------------------------------------ validation
+
+def _decode(**over):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, scale=0.07, heads=16,
+             bs=32, splits=0, batch=2, max_blocks=4, num_blocks=8, kv_dtype=0, kv_scale=1.0,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    lib = mla.library()
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return lib.mla_decode(vp(a["q"]), vp(a["kv"]), vp(a["bt"]), vp(a["sl"]), vp(a["out"]),
+                          vp(a["lse"]), a["scale"], a["heads"], a["bs"], a["splits"], a["batch"],
+                          a["max_blocks"], a["num_blocks"], a["kv_dtype"], a["kv_scale"],
+                          vp(a["ws"]), a["ws_bytes"], None)
+
+
+INVALID = [
+    dict(q=None), dict(kv=None), dict(bt=None), dict(sl=None), dict(out=None), dict(ws=None),
+    dict(q=FAKE + 8), dict(kv=FAKE + 4), dict(out=FAKE + 2), dict(bt=FAKE + 2),
+    dict(sl=FAKE + 1), dict(lse=FAKE + 2), dict(ws=FAKE + 16),
+    dict(heads=0), dict(heads=129), dict(bs=8), dict(bs=48), dict(bs=256), dict(splits=-1),
+    dict(splits=17), dict(batch=-1), dict(max_blocks=0), dict(num_blocks=0),
+    dict(kv_dtype=2), dict(kv_dtype=0, kv_scale=0.5), dict(kv_dtype=1, kv_scale=0.0),
+    dict(kv_dtype=1, kv_scale=float("inf")), dict(scale=float("nan")),
+    dict(max_blocks=1 << 30),
+]
+
+
+@pytest.mark.parametrize("over", INVALID, ids=[str(d) for d in INVALID])
+def test_decode_rejects_before_any_hip_call(over):
+    assert _decode(**over) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_decode_workspace_too_small():
+    assert _decode(ws_bytes=128) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    need = mla.get_workspace_size(2, 16, 4 * 32, 4, 0)
+    assert _decode(splits=4, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
+@pytest.mark.skipif(HAS_GPU, reason="would reach the device")
+def test_decode_without_device():
+    assert _decode() == mla.MLA_ERR_NO_DEVICE
+    assert _decode(kv_dtype=1, kv_scale=0.01) == mla.MLA_ERR_NO_DEVICE
+    assert _decode(batch=0, q=None, kv=None, bt=None, sl=None, out=None, ws=None) == \
+        mla.MLA_ERR_NO_DEVICE
+
+
+def test_decode_profiled_requires_events():
+    lib = mla.library()
+    args = [ctypes.c_void_p(FAKE)] * 5 + [None, 0.07, 16, 32, 0, 2, 4, 8, 0, 1.0,
+                                          ctypes.c_void_p(FAKE), 1 << 30, None]
+    assert lib.mla_decode_profiled(*args, None) == mla.MLA_ERR_INVALID_ARG
+    null_events = (ctypes.c_void_p * 4)(None, None, None, None)
+    assert lib.mla_decode_profiled(*args, null_events) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_combine_rejects():
+    lib = mla.library()
+    f = ctypes.c_void_p(FAKE)
+    assert lib.mla_combine(None, f, f, f, None, 2, 16, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(f, f, f, f, None, -1, 16, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(f, f, f, f, None, 2, 0, None) == mla.MLA_ERR_INVALID_ARG
+    assert lib.mla_combine(ctypes.c_void_p(FAKE + 4), f, f, f, None, 2, 16, None) == \
+        mla.MLA_ERR_INVALID_ARG
+    if not HAS_GPU:
+        assert lib.mla_combine(f, f, f, f, None, 2, 16, None) == mla.MLA_ERR_NO_DEVICE
+
+
+def test_binding_rejects_bad_tensors():
+    q = torch.zeros((2, 16, 512), dtype=torch.bfloat16)
+    kv = torch.zeros((4, 32, 576), dtype=torch.bfloat16)
+    bt = torch.zeros((2, 2), dtype=torch.int32)
+    sl = torch.zeros((2,), dtype=torch.int32)
+    with pytest.raises(ValueError):
+        mla.decode(q, kv, bt, sl, scale=0.1)
+    with pytest.raises(TypeError):
+        mla.decode(torch.zeros((2, 16, 576), dtype=torch.bfloat16),
+                   kv.float(), bt, sl, scale=0.1)
+    with pytest.raises(ValueError):
+        mla.decode(torch.zeros((2, 16, 576), dtype=torch.bfloat16), kv, bt.long(), sl,
+                   scale=0.1)
