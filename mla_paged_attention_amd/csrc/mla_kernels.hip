@@ -367,16 +367,17 @@ __device__ void attend_piece(const AttnArgs& a, AttnSmem& sm, int b, int ht, int
   if constexpr (!KV_FP8) {
     // B operand of the logit MFMA: head c, features 32 s + 8 g .. + 7.
     const uint32_t* qrow = &sm.q[c * kQRowDwordsBf16 + 4 * g];
-    for (int u = u0 + wave; u < u_end; u += kWaves) {
-      int nvalid;
-      const uint8_t* base = unit_base(u, nvalid);
-      // K operand: lane holds token c, features 32 s + 8 g .. + 7.
-      u32x4_t kf[kQChunks];
-      {
-        const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(base + c * kRowBytesKv) + g;
+    // K operand of unit u: lane holds token c, features 32 s + 8 g .. + 7.
+    auto load_k = [&](const uint8_t* base, u32x4_t (&kf)[kQChunks]) {
+      const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(base + c * kRowBytesKv) + g;
 #pragma unroll
-        for (int s = 0; s < kQChunks; ++s) kf[s] = kp[4 * s];
-      }
+      for (int s = 0; s < kQChunks; ++s) kf[s] = kp[4 * s];
+    };
+    // One unit whose K fragment is already in kf; the K fragment of the
+    // wave's next unit is requested into kn before any of this unit's math,
+    // so HBM traffic of the next unit overlaps this unit's compute.
+    auto step = [&](int u, const uint8_t* base, int nvalid, u32x4_t (&kf)[kQChunks],
+                    u32x4_t (&kn)[kQChunks], const uint8_t*& nbase, int& nnvalid) {
       // V rows for P.V: lane holds tokens 4 g + r, features 128 beta + 8 c .. + 7.
       u32x4_t vf[4][4];
 #pragma unroll
@@ -385,6 +386,10 @@ __device__ void attend_piece(const AttnArgs& a, AttnSmem& sm, int b, int ht, int
             reinterpret_cast<const u32x4_t*>(base + (4 * g + r) * kRowBytesKv) + c;
 #pragma unroll
         for (int beta = 0; beta < 4; ++beta) vf[beta][r] = vp[16 * beta];
+      }
+      if (u + kWaves < u_end) {
+        nbase = unit_base(u + kWaves, nnvalid);
+        load_k(nbase, kn);
       }
       // Logits: S^T[token][head] = K . q^T; lane gets tokens 4 g + r of head c.
       f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -437,6 +442,22 @@ __device__ void attend_piece(const AttnArgs& a, AttnSmem& sm, int b, int ht, int
               pa, __builtin_bit_cast(s16x4_t, vo), acc[beta * 8 + 2 * i + 1], 0, 0, 0);
         }
       }
+    };
+    u32x4_t ka[kQChunks], kb[kQChunks];
+    int u = u0 + wave;
+    int nv_a = 0, nv_b = 0;
+    const uint8_t* base_a = nullptr;
+    const uint8_t* base_b = nullptr;
+    if (u < u_end) {
+      base_a = unit_base(u, nv_a);
+      load_k(base_a, ka);
+    }
+    for (; u < u_end; u += kWaves) {
+      step(u, base_a, nv_a, ka, kb, base_b, nv_b);
+#pragma unroll
+      for (int s2 = 0; s2 < kQChunks; ++s2) ka[s2] = kb[s2];
+      base_a = base_b;
+      nv_a = nv_b;
     }
   } else {
     // E4M3 cache: units go in pairs (u, u + kWaves) so that one P.V MFMA
@@ -604,18 +625,11 @@ __device__ void attend_piece(const AttnArgs& a, AttnSmem& sm, int b, int ht, int
   __syncthreads();  // LDS is reused by the next piece
 }
 
-template <int KV_FP8>
-__global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnArgs a) {
-  __shared__ AttnSmem sm;
-  // Workgroups are dispatched to the 8 XCDs round robin. Give the head tiles
-  // of one partition the same XCD (shared L2) and adjacent dispatch slots.
-  const int lin = blockIdx.x;
-  const int xcd = lin & 7, slot = lin >> 3;
-  const int ht = slot % a.head_tiles;
-  const int part = (slot / a.head_tiles) * 8 + xcd;
-
-  // Walk the pieces of this partition: one piece in forced mode, every
-  // request overlapping the partition's cost range in balanced mode.
+// Partition -> pieces. Calls fn(b, u0, u1, piece, pieces) for every piece of
+// partition `part`: one piece in forced mode, every request overlapping the
+// partition's cost range in balanced mode. Uniform across the workgroup.
+template <typename Fn>
+__device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, Fn&& fn) {
   int b, end = 0, P = 1;
   if (a.num_splits > 0) {
     if (part >= a.batch * a.num_splits) return;
@@ -661,10 +675,398 @@ __global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnArgs a) {
       pieces = (ue - 1) / P - ub / P + 1;
       last = ue >= end || b + 1 >= a.batch;
     }
-    attend_piece<KV_FP8>(a, sm, b, ht, u0, u1, piece, pieces);
+    fn(b, u0, u1, piece, pieces);
     if (last) return;
     ++b;
   }
+}
+
+template <int KV_FP8>
+__global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnArgs a) {
+  __shared__ AttnSmem sm;
+  // Workgroups are dispatched to the 8 XCDs round robin. Give the head tiles
+  // of one partition the same XCD (shared L2) and adjacent dispatch slots.
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int ht = slot % a.head_tiles;
+  const int part = (slot / a.head_tiles) * 8 + xcd;
+  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
+    attend_piece<KV_FP8>(a, sm, b, ht, u0, u1, piece, pieces);
+  });
+}
+
+// ----------------------------------------------------------------------------
+// Tile-streaming attention (bf16 cache, one 16-head tile per workgroup).
+//
+// The four waves share every KV tile: 32 tokens (two 16-token units, each in
+// one page) are copied HBM -> LDS with coalesced direct-to-LDS loads into a
+// ring of kStages stages, kept kStages - 2 tiles ahead of the tile being
+// consumed, so that the bytes in flight live in LDS rather than registers.
+// Every wave computes the same 16 x 32 logit tile and softmax (q in
+// registers, K from LDS) and owns 128 of the 512 output features for P.V, so
+// no cross-wave merge is needed. The ring's waits are explicit: each thread
+// issues kDmaPerThread loads per tile and no other vector-memory operation
+// inside the loop, so "tile j landed" is vmcnt <= kDmaPerThread * (tiles
+// issued after j). LDS reads are issued as ds_read_b128 statements followed
+// by an explicit lgkmcnt wait that the results pass through.
+//
+// LDS tile layout: row t (token) holds 72 sixteen-byte chunks; chunk ch of
+// row t sits in slot ch ^ (t & 7), so that 8 rows read at the same chunk, or
+// 8 consecutive chunks of one row, hit 8 different 4-bank groups.
+
+constexpr int kTile = 2 * kUnit;                      // tokens per LDS tile
+constexpr int kStages = 4;                            // LDS ring depth
+constexpr int kRowChunks = kRowBytes / 16;            // 72 chunks per cached row
+constexpr int kTileBytesBf16 = kTile * kRowBytes;     // 36864
+constexpr int kDmaPerThread = kTile * kRowChunks / kThreads;  // 9
+static_assert(kTile * kRowChunks == kDmaPerThread * kThreads, "tile must split evenly");
+
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// Wait until at most `after` (clamped to MAX) later tiles' loads are pending.
+template <int MAX>
+__device__ __forceinline__ void wait_ring(int after) {
+  if constexpr (MAX == 0) {
+    wait_vmem<0>();
+  } else {
+    if (after >= MAX)
+      wait_vmem<MAX * kDmaPerThread>();
+    else
+      wait_ring<MAX - 1>(after);
+  }
+}
+
+__device__ __forceinline__ void wave_barrier_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// LDS reads of one operand set, issued and completed inside one asm
+// statement (no copy of a destination register can be scheduled between the
+// read and its wait).
+#define MLA_DSR(i, base, off) "ds_read_b128 %" #i ", %" #base " offset:" #off "\n\t"
+
+// K operand of one 16-token unit: chunk 2k of row t at a_even + 128 k, chunk
+// 2k + 1 at a_odd + 128 k (the XOR swizzle folded into the two bases).
+__device__ __forceinline__ void lds_read_k(uint32_t a_even, uint32_t a_odd,
+                                           u32x4_t (&kf)[kQChunks]) {
+  asm volatile(
+      MLA_DSR(0, 18, 0) MLA_DSR(1, 19, 0) MLA_DSR(2, 18, 128) MLA_DSR(3, 19, 128)
+      MLA_DSR(4, 18, 256) MLA_DSR(5, 19, 256) MLA_DSR(6, 18, 384) MLA_DSR(7, 19, 384)
+      MLA_DSR(8, 18, 512) MLA_DSR(9, 19, 512) MLA_DSR(10, 18, 640) MLA_DSR(11, 19, 640)
+      MLA_DSR(12, 18, 768) MLA_DSR(13, 19, 768) MLA_DSR(14, 18, 896) MLA_DSR(15, 19, 896)
+      MLA_DSR(16, 18, 1024) MLA_DSR(17, 19, 1024) "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]),
+        "=&v"(kf[6]), "=&v"(kf[7]), "=&v"(kf[8]), "=&v"(kf[9]), "=&v"(kf[10]), "=&v"(kf[11]),
+        "=&v"(kf[12]), "=&v"(kf[13]), "=&v"(kf[14]), "=&v"(kf[15]), "=&v"(kf[16]),
+        "=&v"(kf[17])
+      : "v"(a_even), "v"(a_odd)
+      : "memory");
+}
+
+// Eight V rows (16 bytes each) at eight addresses.
+__device__ __forceinline__ void lds_read_v8(const uint32_t (&ad)[8], u32x4_t (&v)[8]) {
+  asm volatile(
+      MLA_DSR(0, 8, 0) MLA_DSR(1, 9, 0) MLA_DSR(2, 10, 0) MLA_DSR(3, 11, 0) MLA_DSR(4, 12, 0)
+      MLA_DSR(5, 13, 0) MLA_DSR(6, 14, 0) MLA_DSR(7, 15, 0) "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7])
+      : "memory");
+}
+
+// Wave-uniform load through the scalar unit (counted by lgkmcnt, not vmcnt,
+// so it does not disturb the vector-memory pipeline of the KV ring).
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
+// Wave-specialised variant of the tile stream. Waves 0..3 issue the ring's
+// loads and own 128 output features each for P.V; wave 4 (the logit wave)
+// computes the 16 x 32 logit tile, the online softmax and P for tile s while
+// the P.V waves consume tile s - 1. P (already in the A-operand layout), the
+// frame-rescale factors and a rescale flag pass through double-buffered LDS
+// slots; one barrier per step. Ring: at step s the P.V waves read tile
+// s - 1, the logit wave tile s, tiles s + 1 and s + 2 are in flight.
+constexpr int kPvWaves = 4;
+constexpr int kWsThreads = 64 * (kPvWaves + 1);
+
+__device__ __forceinline__ void wave_barrier_lds() {
+  // LDS writes of this wave complete before anyone passes the barrier.
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  wave_barrier_all();
+}
+
+__global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
+  __shared__ uint8_t ring[kStages][kTileBytesBf16];
+  __shared__ u32x4_t pbuf[2][64];          // P of the step's tile, one A operand per lane
+  __shared__ float abuf[2][kHeadTile];     // frame rescale factor per head
+  __shared__ int fbuf[2];                  // 1: rescale the accumulators first
+  __shared__ float lbuf[kHeadTile];        // final softmax denominators
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const bool logit_wave = wave == kPvWaves;
+  const int H = a.num_heads;
+
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int ht = slot % a.head_tiles;
+  const int part = (slot / a.head_tiles) * 8 + xcd;
+  const int h0 = ht * kHeadTile;
+
+  // Per-thread DMA map of the P.V waves: load i fills ring slot i * 256 + tid.
+  uint32_t dma_off[kDmaPerThread];
+  uint32_t dma_hi = 0;
+#pragma unroll
+  for (int i = 0; i < kDmaPerThread; ++i) {
+    const int pos = i * kThreads + (tid & (kThreads - 1));
+    const int t = pos / kRowChunks, sl = pos - (pos / kRowChunks) * kRowChunks;
+    const int ch = sl ^ (t & 7);
+    dma_off[i] = uint32_t((t & 15) * kRowBytes + ch * 16);
+    dma_hi |= uint32_t(t >> 4) << i;
+  }
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (void __attribute__((address_space(3)))*)(&ring[0][0])));
+  const int bs_mask = (1 << a.bs_log2) - 1;
+
+  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
+    const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
+    const int u_end = min(u1, (n + kUnit - 1) / kUnit);
+    const int ntiles = u_end > u0 ? (u_end - u0 + 1) / 2 : 0;
+    const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
+    // Tokens of tile k's two units.
+    auto tile_nv = [&](int k, int (&nv)[2]) {
+      const int t0 = (u0 + 2 * k) * kUnit;
+      nv[0] = min(kUnit, n - t0);
+      nv[1] = u0 + 2 * k + 1 < u_end ? min(kUnit, n - t0 - kUnit) : 0;
+    };
+    // Rows of unit u; a block id outside the cache is replaced by block 0.
+    auto unit_rows = [&](int u, bool valid) -> const uint8_t* {
+      const int t0 = u * kUnit;
+      int blk = valid ? scalar_load_i32(bt_row + (t0 >> a.bs_log2)) : 0;
+      if (blk < 0 || blk >= a.num_blocks) blk = 0;
+      return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowBytes;
+    };
+    auto issue_tile = [&](int k) {
+      int nv[2];
+      tile_nv(k, nv);
+      const uint8_t* r0 = unit_rows(u0 + 2 * k, true);
+      const uint8_t* r1 = nv[1] > 0 ? unit_rows(u0 + 2 * k + 1, true) : r0;
+      uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
+#pragma unroll
+      for (int i = 0; i < kDmaPerThread; ++i) {
+        const uint8_t* src = ((dma_hi >> i) & 1 ? r1 : r0) + dma_off[i];
+        __builtin_amdgcn_global_load_lds(
+            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0, 0);
+      }
+    };
+
+    wave_barrier_all();  // the ring and slots of the previous piece are free
+    u32x4_t qf[kQChunks];
+    if (logit_wave) {
+      // q fragment: head h0 + c (padded heads repeat head H - 1), features
+      // 32 s + 8 g .. + 7.
+      const u32x4_t* qp =
+          reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + min(h0 + c, H - 1)) * kDK) + g;
+#pragma unroll
+      for (int s2 = 0; s2 < kQChunks; ++s2) qf[s2] = qp[4 * s2];
+      wait_vmem<0>();
+    } else {
+      for (int k = 0; k < 2 && k < ntiles; ++k) issue_tile(k);
+    }
+
+    f32x4_t acc[8];  // P.V waves: heads 4 g + r, features 128 wave + 8 c + i
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY;  // logit wave: accumulation frame of head c (log2 domain)
+    float l_run = 0.f;        // logit wave: lane's share of head c's denominator
+
+    for (int s = 0; s <= ntiles; ++s) {
+      if (!logit_wave && s < ntiles) wait_ring<1>(ntiles - 1 - s);  // tile s landed
+      wave_barrier_lds();
+      if (logit_wave) {
+        if (s < ntiles) {
+          const uint32_t st = ring_lds + uint32_t(s % kStages) * kTileBytesBf16;
+          int nv[2];
+          tile_nv(s, nv);
+          float x[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int t = h * kUnit + c;
+            const uint32_t y = uint32_t(g ^ (c & 7));
+            const uint32_t row = st + uint32_t(t * kRowBytes);
+            u32x4_t kf[kQChunks];
+            lds_read_k(row + 16 * y, row + 16 * (y ^ 4), kf);
+            f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s2 = 0; s2 < kQChunks; ++s2)
+              sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                  __builtin_bit_cast(bf16x8_t, kf[s2]), __builtin_bit_cast(bf16x8_t, qf[s2]), sc,
+                  0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              x[h][r] = (4 * g + r < nv[h]) ? sc[r] * a.scale_log2 : -INFINITY;
+          }
+          float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                           fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+          mt = fmaxf(mt, __shfl_xor(mt, 16));
+          mt = fmaxf(mt, __shfl_xor(mt, 32));
+          const bool move = __ballot(mt > m_ref + 8.f) != 0ull;  // wave-uniform
+          if (move) {
+            const float m_new = fmaxf(m_ref, mt);
+            const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+            l_run *= alpha;
+            m_ref = m_new;
+            if (g == 0) abuf[s & 1][c] = alpha;
+          }
+          if (lane == 0) fbuf[s & 1] = move ? 1 : 0;
+          const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+          float p[2][4];
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_use);
+          l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                   ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+          // A operand of P.V: k slots 8 g .. + 3 = unit 0 tokens 4 g + r,
+          // 8 g + 4 .. + 7 = unit 1 tokens 4 g + r.
+          bf16x8_t pa;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pa[r] = (__bf16)p[0][r];
+            pa[4 + r] = (__bf16)p[1][r];
+          }
+          pbuf[s & 1][lane] = __builtin_bit_cast(u32x4_t, pa);
+        }
+        if (s == ntiles - 1 || ntiles == 0) {
+          float l_c = l_run + __shfl_xor(l_run, 16);
+          l_c += __shfl_xor(l_c, 32);
+          if (g == 0) {
+            lbuf[c] = l_c;
+            if (h0 + c < H) {
+              const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
+              if (pieces == 1) {
+                if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
+              } else {
+                a.part_lse[size_t(a.row_ptr[b] + piece) * H + h0 + c] = lse_v;
+              }
+            }
+          }
+        }
+      } else {
+        if (s + 2 < ntiles) issue_tile(s + 2);
+        if (s >= 1) {
+          const int k = s - 1;
+          if (fbuf[k & 1]) {
+            // acc <- diag(alpha) acc on the matrix cores: 4 fp32 MFMAs per
+            // 16 x 16 block, k slot g of MFMA m carrying row 4 g + m.
+            const float alpha = abuf[k & 1][c];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+              for (int m = 0; m < 4; ++m)
+                z = __builtin_amdgcn_mfma_f32_16x16x4f32(c == 4 * g + m ? alpha : 0.f,
+                                                          acc[i][m], z, 0, 0, 0);
+              acc[i] = z;
+            }
+          }
+          const bf16x8_t pa = __builtin_bit_cast(bf16x8_t, pbuf[k & 1][lane]);
+          const uint32_t st = ring_lds + uint32_t(k % kStages) * kTileBytesBf16;
+          int nv[2];
+          tile_nv(k, nv);
+          // V rows: tokens 16 h + 4 g + r, features 128 wave + 8 c .. + 7.
+          u32x4_t vf[2][4];
+          {
+            uint32_t ad[8];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const int t = h * kUnit + 4 * g + r;
+                ad[4 * h + r] =
+                    st + uint32_t(t * kRowBytes) + 16u * uint32_t(16 * wave + (c ^ (t & 7)));
+              }
+            }
+            u32x4_t v8[8];
+            lds_read_v8(ad, v8);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vf[i >> 2][i & 3] = v8[i];
+          }
+          // Masked tokens contribute exactly 0 even if their bytes are NaN.
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if (nv[h] < kUnit) {
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                const unsigned keep = (4 * g + r < nv[h]) ? 0xffffffffu : 0u;
+                vf[h][r] &= keep;
+              }
+            }
+          }
+          // Feature 128 wave + 8 c + e of the 8 tokens as one B operand.
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const unsigned a0 = vf[0][0][i], a1 = vf[0][1][i], a2 = vf[0][2][i],
+                           a3 = vf[0][3][i];
+            const unsigned b0 = vf[1][0][i], b1 = vf[1][1][i], b2 = vf[1][2][i],
+                           b3 = vf[1][3][i];
+            const u32x4_t ve =
+                u32x4_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16),
+                        (b0 & 0xffffu) | (b1 << 16), (b2 & 0xffffu) | (b3 << 16)};
+            const u32x4_t vo =
+                u32x4_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u),
+                        (b0 >> 16) | (b1 & 0xffff0000u), (b2 >> 16) | (b3 & 0xffff0000u)};
+            acc[2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                pa, __builtin_bit_cast(bf16x8_t, ve), acc[2 * i], 0, 0, 0);
+            acc[2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                pa, __builtin_bit_cast(bf16x8_t, vo), acc[2 * i + 1], 0, 0, 0);
+          }
+        }
+      }
+    }
+    wave_barrier_lds();  // lbuf is complete
+
+    if (!logit_wave) {
+      // Epilogue: heads 4 g + r, features 128 wave + 8 c .. + 7 in acc[0..7][r].
+      const bool final_out = pieces == 1;
+      const int row = final_out ? 0 : a.row_ptr[b] + piece;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * g + r;
+        const int h = h0 + hh;
+        const float lh = lbuf[hh];
+        const float inv = lh > 0.f ? 1.f / lh : 0.f;
+        if (h < H) {
+          const int d = 128 * wave + 8 * c;
+          if (final_out) {
+            u32x4_t pk;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pk[e] = unsigned(bf16_bits(acc[2 * e][r] * inv)) |
+                      (unsigned(bf16_bits(acc[2 * e + 1][r] * inv)) << 16);
+            *reinterpret_cast<u32x4_t*>(a.out + (size_t(b) * H + h) * kDV + d) = pk;
+          } else {
+            float* dst = a.part_out + (size_t(row) * H + h) * kDV + d;
+            *reinterpret_cast<f32x4_t*>(dst) =
+                f32x4_t{acc[0][r], acc[1][r], acc[2][r], acc[3][r]} * inv;
+            *reinterpret_cast<f32x4_t*>(dst + 4) =
+                f32x4_t{acc[4][r], acc[5][r], acc[6][r], acc[7][r]} * inv;
+          }
+        }
+      }
+    }
+  });
 }
 
 // ----------------------------------------------------------------------------
@@ -727,7 +1129,7 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
   if (kv_fp8)
     hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(kThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL(attn_kernel<0>, grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL(attn_ws_kernel, grid, dim3(kWsThreads), 0, stream, args);
   return hipGetLastError();
 }
 
