@@ -94,9 +94,9 @@ size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_
  *  seq_lens     [batch] int32, 0 <= seq_lens[b] <= max_blocks_per_seq *
  *               block_size. A request with seq_len 0 gets out = 0,
  *               lse = -inf. Lengths beyond the table capacity are clamped to
- *               it, and block ids outside [0, num_blocks) are skipped (their
- *               tokens contribute nothing): the result of such a request is
- *               then not meaningful, but nothing outside the cache is read.
+ *               it, and a block id outside [0, num_blocks) is read as block 0:
+ *               the result of such a request is then not meaningful, but
+ *               nothing outside the cache is ever read.
  *  out          [batch][num_heads][512] bf16 (fp32 accumulation, round to
  *               nearest even), 16-byte aligned, fully overwritten
  *  lse          [batch][num_heads] fp32 natural-log LSE of the scaled logits,
@@ -160,7 +160,7 @@ mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
  *  partial_out  [total_rows][num_heads][512] fp32, each row already divided
  *               by its own softmax denominator, 16-byte aligned
  *  partial_lse  [total_rows][num_heads] fp32 natural-log LSE; -inf marks an
- *               empty split (weight 0, its partial_out is not read)
+ *               empty split (weight 0; its partial_out values are ignored)
  *  split_indptr [batch + 1] int32, non-decreasing, split_indptr[0] = 0:
  *               request b owns rows split_indptr[b] .. split_indptr[b+1]-1
  *  out          [batch][num_heads][512] bf16: sum_s w_s o_s / sum_s w_s with

@@ -1070,46 +1070,56 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// LSE combine: one workgroup per (request, 16-head tile).
+// LSE combine: one workgroup per (request, 16-head tile, 64-feature chunk);
+// thread (head hh, sub) merges features 4 sub .. 4 sub + 3 of the chunk,
+// with kCombineUnroll partial rows in flight.
+constexpr int kCombineChunk = 64;
+constexpr int kCombineChunks = kDV / kCombineChunk;  // 8
+constexpr int kCombineUnroll = 8;
+
 __global__ void __launch_bounds__(256) combine_kernel(const float* part_out, const float* part_lse,
                                                       const int32_t* row_ptr, uint16_t* out,
                                                       float* lse, int32_t batch, int32_t H,
                                                       int32_t tiles, int zero_empty) {
-  const int b = blockIdx.x / tiles, ht = blockIdx.x - (blockIdx.x / tiles) * tiles;
+  const int blk = blockIdx.x;
+  const int chunk = blk % kCombineChunks;
+  const int bt = blk / kCombineChunks;
+  const int b = bt / tiles, ht = bt - (bt / tiles) * tiles;
   const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
   if (nr <= 0 && !zero_empty) return;
   const int tid = threadIdx.x;
   const int h = ht * kHeadTile + (tid >> 4);
   if (h >= H) return;
-  const int sub = tid & 15;
+  const int d = chunk * kCombineChunk + 4 * (tid & 15);
   float M = -INFINITY;
   for (int s = 0; s < nr; ++s) M = fmaxf(M, part_lse[size_t(r0 + s) * H + h]);
-  f32x4_t acc[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   if (M != -INFINITY) {
-    for (int s = 0; s < nr; ++s) {
-      const float ls = part_lse[size_t(r0 + s) * H + h];
-      if (ls == -INFINITY) continue;
-      const float w = fast_exp2((ls - M) * kLog2e);
-      W += w;
-      const f32x4_t* src = reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s) * H + h) * kDV);
+    for (int s0 = 0; s0 < nr; s0 += kCombineUnroll) {
+      f32x4_t v[kCombineUnroll];
+      float w[kCombineUnroll];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] += w * src[i * 16 + sub];
+      for (int k = 0; k < kCombineUnroll; ++k) {
+        const int s = min(s0 + k, nr - 1);
+        const float ls = part_lse[size_t(r0 + s) * H + h];
+        w[k] = (s0 + k < nr && ls != -INFINITY) ? fast_exp2((ls - M) * kLog2e) : 0.f;
+        v[k] = *reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s) * H + h) * kDV + d);
+      }
+#pragma unroll
+      for (int k = 0; k < kCombineUnroll; ++k) {
+        if (w[k] != 0.f) acc += w[k] * v[k];  // an empty row's values are never used
+        W += w[k];
+      }
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  uint16_t* dst = out + (size_t(b) * H + h) * kDV;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    f32x4_t v = acc[i] * inv;
-    u32x2_t pk;
-    pk[0] = unsigned(bf16_bits(v[0])) | (unsigned(bf16_bits(v[1])) << 16);
-    pk[1] = unsigned(bf16_bits(v[2])) | (unsigned(bf16_bits(v[3])) << 16);
-    *reinterpret_cast<u32x2_t*>(dst + (i * 16 + sub) * 4) = pk;
-  }
-  if (sub == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
+  const f32x4_t o = acc * inv;
+  u32x2_t pk;
+  pk[0] = unsigned(bf16_bits(o[0])) | (unsigned(bf16_bits(o[1])) << 16);
+  pk[1] = unsigned(bf16_bits(o[2])) | (unsigned(bf16_bits(o[3])) << 16);
+  *reinterpret_cast<u32x2_t*>(out + (size_t(b) * H + h) * kDV + d) = pk;
+  if (chunk == 0 && (tid & 15) == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
 // ----------------------------------------------------------------------------
@@ -1137,7 +1147,8 @@ hipError_t launch_combine(const float* part_out, const float* part_lse,
                           const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
                           int32_t num_heads, int zero_empty, hipStream_t stream) {
   const int tiles = head_tiles(num_heads);
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(batch) * unsigned(tiles)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(batch) * unsigned(tiles) * kCombineChunks),
+                     dim3(256), 0, stream,
                      part_out, part_lse, row_ptr, out, lse, batch, num_heads, tiles, zero_empty);
   return hipGetLastError();
 }
