@@ -140,7 +140,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
     w = mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits));
   } else {
     // Largest partition count whose partial rows fit the given workspace.
-    max_parts = mla::max_partitions(dev.cus, a.num_heads);
+    max_parts = mla::max_partitions(dev.cus, a.num_heads, a.kv_dtype == MLA_KV_FP8_E4M3);
     while (max_parts > 1 &&
            mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, max_parts, cap)).total >
                a.workspace_bytes)
@@ -188,6 +188,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.cap_tokens = int32_t(cap);
   args.num_splits = a.num_splits;
   args.head_tiles = mla::head_tiles(a.num_heads);
+  args.head_groups = (args.head_tiles + 3) / 4;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
   int64_t parts_launched = (parts + 7) / 8 * 8;
   if (parts_launched * args.head_tiles > INT32_MAX) return MLA_ERR_INVALID_ARG;
@@ -219,7 +220,7 @@ size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_
   if (num_cus <= 0) num_cus = kDefaultCus;
   int64_t rows = num_splits > 0
                      ? forced_rows(batch, num_splits)
-                     : auto_rows(batch, mla::max_partitions(num_cus, num_heads), max_seq_len);
+                     : auto_rows(batch, mla::max_partitions(num_cus, num_heads, 0), max_seq_len);
   return mla::workspace_layout(batch, num_heads, rows).total;
 }
 

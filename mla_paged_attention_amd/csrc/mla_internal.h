@@ -51,10 +51,17 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
 
 inline int head_tiles(int num_heads) { return (num_heads + kHeadTile - 1) / kHeadTile; }
 
+// Workgroups per partition: the bf16 many-head kernel puts four head tiles
+// in one workgroup; the other kernels use one workgroup per head tile.
+inline int workgroups_per_partition(int num_heads, int kv_fp8) {
+  const int ht = head_tiles(num_heads);
+  return (kv_fp8 || ht == 1) ? ht : (ht + 3) / 4;
+}
+
 // Upper bound on balanced partitions for a device with `num_cus` CUs: one
-// attention workgroup per CU at a time, shared by the head tiles.
-inline int64_t max_partitions(int64_t num_cus, int64_t num_heads) {
-  int64_t g = num_cus / head_tiles(int(num_heads));
+// attention workgroup per CU at a time.
+inline int64_t max_partitions(int64_t num_cus, int64_t num_heads, int kv_fp8) {
+  int64_t g = num_cus / workgroups_per_partition(int(num_heads), kv_fp8);
   return g < 8 ? 8 : g;
 }
 
@@ -79,7 +86,8 @@ struct AttnArgs {
   int32_t bs_log2;
   int32_t cap_tokens;        // max_blocks * block_size
   int32_t num_splits;        // 0 = balanced plan
-  int32_t head_tiles;
+  int32_t head_tiles;        // ceil(num_heads / 16)
+  int32_t head_groups;       // workgroups per partition of the many-head kernel
 };
 
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,

@@ -1070,6 +1070,249 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// Many-head tile stream (bf16 cache, more than 16 heads). Each workgroup
+// covers up to four 16-head tiles: wave w owns head tile 4 hg + w (hg = the
+// workgroup's head group) with all 512 output features, so the logits of a
+// head tile are computed once and the KV tile in LDS feeds four head tiles.
+// Head groups of one partition run on the same XCD in adjacent dispatch
+// slots, so the second group's ring loads are L2 hits. Ring, DMA map and
+// waits as in the 16-head kernels.
+__global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
+  __shared__ uint8_t ring[kStages][kTileBytesBf16];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int H = a.num_heads;
+
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int hg = slot % a.head_groups;
+  const int part = (slot / a.head_groups) * 8 + xcd;
+  const int ht = 4 * hg + wave;
+  const bool active = ht < a.head_tiles;  // inactive waves only stream the ring
+  const int h0 = ht * kHeadTile;
+
+  uint32_t dma_off[kDmaPerThread];
+  uint32_t dma_hi = 0;
+#pragma unroll
+  for (int i = 0; i < kDmaPerThread; ++i) {
+    const int pos = i * kThreads + tid;
+    const int t = pos / kRowChunks, sl = pos - (pos / kRowChunks) * kRowChunks;
+    const int ch = sl ^ (t & 7);
+    dma_off[i] = uint32_t((t & 15) * kRowBytes + ch * 16);
+    dma_hi |= uint32_t(t >> 4) << i;
+  }
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (void __attribute__((address_space(3)))*)(&ring[0][0])));
+  const int bs_mask = (1 << a.bs_log2) - 1;
+
+  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
+    const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
+    const int u_end = min(u1, (n + kUnit - 1) / kUnit);
+    const int ntiles = u_end > u0 ? (u_end - u0 + 1) / 2 : 0;
+    const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
+    auto tile_nv = [&](int k, int (&nv)[2]) {
+      const int t0 = (u0 + 2 * k) * kUnit;
+      nv[0] = min(kUnit, n - t0);
+      nv[1] = u0 + 2 * k + 1 < u_end ? min(kUnit, n - t0 - kUnit) : 0;
+    };
+    auto unit_rows = [&](int u) -> const uint8_t* {
+      const int t0 = u * kUnit;
+      int blk = scalar_load_i32(bt_row + (t0 >> a.bs_log2));
+      if (blk < 0 || blk >= a.num_blocks) blk = 0;
+      return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowBytes;
+    };
+    auto issue_tile = [&](int k) {
+      int nv[2];
+      tile_nv(k, nv);
+      const uint8_t* r0 = unit_rows(u0 + 2 * k);
+      const uint8_t* r1 = nv[1] > 0 ? unit_rows(u0 + 2 * k + 1) : r0;
+      uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
+#pragma unroll
+      for (int i = 0; i < kDmaPerThread; ++i) {
+        const uint8_t* src = ((dma_hi >> i) & 1 ? r1 : r0) + dma_off[i];
+        __builtin_amdgcn_global_load_lds(
+            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0, 0);
+      }
+    };
+
+    wave_barrier_all();  // the ring of the previous piece is consumed
+    // q fragment of this wave's head tile (padded heads repeat head H - 1).
+    u32x4_t qf[kQChunks];
+    {
+      const int hq = min(h0 + c, H - 1);
+      const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + hq) * kDK) + g;
+#pragma unroll
+      for (int s2 = 0; s2 < kQChunks; ++s2) qf[s2] = qp[4 * s2];
+    }
+    wait_vmem<0>();
+    for (int k = 0; k < kStages - 1 && k < ntiles; ++k) issue_tile(k);
+
+    f32x4_t acc[32];  // heads 4 g + r; features 128 beta + 8 c + e in acc[8 beta + e]
+#pragma unroll
+    for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_ref = -INFINITY;  // frame of head c (log2 domain)
+    float l_run = 0.f;        // lane's share of head c's denominator
+
+    for (int j = 0; j < ntiles; ++j) {
+      wait_ring<kStages - 2>(ntiles - 1 - j);
+      wave_barrier_all();
+      if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
+      if (!active) continue;
+
+      const uint32_t st = ring_lds + uint32_t(j % kStages) * kTileBytesBf16;
+      int nv[2];
+      tile_nv(j, nv);
+      float x[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int t = h * kUnit + c;
+        const uint32_t y = uint32_t(g ^ (c & 7));
+        const uint32_t row = st + uint32_t(t * kRowBytes);
+        u32x4_t kf[kQChunks];
+        lds_read_k(row + 16 * y, row + 16 * (y ^ 4), kf);
+        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s2 = 0; s2 < kQChunks; ++s2)
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s2]),
+                                                       __builtin_bit_cast(bf16x8_t, qf[s2]), sc,
+                                                       0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          x[h][r] = (4 * g + r < nv[h]) ? sc[r] * a.scale_log2 : -INFINITY;
+      }
+      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      mt = fmaxf(mt, __shfl_xor(mt, 16));
+      mt = fmaxf(mt, __shfl_xor(mt, 32));
+      if (__ballot(mt > m_ref + 8.f) != 0ull) {  // wave-uniform, rare after the first tile
+        const float m_new = fmaxf(m_ref, mt);
+        if (__ballot(m_ref != -INFINITY) != 0ull) {
+          // acc <- diag(alpha) acc on the matrix cores (k slot g of MFMA m
+          // carries row 4 g + m of each 16 x 16 block).
+          const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+              z = __builtin_amdgcn_mfma_f32_16x16x4f32(c == 4 * g + m ? alpha : 0.f, acc[i][m],
+                                                        z, 0, 0, 0);
+            acc[i] = z;
+          }
+        }
+        m_ref = m_new;
+      }
+      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+      float p[2][4];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_use);
+      l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+               ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+      bf16x8_t pa;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pa[r] = (__bf16)p[0][r];
+        pa[4 + r] = (__bf16)p[1][r];
+      }
+      // P.V over the 512 features, 128 at a time: rows 16 h + 4 g + r,
+      // features 128 beta + 8 c .. + 7.
+#pragma unroll
+      for (int beta = 0; beta < 4; ++beta) {
+        u32x4_t vf[2][4];
+        {
+          uint32_t ad[8];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = h * kUnit + 4 * g + r;
+              ad[4 * h + r] =
+                  st + uint32_t(t * kRowBytes) + 16u * uint32_t(16 * beta + (c ^ (t & 7)));
+            }
+          }
+          u32x4_t v8[8];
+          lds_read_v8(ad, v8);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) vf[i >> 2][i & 3] = v8[i];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          if (nv[h] < kUnit) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const unsigned keep = (4 * g + r < nv[h]) ? 0xffffffffu : 0u;
+              vf[h][r] &= keep;
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const unsigned a0 = vf[0][0][i], a1 = vf[0][1][i], a2 = vf[0][2][i], a3 = vf[0][3][i];
+          const unsigned b0 = vf[1][0][i], b1 = vf[1][1][i], b2 = vf[1][2][i], b3 = vf[1][3][i];
+          const u32x4_t ve = u32x4_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16),
+                                     (b0 & 0xffffu) | (b1 << 16), (b2 & 0xffffu) | (b3 << 16)};
+          const u32x4_t vo =
+              u32x4_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u),
+                      (b0 >> 16) | (b1 & 0xffff0000u), (b2 >> 16) | (b3 & 0xffff0000u)};
+          acc[8 * beta + 2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pa, __builtin_bit_cast(bf16x8_t, ve), acc[8 * beta + 2 * i], 0, 0, 0);
+          acc[8 * beta + 2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              pa, __builtin_bit_cast(bf16x8_t, vo), acc[8 * beta + 2 * i + 1], 0, 0, 0);
+        }
+      }
+    }
+
+    if (active) {
+      float l_c = l_run + __shfl_xor(l_run, 16);
+      l_c += __shfl_xor(l_c, 32);
+      const bool final_out = pieces == 1;
+      const int row = final_out ? 0 : a.row_ptr[b] + piece;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * g + r;
+        const int h = h0 + hh;
+        const float lh = __shfl(l_c, hh);
+        const float inv = lh > 0.f ? 1.f / lh : 0.f;
+        if (h < H) {
+#pragma unroll
+          for (int beta = 0; beta < 4; ++beta) {
+            const int d = 128 * beta + 8 * c;
+            if (final_out) {
+              u32x4_t pk;
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                pk[e] = unsigned(bf16_bits(acc[8 * beta + 2 * e][r] * inv)) |
+                        (unsigned(bf16_bits(acc[8 * beta + 2 * e + 1][r] * inv)) << 16);
+              *reinterpret_cast<u32x4_t*>(a.out + (size_t(b) * H + h) * kDV + d) = pk;
+            } else {
+              float* dst = a.part_out + (size_t(row) * H + h) * kDV + d;
+              *reinterpret_cast<f32x4_t*>(dst) =
+                  f32x4_t{acc[8 * beta][r], acc[8 * beta + 1][r], acc[8 * beta + 2][r],
+                          acc[8 * beta + 3][r]} * inv;
+              *reinterpret_cast<f32x4_t*>(dst + 4) =
+                  f32x4_t{acc[8 * beta + 4][r], acc[8 * beta + 5][r], acc[8 * beta + 6][r],
+                          acc[8 * beta + 7][r]} * inv;
+            }
+          }
+        }
+      }
+      if (g == 0 && h0 + c < H) {
+        const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
+        if (final_out) {
+          if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
+        } else {
+          a.part_lse[size_t(row) * H + h0 + c] = lse_v;
+        }
+      }
+    }
+  });
+}
+
+// ----------------------------------------------------------------------------
 // LSE combine: one workgroup per (request, 16-head tile, 64-feature chunk);
 // thread (head hh, sub) merges features 4 sub .. 4 sub + 3 of the chunk,
 // with kCombineUnroll partial rows in flight.
@@ -1138,8 +1381,11 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
   dim3 grid(unsigned(parts_launched) * unsigned(args.head_tiles));
   if (kv_fp8)
     hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(kThreads), 0, stream, args);
-  else
+  else if (args.head_tiles == 1)
     hipLaunchKernelGGL(attn_ws_kernel, grid, dim3(kWsThreads), 0, stream, args);
+  else
+    hipLaunchKernelGGL(attn_heads_kernel, dim3(unsigned(parts_launched) * unsigned(args.head_groups)),
+                       dim3(kThreads), 0, stream, args);
   return hipGetLastError();
 }
 

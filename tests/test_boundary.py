@@ -87,8 +87,10 @@ def test_workspace_size_auto_mode():
     # 256 CUs, 16 heads: up to 256 partitions -> at most 2 * 255 partial rows.
     assert mla.get_workspace_size(512, 16, 3072, 0, 0) == _layout(512, 16, 510)
     assert mla.get_workspace_size(512, 16, 3072, 0, 256) == _layout(512, 16, 510)
-    # 128 heads: 8 head tiles share a CU, 32 partitions.
-    assert mla.get_workspace_size(128, 128, 32768, 0, 0) == _layout(128, 128, 62)
+    # 128 heads: two workgroups (four 16-head tiles each) per partition -> 128.
+    assert mla.get_workspace_size(128, 128, 32768, 0, 0) == _layout(128, 128, 254)
+    # 64 heads fit one workgroup per partition.
+    assert mla.get_workspace_size(128, 64, 32768, 0, 0) == _layout(128, 64, 510)
     # Never more rows than every request split into one piece per 16-token unit.
     assert mla.get_workspace_size(2, 16, 32, 0, 0) == _layout(2, 16, 4)
     assert mla.get_workspace_size(2, 16, 16, 0, 0) == _layout(2, 16, 0)
