@@ -37,6 +37,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "mla_internal.h"
 
 namespace mla {
@@ -781,6 +783,35 @@ __device__ __forceinline__ void lds_read_v8(const uint32_t (&ad)[8], u32x4_t (&v
       : "memory");
 }
 
+// Eight transposing LDS reads (ds_read_b64_tr_b16): for n' = 0..3 and token
+// halves h = 0, 1, read n' at vb[n'] + 128 M + 18432 h (one 16-token unit is
+// 16 rows of 1152 bytes). Within each 16-lane group, lane 4 a + b receives
+// element b of the 8-byte words addressed by lanes a, a + 4, a + 8, a + 12.
+#define MLA_DSTR(i, base, off) "ds_read_b64_tr_b16 %" #i ", %" #base " offset:" #off "\n\t"
+#define MLA_TR8(o0, o1)                                                                  \
+  asm volatile(MLA_DSTR(0, 8, o0) MLA_DSTR(1, 8, o1) MLA_DSTR(2, 9, o0) MLA_DSTR(3, 9, o1) \
+               MLA_DSTR(4, 10, o0) MLA_DSTR(5, 10, o1) MLA_DSTR(6, 11, o0)               \
+               MLA_DSTR(7, 11, o1) "s_waitcnt lgkmcnt(0)"                                 \
+               : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]),          \
+                 "=&v"(t[2][0]), "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1])           \
+               : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3])                           \
+               : "memory")
+
+template <int M>
+__device__ __forceinline__ void lds_read_tr8(const uint32_t (&vb)[4], u32x2_t (&t)[4][2]) {
+  static_assert(M >= 0 && M < 8, "feature group");
+  if constexpr (M == 0) MLA_TR8(0, 18432);
+  else if constexpr (M == 1) MLA_TR8(128, 18560);
+  else if constexpr (M == 2) MLA_TR8(256, 18688);
+  else if constexpr (M == 3) MLA_TR8(384, 18816);
+  else if constexpr (M == 4) MLA_TR8(512, 18944);
+  else if constexpr (M == 5) MLA_TR8(640, 19072);
+  else if constexpr (M == 6) MLA_TR8(768, 19200);
+  else MLA_TR8(896, 19328);
+}
+#undef MLA_TR8
+#undef MLA_DSTR
+
 // Wave-uniform load through the scalar unit (counted by lgkmcnt, not vmcnt,
 // so it does not disturb the vector-memory pipeline of the KV ring).
 __device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
@@ -1077,8 +1108,17 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
 // Head groups of one partition run on the same XCD in adjacent dispatch
 // slots, so the second group's ring loads are L2 hits. Ring, DMA map and
 // waits as in the 16-head kernels.
+// Frame of the many-head kernel: set from the first tile's maxima and
+// never moved while weights 2^(x - frame) stay below 2^kHeadsSlack, so fp32
+// accumulators cannot overflow. A head whose logits ever rise further makes
+// the workgroup stream the piece a second time with the frame preset to the
+// true maximum observed in the first pass (the first pass's sums are
+// discarded), so the accumulators are only ever zeroed or MFMA-updated.
+constexpr float kHeadsSlack = 64.f;
+
 __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
   __shared__ uint8_t ring[kStages][kTileBytesBf16];
+  __shared__ int redo_any;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
@@ -1136,7 +1176,6 @@ __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
       }
     };
 
-    wave_barrier_all();  // the ring of the previous piece is consumed
     // q fragment of this wave's head tile (padded heads repeat head H - 1).
     u32x4_t qf[kQChunks];
     {
@@ -1145,125 +1184,140 @@ __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < kQChunks; ++s2) qf[s2] = qp[4 * s2];
     }
-    wait_vmem<0>();
-    for (int k = 0; k < kStages - 1 && k < ntiles; ++k) issue_tile(k);
 
-    f32x4_t acc[32];  // heads 4 g + r; features 128 beta + 8 c + e in acc[8 beta + e]
-#pragma unroll
-    for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    f32x4_t acc[32];      // acc[n][r]: head 4 g + r, feature 16 n + c
     float m_ref = -INFINITY;  // frame of head c (log2 domain)
+    float m_seen = -INFINITY; // largest logit of head c seen in the first pass
     float l_run = 0.f;        // lane's share of head c's denominator
+    bool redo = false;        // this wave's frame was exceeded in the first pass
 
-    for (int j = 0; j < ntiles; ++j) {
-      wait_ring<kStages - 2>(ntiles - 1 - j);
-      wave_barrier_all();
-      if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
-      if (!active) continue;
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool work = active && (pass == 0 || redo);
+      if (pass == 1) {
+        m_ref = m_seen;  // preset frame: no weight exceeds 1
+        redo = false;
+      }
+#pragma unroll
+      for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      l_run = 0.f;
 
-      const uint32_t st = ring_lds + uint32_t(j % kStages) * kTileBytesBf16;
-      int nv[2];
-      tile_nv(j, nv);
-      float x[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int t = h * kUnit + c;
-        const uint32_t y = uint32_t(g ^ (c & 7));
-        const uint32_t row = st + uint32_t(t * kRowBytes);
-        u32x4_t kf[kQChunks];
-        lds_read_k(row + 16 * y, row + 16 * (y ^ 4), kf);
-        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s2 = 0; s2 < kQChunks; ++s2)
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s2]),
-                                                       __builtin_bit_cast(bf16x8_t, qf[s2]), sc,
-                                                       0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[h][r] = (4 * g + r < nv[h]) ? sc[r] * a.scale_log2 : -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      if (__ballot(mt > m_ref + 8.f) != 0ull) {  // wave-uniform, rare after the first tile
-        const float m_new = fmaxf(m_ref, mt);
-        if (__ballot(m_ref != -INFINITY) != 0ull) {
-          // acc <- diag(alpha) acc on the matrix cores (k slot g of MFMA m
-          // carries row 4 g + m of each 16 x 16 block).
-          const float alpha = m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-              z = __builtin_amdgcn_mfma_f32_16x16x4f32(c == 4 * g + m ? alpha : 0.f, acc[i][m],
-                                                        z, 0, 0, 0);
-            acc[i] = z;
-          }
+      wave_barrier_all();  // the ring of the previous pass or piece is consumed
+      wait_vmem<0>();      // q has landed; only ring loads are in flight from here
+      for (int k = 0; k < kStages - 1 && k < ntiles; ++k) issue_tile(k);
+
+      if (!work) {
+        // Waves without a head tile (or with nothing to redo) keep the ring
+        // moving: same waits, barriers and loads as the computing waves.
+        for (int j = 0; j < ntiles; ++j) {
+          wait_ring<kStages - 2>(ntiles - 1 - j);
+          wave_barrier_all();
+          if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
         }
-        m_ref = m_new;
-      }
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float p[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_use);
-      l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-               ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-      bf16x8_t pa;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pa[r] = (__bf16)p[0][r];
-        pa[4 + r] = (__bf16)p[1][r];
-      }
-      // P.V over the 512 features, 128 at a time: rows 16 h + 4 g + r,
-      // features 128 beta + 8 c .. + 7.
-#pragma unroll
-      for (int beta = 0; beta < 4; ++beta) {
-        u32x4_t vf[2][4];
-        {
-          uint32_t ad[8];
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int t = h * kUnit + 4 * g + r;
-              ad[4 * h + r] =
-                  st + uint32_t(t * kRowBytes) + 16u * uint32_t(16 * beta + (c ^ (t & 7)));
-            }
-          }
-          u32x4_t v8[8];
-          lds_read_v8(ad, v8);
-#pragma unroll
-          for (int i = 0; i < 8; ++i) vf[i >> 2][i & 3] = v8[i];
-        }
+      } else for (int j = 0; j < ntiles; ++j) {
+        wait_ring<kStages - 2>(ntiles - 1 - j);
+        wave_barrier_all();
+        if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
+
+        const uint32_t st = ring_lds + uint32_t(j % kStages) * kTileBytesBf16;
+        int nv[2];
+        tile_nv(j, nv);
+        float x[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          if (nv[h] < kUnit) {
+          const int t = h * kUnit + c;
+          const uint32_t y = uint32_t(g ^ (c & 7));
+          const uint32_t row = st + uint32_t(t * kRowBytes);
+          u32x4_t kf[kQChunks];
+          lds_read_k(row + 16 * y, row + 16 * (y ^ 4), kf);
+          f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const unsigned keep = (4 * g + r < nv[h]) ? 0xffffffffu : 0u;
-              vf[h][r] &= keep;
-            }
+          for (int s2 = 0; s2 < kQChunks; ++s2)
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s2]),
+                                                         __builtin_bit_cast(bf16x8_t, qf[s2]), sc,
+                                                         0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[h][r] = (4 * g + r < nv[h]) ? sc[r] * a.scale_log2 : -INFINITY;
+        }
+        float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
+                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        m_seen = fmaxf(m_seen, mt);
+        if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): set the frame
+        // Once set, the pass's sums are discarded; they are still computed
+        // so that the accumulators see no branch.
+        if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
+        float p[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_ref);
+        l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                 ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+        bf16x8_t pa;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pa[r] = (__bf16)p[0][r];
+          pa[4 + r] = (__bf16)p[1][r];
+        }
+        // P.V over 16-feature blocks n = 4 M + n' (features 16 n .. 16 n + 15).
+        // Lane s = 4 e + a of group g points at token row 4 g + e (and 16 more),
+        // features 16 n + 4 a .. + 3, so the transposing read hands lane c the
+        // B operand column of feature 16 n + c over tokens 4 g .. 4 g + 3 (and
+        // 16 + 4 g ..), the same token slots the P operand holds.
+        uint32_t vb[4];
+        {
+          const int s4 = lane & 15, av = s4 & 3, ev = s4 >> 2;
+          const int t0 = 4 * g + ev;
+#pragma unroll
+          for (int n2 = 0; n2 < 4; ++n2)
+            vb[n2] = st + uint32_t(t0 * kRowBytes) +
+                     16u * uint32_t((2 * n2 + (av >> 1)) ^ (t0 & 7)) + 8u * uint32_t(av & 1);
+        }
+        // Tokens past the end of a partial unit: zero their V elements (their
+        // P is zero, but unused rows may hold non-finite bit patterns).
+        uint64_t vkeep[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int kc = min(max(nv[h] - 4 * g, 0), 4);
+          vkeep[h] = kc >= 4 ? ~0ull : ((1ull << (16 * kc)) - 1ull);
+        }
+        const bool vmask = (nv[0] < kUnit) | (nv[1] < kUnit);
+        auto pv_group = [&](auto mc) {
+          constexpr int M = decltype(mc)::value;
+          u32x2_t t[4][2];
+          lds_read_tr8<M>(vb, t);
+          if (vmask) {
+#pragma unroll
+            for (int n2 = 0; n2 < 4; ++n2)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                t[n2][h] = __builtin_bit_cast(
+                    u32x2_t, __builtin_bit_cast(uint64_t, t[n2][h]) & vkeep[h]);
           }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned a0 = vf[0][0][i], a1 = vf[0][1][i], a2 = vf[0][2][i], a3 = vf[0][3][i];
-          const unsigned b0 = vf[1][0][i], b1 = vf[1][1][i], b2 = vf[1][2][i], b3 = vf[1][3][i];
-          const u32x4_t ve = u32x4_t{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16),
-                                     (b0 & 0xffffu) | (b1 << 16), (b2 & 0xffffu) | (b3 << 16)};
-          const u32x4_t vo =
-              u32x4_t{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u),
-                      (b0 >> 16) | (b1 & 0xffff0000u), (b2 >> 16) | (b3 & 0xffff0000u)};
-          acc[8 * beta + 2 * i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pa, __builtin_bit_cast(bf16x8_t, ve), acc[8 * beta + 2 * i], 0, 0, 0);
-          acc[8 * beta + 2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              pa, __builtin_bit_cast(bf16x8_t, vo), acc[8 * beta + 2 * i + 1], 0, 0, 0);
-        }
+          for (int n2 = 0; n2 < 4; ++n2) {
+            const u32x4_t bv = u32x4_t{t[n2][0][0], t[n2][0][1], t[n2][1][0], t[n2][1][1]};
+            acc[4 * M + n2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                pa, __builtin_bit_cast(bf16x8_t, bv), acc[4 * M + n2], 0, 0, 0);
+          }
+        };
+        pv_group(std::integral_constant<int, 0>{});
+        pv_group(std::integral_constant<int, 1>{});
+        pv_group(std::integral_constant<int, 2>{});
+        pv_group(std::integral_constant<int, 3>{});
+        pv_group(std::integral_constant<int, 4>{});
+        pv_group(std::integral_constant<int, 5>{});
+        pv_group(std::integral_constant<int, 6>{});
+        pv_group(std::integral_constant<int, 7>{});
       }
+      // Does any wave need a second pass?
+      if (tid == 0) redo_any = 0;
+      wave_barrier_lds();
+      if (work && redo && lane == 0) redo_any = 1;
+      wave_barrier_lds();
+      if (redo_any == 0) break;
     }
 
     if (active) {
@@ -1278,25 +1332,15 @@ __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
         const float lh = __shfl(l_c, hh);
         const float inv = lh > 0.f ? 1.f / lh : 0.f;
         if (h < H) {
+          // acc[n][r]: head 4 g + r, feature 16 n + c.
+          if (final_out) {
+            uint16_t* dst = a.out + (size_t(b) * H + h) * kDV + c;
 #pragma unroll
-          for (int beta = 0; beta < 4; ++beta) {
-            const int d = 128 * beta + 8 * c;
-            if (final_out) {
-              u32x4_t pk;
+            for (int n = 0; n < 32; ++n) dst[16 * n] = bf16_bits(acc[n][r] * inv);
+          } else {
+            float* dst = a.part_out + (size_t(row) * H + h) * kDV + c;
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                pk[e] = unsigned(bf16_bits(acc[8 * beta + 2 * e][r] * inv)) |
-                        (unsigned(bf16_bits(acc[8 * beta + 2 * e + 1][r] * inv)) << 16);
-              *reinterpret_cast<u32x4_t*>(a.out + (size_t(b) * H + h) * kDV + d) = pk;
-            } else {
-              float* dst = a.part_out + (size_t(row) * H + h) * kDV + d;
-              *reinterpret_cast<f32x4_t*>(dst) =
-                  f32x4_t{acc[8 * beta][r], acc[8 * beta + 1][r], acc[8 * beta + 2][r],
-                          acc[8 * beta + 3][r]} * inv;
-              *reinterpret_cast<f32x4_t*>(dst + 4) =
-                  f32x4_t{acc[8 * beta + 4][r], acc[8 * beta + 5][r], acc[8 * beta + 6][r],
-                          acc[8 * beta + 7][r]} * inv;
-            }
+            for (int n = 0; n < 32; ++n) dst[16 * n] = acc[n][r] * inv;
           }
         }
       }
