@@ -1192,14 +1192,16 @@ __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
     bool redo = false;        // this wave's frame was exceeded in the first pass
 
     for (int pass = 0; pass < 2; ++pass) {
+      // Pass 1 recomputes only the waves that asked for it; the others keep
+      // their pass-0 sums and frame.
       const bool work = active && (pass == 0 || redo);
-      if (pass == 1) {
-        m_ref = m_seen;  // preset frame: no weight exceeds 1
-        redo = false;
-      }
+      if (work) {
+        if (pass == 1) m_ref = m_seen;  // preset frame: no weight exceeds 1
 #pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      l_run = 0.f;
+        for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        l_run = 0.f;
+      }
+      redo = false;
 
       wave_barrier_all();  // the ring of the previous pass or piece is consumed
       wait_vmem<0>();      // q has landed; only ring loads are in flight from here

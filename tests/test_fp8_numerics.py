@@ -3,8 +3,9 @@
 The fp8 cache path quantises q in-kernel and feeds P to fp8 matrix cores.
 This emulation (fp64 arithmetic with torch's float8_e4m3fn rounding) shows
 that one E4M3 term for q, or for P, can exceed the 2e-2 + 2e-2|ref| bound,
-while the two-term form (rounded value + rounded, separately scaled
-residual) stays well inside it. It tests the numerical design, not the
+while the two-term form (rounded value + rounded residual, both E4M3 codes
+in the same scale, so that one matrix instruction can take the pair as
+a doubled contraction depth) stays well inside it. It tests the numerical design, not the
 kernel; the GPU parity tests check the kernel against the oracle.
 """
 import torch
@@ -23,9 +24,9 @@ def quantise_rows(q, two_terms):
     hi = e4m3(q / s1) * s1
     if not two_terms:
         return hi
-    r = q - hi
-    s2 = r.abs().amax(-1, keepdim=True) / 448
-    return hi + e4m3(r / s2) * s2
+    # the residual is at most half an E4M3 step of 448 (16 codes), so it
+    # fits the same scale without saturating
+    return hi + e4m3((q - hi) / s1) * s1
 
 
 def quantise_p(p, two_terms):

@@ -89,6 +89,16 @@ def test_fp8_small(orc, num_splits):
     _check(orc, wl, num_splits, what=f"fp8 small splits={num_splits}")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("num_heads", [16, 20, 128])
+def test_rising_logits(orc, num_heads, kv_dtype):
+    # Head 0's logits climb by ~100 after the first tiles: the kernels' frame
+    # handling (moves, or a second pass) must keep every sum finite and exact.
+    wl = workloads.make_rising(num_heads, kv_dtype, seed=71 + num_heads)
+    for s in (0, 1, 3):
+        _check(orc, wl, s, what=f"{wl.name} splits={s}")
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_block_permutation_bitwise():

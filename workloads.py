@@ -153,17 +153,50 @@ def make_workload(name: str = "custom", *, batch: int, num_heads: int, seq, bloc
         kv_scale = 1.0
     elif kv_dtype == "fp8":
         kv32 = torch.randn((pool * block_size, D_K), generator=gen, dtype=torch.float32)
-        amax = float(kv32.abs().max())
-        kv_scale = float(np.float32(amax / E4M3_MAX))
-        codes = (kv32 / kv_scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+        kv, kv_scale = quantize_e4m3(kv32)
         del kv32
-        kv = codes.view(torch.uint8).view(pool, block_size, D_K)
+        kv = kv.view(pool, block_size, D_K)
     else:
         raise ValueError(f"unknown kv dtype {kv_dtype}")
     wl = Workload(name=name, q=q, kv=kv, block_table=table, seq_lens=seq_lens,
                   block_size=block_size, kv_dtype=kv_dtype, kv_scale=kv_scale)
     if poison:
         poison_unused(wl)
+    return wl
+
+
+def quantize_e4m3(kv32: torch.Tensor):
+    """Per-tensor E4M3 codes (uint8) and fp32 scale: amax maps to 448."""
+    amax = float(kv32.abs().max())
+    kv_scale = float(np.float32(amax / E4M3_MAX)) if amax > 0 else 1.0
+    codes = (kv32 / kv_scale).clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn)
+    return codes.view(torch.uint8), kv_scale
+
+
+def make_rising(num_heads: int, kv_dtype: str, seed: int, block_size: int = 64) -> Workload:
+    """Logits that climb far above the first tile's: past the first third of
+    each request, key row t is alpha_t * q[b, 0] plus small noise, alpha_t
+    ramping from 0.5 to 3.0, so head 0's logits rise from about 20 to about
+    125 (natural log units) while the other heads stay near N(0, 3)."""
+    lens = [200, 900, 2100]
+    wl = make_workload("rising", batch=len(lens), num_heads=num_heads, seq=("fixed", lens),
+                       block_size=block_size, seed=seed, kv_dtype="bf16")
+    gen = torch.Generator("cpu").manual_seed(seed + 1)
+    kv32 = wl.kv.float().reshape(-1, D_K).clone()
+    for b, n in enumerate(lens):
+        t0 = n // 3
+        t = torch.arange(t0, n)
+        rows = wl.block_table[b, t // block_size].long() * block_size + t % block_size
+        alpha = 0.5 + 2.5 * (t - t0).float() / max(n - 1 - t0, 1)
+        noise = 0.2 * torch.randn((len(t), D_K), generator=gen)
+        kv32[rows] = alpha[:, None] * wl.q[b, 0].float()[None, :] + noise
+    if kv_dtype == "bf16":
+        wl.kv = kv32.to(torch.bfloat16).view(wl.kv.shape)
+    else:
+        codes, wl.kv_scale = quantize_e4m3(kv32)
+        wl.kv = codes.view(wl.kv.shape)
+        wl.kv_dtype = "fp8"
+    wl.name = f"rising-{kv_dtype}-H{num_heads}"
     return wl
 
 
