@@ -51,11 +51,11 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
 
 inline int head_tiles(int num_heads) { return (num_heads + kHeadTile - 1) / kHeadTile; }
 
-// Workgroups per partition: the bf16 many-head kernel puts four head tiles
-// in one workgroup; the other kernels use one workgroup per head tile.
+// Workgroups per partition: the many-head kernels (and the E4M3 kernel) put
+// four 16-head tiles in one workgroup; the 16-head bf16 kernel uses one.
 inline int workgroups_per_partition(int num_heads, int kv_fp8) {
-  const int ht = head_tiles(num_heads);
-  return (kv_fp8 || ht == 1) ? ht : (ht + 3) / 4;
+  (void)kv_fp8;
+  return (head_tiles(num_heads) + 3) / 4;
 }
 
 // Upper bound on balanced partitions for a device with `num_cus` CUs: one

@@ -1359,6 +1359,412 @@ __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
+// E4M3 cache: the many-head tile stream on scaled 16x16x128 E4M3 matrix ops.
+//
+// A tile is 64 tokens (four 16-token units) of 576-byte rows, 36,864 bytes as
+// in the bf16 kernels, so ring, DMA map and waits are theirs. Chunk ch (16
+// bytes) of row t sits in slot ch ^ fp8_swizzle(t), a permutation inside each
+// aligned group of four chunks that keeps both read patterns below free of
+// LDS bank conflicts.
+//
+// Logits: one op covers 64 dimensions twice. A holds K's 16 bytes of the
+// lane's dimension group twice, B holds q's rounded E4M3 term and its
+// residual (both in q's per-head scale amax / 448), so one instruction sums
+// K . (q_hi + q_lo), q to about 2^-8 relative error as with bf16.
+// P.V: one op covers the tile's 64 tokens twice. A holds P_hi and P_lo (the
+// rounded weight times 2^8 and its E4M3 residual) of 16 tokens per lane
+// group, B the same V bytes twice, read with ds_read_b64_tr_b8.
+// Weights: each head keeps the frame m of its first tile for the whole piece.
+// Per tile and head, e = ceil(tile max - m) (at least 0) moves into the op's
+// per-lane E8M0 scale of A, so the stored weights 2^(x - m - e) never exceed
+// 1 while the products carry 2^(x - m); the frame never has to move. As in
+// the bf16 kernel, a head whose logits rise more than 64 above its frame
+// makes the workgroup stream the piece again with the frame preset.
+constexpr int kTileFp8 = 4 * kUnit;          // tokens per E4M3 tile
+constexpr int kRowChunksFp8 = kDK / 16;      // 36
+constexpr int kKChunksFp8 = kDK / 64;        // 9 logit ops per unit
+static_assert(kTileFp8 * kDK == kTileBytesBf16, "E4M3 tile matches the bf16 tile size");
+static_assert(kTileFp8 * kRowChunksFp8 == kDmaPerThread * kThreads, "tile must split evenly");
+
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ int fp8_swizzle(int t) {
+  return ((t >> 2) & 3) ^ (((t >> 4) & 1) << 1);
+}
+
+// E4M3 encoding without range clamp (callers guarantee |x| <= 448).
+__device__ __forceinline__ unsigned pack_e4m3x4_inrange(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
+  return unsigned(w);
+}
+
+// The nine K chunks of one unit: base + OFF + 64 m, m = 0..8.
+template <int OFF>
+__device__ __forceinline__ void lds_read_k9(uint32_t base, u32x4_t (&kf)[kKChunksFp8]) {
+  asm volatile(
+      "ds_read_b128 %0, %9 offset:%10\n\t"
+      "ds_read_b128 %1, %9 offset:%11\n\t"
+      "ds_read_b128 %2, %9 offset:%12\n\t"
+      "ds_read_b128 %3, %9 offset:%13\n\t"
+      "ds_read_b128 %4, %9 offset:%14\n\t"
+      "ds_read_b128 %5, %9 offset:%15\n\t"
+      "ds_read_b128 %6, %9 offset:%16\n\t"
+      "ds_read_b128 %7, %9 offset:%17\n\t"
+      "ds_read_b128 %8, %9 offset:%18\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(kf[0]), "=&v"(kf[1]), "=&v"(kf[2]), "=&v"(kf[3]), "=&v"(kf[4]), "=&v"(kf[5]),
+        "=&v"(kf[6]), "=&v"(kf[7]), "=&v"(kf[8])
+      : "v"(base), "i"(OFF), "i"(OFF + 64), "i"(OFF + 128), "i"(OFF + 192), "i"(OFF + 256),
+        "i"(OFF + 320), "i"(OFF + 384), "i"(OFF + 448), "i"(OFF + 512)
+      : "memory");
+}
+
+// Eight transposing byte reads (ds_read_b64_tr_b8): for n' = 0..3 and row
+// halves h = 0, 1, read (n', h) at vb[n'] + OFF + 18432 h (32 rows of 576
+// bytes). Within each 16-lane group, lane 8 a + b receives byte b of the
+// 8-byte words addressed by lanes a, a + 2, ..., a + 14.
+template <int OFF>
+__device__ __forceinline__ void lds_read_trb8(const uint32_t (&vb)[4], u32x2_t (&t)[4][2]) {
+  asm volatile(
+      "ds_read_b64_tr_b8 %0, %8 offset:%12\n\t"
+      "ds_read_b64_tr_b8 %1, %8 offset:%13\n\t"
+      "ds_read_b64_tr_b8 %2, %9 offset:%12\n\t"
+      "ds_read_b64_tr_b8 %3, %9 offset:%13\n\t"
+      "ds_read_b64_tr_b8 %4, %10 offset:%12\n\t"
+      "ds_read_b64_tr_b8 %5, %10 offset:%13\n\t"
+      "ds_read_b64_tr_b8 %6, %11 offset:%12\n\t"
+      "ds_read_b64_tr_b8 %7, %11 offset:%13\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(t[0][0]), "=&v"(t[0][1]), "=&v"(t[1][0]), "=&v"(t[1][1]), "=&v"(t[2][0]),
+        "=&v"(t[2][1]), "=&v"(t[3][0]), "=&v"(t[3][1])
+      : "v"(vb[0]), "v"(vb[1]), "v"(vb[2]), "v"(vb[3]), "i"(OFF), "i"(OFF + 18432)
+      : "memory");
+}
+
+__device__ __forceinline__ f32x4_t mfma_e4m3_128(const i32x8_t& a, const i32x8_t& b,
+                                                 const f32x4_t& c, int scale_a) {
+  // Format code 0 = E4M3 for both operands; E8M0 scales (127 = 2^0).
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
+}
+
+__global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
+  __shared__ uint8_t ring[kStages][kTileBytesBf16];
+  __shared__ int redo_any;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int c = lane & 15, g = lane >> 4;
+  const int H = a.num_heads;
+
+  const int lin = blockIdx.x;
+  const int xcd = lin & 7, slot = lin >> 3;
+  const int hg = slot % a.head_groups;
+  const int part = (slot / a.head_groups) * 8 + xcd;
+  const int ht = 4 * hg + wave;
+  const bool active = ht < a.head_tiles;  // inactive waves only stream the ring
+  const int h0 = ht * kHeadTile;
+
+  // DMA map: load i fills LDS slot i * 256 + tid of the stage, which holds
+  // chunk (slot ^ swizzle) of row t of unit t >> 4.
+  uint32_t dma_off[kDmaPerThread];
+  uint32_t dma_unit = 0;  // two bits per load
+#pragma unroll
+  for (int i = 0; i < kDmaPerThread; ++i) {
+    const int pos = i * kThreads + tid;
+    const int t = pos / kRowChunksFp8, sl = pos - (pos / kRowChunksFp8) * kRowChunksFp8;
+    const int ch = sl ^ fp8_swizzle(t);
+    dma_off[i] = uint32_t((t & 15) * kDK + ch * 16);
+    dma_unit |= uint32_t(t >> 4) << (2 * i);
+  }
+  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (void __attribute__((address_space(3)))*)(&ring[0][0])));
+  const int bs_mask = (1 << a.bs_log2) - 1;
+
+  // Per-lane LDS read bases that do not depend on the stage.
+  // K: row c of a unit, chunk 4 m + (g ^ swizzle): units 0, 2 and 1, 3.
+  const uint32_t k_even = uint32_t(c * kDK + 16 * (g ^ fp8_swizzle(c)));
+  const uint32_t k_odd = uint32_t(c * kDK + 16 * (g ^ fp8_swizzle(16 + c)));
+  // V: lane s = 2 e + a of group g points at row 16 (e >> 2) + 4 g + (e & 3)
+  // (and 32 rows further), bytes 16 n + 8 a.
+  uint32_t v_off[4];
+  {
+    const int s4 = lane & 15, av = s4 & 1, ev = s4 >> 1;
+    const int t = 16 * (ev >> 2) + 4 * g + (ev & 3);
+#pragma unroll
+    for (int n2 = 0; n2 < 4; ++n2)
+      v_off[n2] = uint32_t(t * kDK + 16 * (n2 ^ fp8_swizzle(t)) + 8 * av);
+  }
+
+  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
+    const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
+    const int u_end = min(u1, (n + kUnit - 1) / kUnit);
+    const int ntiles = u_end > u0 ? (u_end - u0 + 3) / 4 : 0;
+    const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
+    auto tile_nv = [&](int k, int (&nv)[4]) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int uu = u0 + 4 * k + u;
+        nv[u] = uu < u_end ? min(kUnit, n - uu * kUnit) : 0;
+      }
+    };
+    auto unit_rows = [&](int u) -> const uint8_t* {
+      const int t0 = u * kUnit;
+      int blk = scalar_load_i32(bt_row + (t0 >> a.bs_log2));
+      if (blk < 0 || blk >= a.num_blocks) blk = 0;
+      return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kDK;
+    };
+    auto issue_tile = [&](int k) {
+      const int uk = u0 + 4 * k;
+      const uint8_t* r0 = unit_rows(uk);
+      const uint8_t* r1 = uk + 1 < u_end ? unit_rows(uk + 1) : r0;
+      const uint8_t* r2 = uk + 2 < u_end ? unit_rows(uk + 2) : r0;
+      const uint8_t* r3 = uk + 3 < u_end ? unit_rows(uk + 3) : r0;
+      uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
+#pragma unroll
+      for (int i = 0; i < kDmaPerThread; ++i) {
+        const uint32_t us = (dma_unit >> (2 * i)) & 3u;
+        const uint8_t* base = (us & 2) ? ((us & 1) ? r3 : r2) : ((us & 1) ? r1 : r0);
+        __builtin_amdgcn_global_load_lds(
+            base + dma_off[i], (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16),
+            16, 0, 0);
+      }
+    };
+
+    // q of head h0 + c (padded heads repeat head H - 1), dimensions
+    // 64 m + 16 g .. + 15: qf[m] = 16 bytes of q_hi, then 16 bytes of q_lo.
+    i32x8_t qf[kKChunksFp8];
+    float xscale;  // logit scale of head c, log2 domain
+    {
+      const int hq = min(h0 + c, H - 1);
+      const u32x4_t* qp =
+          reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + hq) * kDK + 16 * g);
+      u32x4_t raw[kKChunksFp8][2];
+#pragma unroll
+      for (int m = 0; m < kKChunksFp8; ++m) {
+        raw[m][0] = qp[8 * m];
+        raw[m][1] = qp[8 * m + 1];
+      }
+      float amax = 0.f;
+#pragma unroll
+      for (int m = 0; m < kKChunksFp8; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const unsigned x = raw[m][h][w];
+            amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
+                                     fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
+          }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float inv = amax > 0.f ? 448.f / amax : 0.f;
+      xscale = (amax / 448.f) * a.kv_scale * a.scale_log2;
+#pragma unroll
+      for (int m = 0; m < kKChunksFp8; ++m) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int w2 = 0; w2 < 2; ++w2) {
+            const unsigned x0 = raw[m][h][2 * w2], x1 = raw[m][h][2 * w2 + 1];
+            const float f0 = __builtin_bit_cast(float, x0 << 16) * inv;
+            const float f1 = __builtin_bit_cast(float, x0 & 0xffff0000u) * inv;
+            const float f2 = __builtin_bit_cast(float, x1 << 16) * inv;
+            const float f3 = __builtin_bit_cast(float, x1 & 0xffff0000u) * inv;
+            const unsigned hi = pack_e4m3x4_inrange(f0, f1, f2, f3);
+            const unsigned lo = pack_e4m3x4_inrange(
+                f0 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 0),
+                f1 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 1),
+                f2 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 2),
+                f3 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 3));
+            qf[m][2 * h + w2] = int(hi);
+            qf[m][4 + 2 * h + w2] = int(lo);
+          }
+        }
+      }
+    }
+
+    f32x4_t acc[32];          // acc[n][r]: head 4 g + r, feature 16 n + c (units 2^-8 / kv_scale)
+    float m_ref = -INFINITY;  // frame of head c (log2 domain)
+    float m_seen = -INFINITY; // largest logit of head c seen in the first pass
+    float l_run = 0.f;        // lane's share of head c's denominator (frame m_ref)
+    bool redo = false;
+
+    for (int pass = 0; pass < 2; ++pass) {
+      const bool work = active && (pass == 0 || redo);
+      if (work) {
+        if (pass == 1) m_ref = m_seen;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        l_run = 0.f;
+      }
+      redo = false;
+
+      wave_barrier_all();  // the ring of the previous pass or piece is consumed
+      wait_vmem<0>();      // q has landed; only ring loads are in flight from here
+      for (int k = 0; k < kStages - 1 && k < ntiles; ++k) issue_tile(k);
+
+      if (!work) {
+        for (int j = 0; j < ntiles; ++j) {
+          wait_ring<kStages - 2>(ntiles - 1 - j);
+          wave_barrier_all();
+          if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
+        }
+      } else for (int j = 0; j < ntiles; ++j) {
+        wait_ring<kStages - 2>(ntiles - 1 - j);
+        wave_barrier_all();
+        if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
+
+        const uint32_t st = ring_lds + uint32_t(j % kStages) * kTileBytesBf16;
+        int nv[4];
+        tile_nv(j, nv);
+        // Logits of units u = 0..3: lane (c, g) gets tokens 16 u + 4 g + r of head c.
+        float x[4][4];
+        auto logits = [&](auto uc) {
+          constexpr int U = decltype(uc)::value;
+          u32x4_t kf[kKChunksFp8];
+          lds_read_k9<U * kUnit * kDK>(st + ((U & 1) ? k_odd : k_even), kf);
+          f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int m = 0; m < kKChunksFp8; ++m) {
+            const i32x8_t ka = i32x8_t{int(kf[m][0]), int(kf[m][1]), int(kf[m][2]), int(kf[m][3]),
+                                       int(kf[m][0]), int(kf[m][1]), int(kf[m][2]), int(kf[m][3])};
+            sc = mfma_e4m3_128(ka, qf[m], sc, 127);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            x[U][r] = (4 * g + r < nv[U]) ? sc[r] * xscale : -INFINITY;
+        };
+        logits(std::integral_constant<int, 0>{});
+        logits(std::integral_constant<int, 1>{});
+        logits(std::integral_constant<int, 2>{});
+        logits(std::integral_constant<int, 3>{});
+
+        float mt = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          mt = fmaxf(mt, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+        mt = fmaxf(mt, __shfl_xor(mt, 16));
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        m_seen = fmaxf(m_seen, mt);
+        if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): set the frame
+        if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
+        // Exponent carried by the op's A scale: 0 <= e <= 64.
+        const float rise = mt - m_ref;
+        const int e = rise > 0.f ? min(int(ceilf(rise)), int(kHeadsSlack)) : 0;
+        const float fe = m_ref + float(e);
+        unsigned ph[4], pl[4];
+        float lt = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          float ps[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float p = fast_exp2(x[u][r] - fe);
+            lt += p;
+            ps[r] = p * 256.f;
+          }
+          ph[u] = pack_e4m3x4_inrange(ps[0], ps[1], ps[2], ps[3]);
+          pl[u] = pack_e4m3x4_inrange(ps[0] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 0),
+                                      ps[1] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 1),
+                                      ps[2] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 2),
+                                      ps[3] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 3));
+        }
+        l_run += __builtin_amdgcn_ldexpf(lt, e);
+        const i32x8_t pa = i32x8_t{int(ph[0]), int(ph[1]), int(ph[2]), int(ph[3]),
+                                   int(pl[0]), int(pl[1]), int(pl[2]), int(pl[3])};
+        const int sa = 127 + e;
+
+        // Tokens past the end of a partial unit: zero their V bytes (their
+        // weight is zero, but unused rows may hold NaN codes).
+        const bool vmask = (nv[0] < kUnit) | (nv[1] < kUnit) | (nv[2] < kUnit) | (nv[3] < kUnit);
+        uint64_t vkeep[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          uint64_t k2 = 0;
+#pragma unroll
+          for (int q2 = 0; q2 < 2; ++q2) {
+            const int kc = min(max(nv[2 * h + q2] - 4 * g, 0), 4);
+            const uint64_t m4 = kc >= 4 ? 0xffffffffull : ((1ull << (8 * kc)) - 1ull);
+            k2 |= m4 << (32 * q2);
+          }
+          vkeep[h] = k2;
+        }
+        uint32_t vb[4];
+#pragma unroll
+        for (int n2 = 0; n2 < 4; ++n2) vb[n2] = st + v_off[n2];
+        auto pv_group = [&](auto mc) {
+          constexpr int M = decltype(mc)::value;
+          u32x2_t t[4][2];
+          lds_read_trb8<64 * M>(vb, t);
+          if (vmask) {
+#pragma unroll
+            for (int n2 = 0; n2 < 4; ++n2)
+#pragma unroll
+              for (int h = 0; h < 2; ++h)
+                t[n2][h] = __builtin_bit_cast(
+                    u32x2_t, __builtin_bit_cast(uint64_t, t[n2][h]) & vkeep[h]);
+          }
+#pragma unroll
+          for (int n2 = 0; n2 < 4; ++n2) {
+            const i32x8_t bv = i32x8_t{int(t[n2][0][0]), int(t[n2][0][1]), int(t[n2][1][0]),
+                                       int(t[n2][1][1]), int(t[n2][0][0]), int(t[n2][0][1]),
+                                       int(t[n2][1][0]), int(t[n2][1][1])};
+            acc[4 * M + n2] = mfma_e4m3_128(pa, bv, acc[4 * M + n2], sa);
+          }
+        };
+        pv_group(std::integral_constant<int, 0>{});
+        pv_group(std::integral_constant<int, 1>{});
+        pv_group(std::integral_constant<int, 2>{});
+        pv_group(std::integral_constant<int, 3>{});
+        pv_group(std::integral_constant<int, 4>{});
+        pv_group(std::integral_constant<int, 5>{});
+        pv_group(std::integral_constant<int, 6>{});
+        pv_group(std::integral_constant<int, 7>{});
+      }
+      if (tid == 0) redo_any = 0;
+      wave_barrier_lds();
+      if (work && redo && lane == 0) redo_any = 1;
+      wave_barrier_lds();
+      if (redo_any == 0) break;
+    }
+
+    if (active) {
+      float l_c = l_run + __shfl_xor(l_run, 16);
+      l_c += __shfl_xor(l_c, 32);
+      const bool final_out = pieces == 1;
+      const int row = final_out ? 0 : a.row_ptr[b] + piece;
+      const float out_scale = a.kv_scale * (1.f / 256.f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int hh = 4 * g + r;
+        const int h = h0 + hh;
+        const float lh = __shfl(l_c, hh);
+        const float inv = lh > 0.f ? out_scale / lh : 0.f;
+        if (h < H) {
+          if (final_out) {
+            uint16_t* dst = a.out + (size_t(b) * H + h) * kDV + c;
+#pragma unroll
+            for (int n2 = 0; n2 < 32; ++n2) dst[16 * n2] = bf16_bits(acc[n2][r] * inv);
+          } else {
+            float* dst = a.part_out + (size_t(row) * H + h) * kDV + c;
+#pragma unroll
+            for (int n2 = 0; n2 < 32; ++n2) dst[16 * n2] = acc[n2][r] * inv;
+          }
+        }
+      }
+      if (g == 0 && h0 + c < H) {
+        const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
+        if (final_out) {
+          if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
+        } else {
+          a.part_lse[size_t(row) * H + h0 + c] = lse_v;
+        }
+      }
+    }
+  });
+}
+
+// ----------------------------------------------------------------------------
 // LSE combine: one workgroup per (request, 16-head tile, 64-feature chunk);
 // thread (head hh, sub) merges features 4 sub .. 4 sub + 3 of the chunk,
 // with kCombineUnroll partial rows in flight.
@@ -1426,7 +1832,8 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
                             hipStream_t stream) {
   dim3 grid(unsigned(parts_launched) * unsigned(args.head_tiles));
   if (kv_fp8)
-    hipLaunchKernelGGL(attn_kernel<1>, grid, dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL(attn_fp8_kernel, dim3(unsigned(parts_launched) * unsigned(args.head_groups)),
+                       dim3(kThreads), 0, stream, args);
   else if (args.head_tiles == 1)
     hipLaunchKernelGGL(attn_ws_kernel, grid, dim3(kWsThreads), 0, stream, args);
   else
