@@ -13,15 +13,16 @@
 //     unrestricted num_heads (< 128) for DeepSeek TP", summary of changes: a
 //     tile scheduler and splitting KV across multiple blocks/SMs.)
 //
-//  2. attn_kernel: one workgroup per (partition, 16-head tile). Its four
-//     waves take the 16-token units of a piece round robin. For each unit a
-//     wave loads the 16 cached rows (contiguous: a unit never straddles a
-//     page because block sizes are multiples of 16) straight from HBM into
-//     registers, computes the 16x16 logit tile on bf16 MFMA, updates an fp32
-//     online softmax, and accumulates P.V on MFMA into a 16x512 fp32 tile.
-//     The four waves' states are merged through LDS; a one-piece request is
-//     written as the final bf16 output and LSE, a piece of a split request
-//     as a normalised fp32 partial plus its LSE.
+//  2. attention: one workgroup per partition (and group of up to four
+//     16-head tiles). The KV of each piece streams HBM -> LDS in tiles with
+//     coalesced direct-to-LDS loads through a four-stage ring; the logits
+//     (q from registers, K from LDS) and P.V (V through LDS transpose reads)
+//     run on matrix cores with an fp32 online softmax in the log2 domain. A
+//     one-piece request is written as the final bf16 output and LSE, a piece
+//     of a split request as a normalised fp32 partial plus its LSE. Three
+//     variants: attn_ws_kernel (bf16, up to 16 heads: a logit wave feeds four
+//     P.V waves), attn_heads_kernel (bf16, more heads: four waves of 16
+//     heads each), attn_fp8_kernel (E4M3 cache, any head count).
 //
 //  3. combine_kernel: log-sum-exp merge of the partial rows of each split
 //     request (PR #20769, summary of changes: the reduction kernel that
@@ -159,474 +160,6 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* seq_l
 // ----------------------------------------------------------------------------
 // Attention.
 
-// q tile rows in LDS, padded so consecutive rows start 4 or 20 banks apart.
-constexpr int kQRowDwordsBf16 = kDK / 2 + 4;  // 1152 B + 16 B
-constexpr int kQRowDwordsFp8 = kDK / 4 + 4;   // 576 B + 16 B
-
-struct AttnSmem {
-  float o[kWaves][kHeadTile][kDV];          // per-wave accumulators (frame m_lds)
-  float m[kWaves][kHeadTile];               // per-wave final frame (log2 domain)
-  float l[kWaves][kHeadTile];               // per-wave softmax denominators
-  uint32_t q[2 * kHeadTile * kQRowDwordsFp8 > kHeadTile * kQRowDwordsBf16
-                 ? 2 * kHeadTile * kQRowDwordsFp8
-                 : kHeadTile * kQRowDwordsBf16];  // q tile: bf16 pairs, or E4M3 hi|lo quads
-  float qscale[2][kHeadTile];               // E4M3 path: per-head scales of q_hi, q_lo
-};
-
-// Per-cache-type layout of the P.V accumulators: lane (c, g) holds, for block
-// beta < kBlocks and e < kDimsPerLane, output feature
-// kBlockWidth * beta + kDimsPerLane * c + e of heads 4 g + r in acc[beta * kDimsPerLane + e].
-template <int KV_FP8>
-struct PvLayout {
-  static constexpr int kDimsPerLane = KV_FP8 ? 16 : 8;
-  static constexpr int kBlocks = kDV / (16 * kDimsPerLane);  // 4 (bf16) or 2 (fp8)
-  static constexpr int kBlockWidth = 16 * kDimsPerLane;
-  // E4M3 weights are stored as p * 2^8 (kept in the normal range); the
-  // frame slack keeps 2^slack * 2^8 below 448.
-  static constexpr float kFrameSlack = KV_FP8 ? 0.75f : 8.f;
-  static constexpr float kPScale = KV_FP8 ? 256.f : 1.f;
-};
-
-__device__ __forceinline__ unsigned pack_e4m3x4(float a, float b, float c, float d) {
-  // OCP E4M3FN, round to nearest even; inputs are clamped to +-448 first
-  // (out-of-range values would otherwise become NaN: the format has no inf).
-  a = fminf(fmaxf(a, -448.f), 448.f);
-  b = fminf(fmaxf(b, -448.f), 448.f);
-  c = fminf(fmaxf(c, -448.f), 448.f);
-  d = fminf(fmaxf(d, -448.f), 448.f);
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-  w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
-  return unsigned(w);
-}
-
-// Byte k of each of a0..a3 gathered into one dword (a 4x4 byte transpose).
-__device__ __forceinline__ unsigned gather_byte(unsigned a0, unsigned a1, unsigned a2,
-                                                unsigned a3, int k) {
-  const int sh = 8 * k;
-  return ((a0 >> sh) & 0xffu) | (((a1 >> sh) & 0xffu) << 8) | (((a2 >> sh) & 0xffu) << 16) |
-         (((a3 >> sh) & 0xffu) << 24);
-}
-
-// Stage the q tile of (request b, heads h0..h0+15) in LDS. bf16: as is.
-// E4M3: each head row becomes two E4M3 rows, q ~ s_hi q_hi + s_lo q_lo: q_hi
-// with scale amax|q| / 448, q_lo the rounding residual with its own
-// amax / 448 scale. One E4M3 term alone carries a 2^-4 relative error into
-// every logit; the residual term brings it to about 2^-8, like bf16.
-template <int KV_FP8>
-__device__ void stage_q(const AttnArgs& a, AttnSmem& sm, int b, int h0) {
-  const int tid = threadIdx.x, H = a.num_heads;
-  const uint16_t* qtile = a.q + (size_t(b) * H + h0) * kDK;
-  if constexpr (!KV_FP8) {
-    const u32x4_t* qsrc = reinterpret_cast<const u32x4_t*>(qtile);
-    for (int i = tid; i < kHeadTile * (kDK / 8); i += kThreads) {
-      const int row = i / (kDK / 8), ch = i - row * (kDK / 8);
-      u32x4_t v = h0 + row < H ? qsrc[i] : u32x4_t{0, 0, 0, 0};
-      *reinterpret_cast<u32x4_t*>(&sm.q[row * kQRowDwordsBf16 + ch * 4]) = v;
-    }
-  } else {
-    // Wave w quantises rows 4w..4w+3; lane handles features 256 blk + 4 lane
-    // .. + 3 for blk = 0, 1 and, in lanes < 16, the 64 rope features (blk 2).
-    const int wave = tid >> 6, lane = tid & 63;
-    for (int rr = 0; rr < 4; ++rr) {
-      const int row = 4 * wave + rr;
-      float v[12];
-      float amax = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 3; ++blk) {
-        u32x2_t w = u32x2_t{0, 0};
-        if (h0 + row < H && (blk < 2 || lane < 16))
-          w = *reinterpret_cast<const u32x2_t*>(qtile + size_t(row) * kDK + blk * 256 + 4 * lane);
-        v[4 * blk + 0] = __builtin_bit_cast(float, w[0] << 16);
-        v[4 * blk + 1] = __builtin_bit_cast(float, w[0] & 0xffff0000u);
-        v[4 * blk + 2] = __builtin_bit_cast(float, w[1] << 16);
-        v[4 * blk + 3] = __builtin_bit_cast(float, w[1] & 0xffff0000u);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) amax = fmaxf(amax, fabsf(v[4 * blk + k]));
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) amax = fmaxf(amax, __shfl_xor(amax, d));
-      const float inv = amax > 0.f ? 448.f / amax : 0.f;
-      const float s_hi = amax > 0.f ? amax / 448.f : 0.f;
-      uint8_t* dst_hi = reinterpret_cast<uint8_t*>(&sm.q[row * kQRowDwordsFp8]);
-      uint8_t* dst_lo = reinterpret_cast<uint8_t*>(&sm.q[(kHeadTile + row) * kQRowDwordsFp8]);
-      float res[12];
-      float amax_lo = 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 3; ++blk) {
-        const unsigned w = pack_e4m3x4(v[4 * blk] * inv, v[4 * blk + 1] * inv,
-                                       v[4 * blk + 2] * inv, v[4 * blk + 3] * inv);
-        if (blk < 2 || lane < 16) *reinterpret_cast<unsigned*>(dst_hi + blk * 256 + 4 * lane) = w;
-        res[4 * blk + 0] = v[4 * blk + 0] - __builtin_amdgcn_cvt_f32_fp8(int(w), 0) * s_hi;
-        res[4 * blk + 1] = v[4 * blk + 1] - __builtin_amdgcn_cvt_f32_fp8(int(w), 1) * s_hi;
-        res[4 * blk + 2] = v[4 * blk + 2] - __builtin_amdgcn_cvt_f32_fp8(int(w), 2) * s_hi;
-        res[4 * blk + 3] = v[4 * blk + 3] - __builtin_amdgcn_cvt_f32_fp8(int(w), 3) * s_hi;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) amax_lo = fmaxf(amax_lo, fabsf(res[4 * blk + k]));
-      }
-#pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) amax_lo = fmaxf(amax_lo, __shfl_xor(amax_lo, d));
-      const float inv_lo = amax_lo > 0.f ? 448.f / amax_lo : 0.f;
-#pragma unroll
-      for (int blk = 0; blk < 3; ++blk) {
-        if (blk < 2 || lane < 16) {
-          const unsigned w = pack_e4m3x4(res[4 * blk] * inv_lo, res[4 * blk + 1] * inv_lo,
-                                         res[4 * blk + 2] * inv_lo, res[4 * blk + 3] * inv_lo);
-          *reinterpret_cast<unsigned*>(dst_lo + blk * 256 + 4 * lane) = w;
-        }
-      }
-      if (lane == 0) {
-        sm.qscale[0][row] = s_hi;
-        sm.qscale[1][row] = amax_lo > 0.f ? amax_lo / 448.f : 0.f;
-      }
-    }
-  }
-}
-
-// Process one piece: tokens of units [u0, u1) of request b, heads of tile ht.
-// piece = index of this piece within the request, pieces = how many it has.
-template <int KV_FP8>
-__device__ void attend_piece(const AttnArgs& a, AttnSmem& sm, int b, int ht, int u0, int u1,
-                             int piece, int pieces) {
-  using L = PvLayout<KV_FP8>;
-  constexpr int kRowBytesKv = KV_FP8 ? kDK : 2 * kDK;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int c = lane & 15, g = lane >> 4;
-  const int H = a.num_heads;
-  const int h0 = ht * kHeadTile;
-  const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
-
-  stage_q<KV_FP8>(a, sm, b, h0);
-  __syncthreads();
-  // Logit scale of head c (log2 domain), including the E4M3 dequantisation
-  // (xscale_lo weighs the residual term of q in the E4M3 path).
-  const float xscale = KV_FP8 ? a.scale_log2 * a.kv_scale * sm.qscale[0][c] : a.scale_log2;
-  const float xscale_lo = KV_FP8 ? a.scale_log2 * a.kv_scale * sm.qscale[1][c] : 0.f;
-
-  // Accumulation frames (log2 domain). The register accumulator holds
-  // sum_t 2^(x_t - m_ref) v_t for the tokens seen since its last flush; the
-  // wave's LDS slot sm.o[wave] holds the earlier tokens in frame m_lds. The
-  // register accumulator is never rescaled in place: when a head's max rises
-  // more than the frame slack above m_ref, the accumulator is folded into the
-  // LDS slot (rescaling only the LDS copy) and restarted from zero in the new
-  // frame. Weights 2^(x - m_ref) therefore stay below 2^slack.
-  f32x4_t acc[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = -INFINITY;  // frame of head c (same value in all 4 lane groups)
-  float l_run = 0.f;        // this lane's share of the denominator of head c, frame m_ref
-  float m_lds[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};  // LDS frame, heads 4g + r
-
-  // Fold acc (frame m_ref) into the LDS slot, which moves to frame m_ref.
-  auto flush = [&]() {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float mr = __shfl(m_ref, 4 * g + r);
-      const bool fresh = m_lds[r] == -INFINITY;
-      const float f = fresh ? 0.f : fast_exp2(m_lds[r] - mr);
-#pragma unroll
-      for (int beta = 0; beta < L::kBlocks; ++beta) {
-        float* dst = &sm.o[wave][4 * g + r][L::kBlockWidth * beta + L::kDimsPerLane * c];
-#pragma unroll
-        for (int e4 = 0; e4 < L::kDimsPerLane; e4 += 4) {
-          const int i0 = beta * L::kDimsPerLane + e4;
-          f32x4_t v = f32x4_t{acc[i0][r], acc[i0 + 1][r], acc[i0 + 2][r], acc[i0 + 3][r]};
-          if (!fresh) v += *reinterpret_cast<const f32x4_t*>(dst + e4) * f;
-          *reinterpret_cast<f32x4_t*>(dst + e4) = v;
-        }
-      }
-      m_lds[r] = mr;
-    }
-  };
-
-  // Move the frame if this tile's max (mt, per head c) rose past the slack.
-  auto update_frame = [&](float mt) {
-    if (__ballot(mt > m_ref + L::kFrameSlack) != 0ull) {  // wave-uniform, rare after warm-up
-      if (__ballot(m_ref != -INFINITY) != 0ull) flush();
-#pragma unroll
-      for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      const float m_new = fmaxf(m_ref, mt);
-      l_run *= m_ref == -INFINITY ? 0.f : fast_exp2(m_ref - m_new);
-      m_ref = m_new;
-    }
-  };
-
-  // Row base of unit u (16 contiguous cached rows), and its valid token count.
-  const int bs_mask = (1 << a.bs_log2) - 1;
-  auto unit_base = [&](int u, int& nvalid) -> const uint8_t* {
-    const int t0 = u * kUnit;
-    nvalid = min(kUnit, n - t0);
-    int blk = nvalid > 0 ? a.block_table[size_t(b) * a.max_blocks + (t0 >> a.bs_log2)] : 0;
-    if (blk < 0 || blk >= a.num_blocks) {  // never read outside the cache
-      blk = 0;
-      nvalid = 0;
-    }
-    if (nvalid < 0) nvalid = 0;
-    return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowBytesKv;
-  };
-
-  const int u_end = min(u1, (n + kUnit - 1) / kUnit);
-  if constexpr (!KV_FP8) {
-    // B operand of the logit MFMA: head c, features 32 s + 8 g .. + 7.
-    const uint32_t* qrow = &sm.q[c * kQRowDwordsBf16 + 4 * g];
-    // K operand of unit u: lane holds token c, features 32 s + 8 g .. + 7.
-    auto load_k = [&](const uint8_t* base, u32x4_t (&kf)[kQChunks]) {
-      const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(base + c * kRowBytesKv) + g;
-#pragma unroll
-      for (int s = 0; s < kQChunks; ++s) kf[s] = kp[4 * s];
-    };
-    // One unit whose K fragment is already in kf; the K fragment of the
-    // wave's next unit is requested into kn before any of this unit's math,
-    // so HBM traffic of the next unit overlaps this unit's compute.
-    auto step = [&](int u, const uint8_t* base, int nvalid, u32x4_t (&kf)[kQChunks],
-                    u32x4_t (&kn)[kQChunks], const uint8_t*& nbase, int& nnvalid) {
-      // V rows for P.V: lane holds tokens 4 g + r, features 128 beta + 8 c .. + 7.
-      u32x4_t vf[4][4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const u32x4_t* vp =
-            reinterpret_cast<const u32x4_t*>(base + (4 * g + r) * kRowBytesKv) + c;
-#pragma unroll
-        for (int beta = 0; beta < 4; ++beta) vf[beta][r] = vp[16 * beta];
-      }
-      if (u + kWaves < u_end) {
-        nbase = unit_base(u + kWaves, nnvalid);
-        load_k(nbase, kn);
-      }
-      // Logits: S^T[token][head] = K . q^T; lane gets tokens 4 g + r of head c.
-      f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < kQChunks; ++s) {
-        const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(qrow + 16 * s);
-        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s]),
-                                                     __builtin_bit_cast(bf16x8_t, qv), sc, 0,
-                                                     0, 0);
-      }
-      float x[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) x[r] = (4 * g + r < nvalid) ? sc[r] * xscale : -INFINITY;
-      float mt = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      update_frame(mt);
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(x[r] - m_use);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      // P as the A operand: head c, tokens 4 g .. 4 g + 3 (already in place).
-      s16x4_t pa;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) pa[r] = (short)bf16_bits(p[r]);
-      // Masked tokens must contribute exactly 0 even if their bytes are NaN.
-      if (nvalid < kUnit) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const unsigned keep = (4 * g + r < nvalid) ? 0xffffffffu : 0u;
-#pragma unroll
-          for (int beta = 0; beta < 4; ++beta) vf[beta][r] &= keep;
-        }
-      }
-      // P.V: for each feature e of the lane's 8, gather the 4 tokens' values
-      // into one B operand (a 4x8 -> 8x4 transpose of 16-bit values).
-#pragma unroll
-      for (int beta = 0; beta < 4; ++beta) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const unsigned d0 = vf[beta][0][i], d1 = vf[beta][1][i];
-          const unsigned d2 = vf[beta][2][i], d3 = vf[beta][3][i];
-          u32x2_t ve = u32x2_t{(d0 & 0xffffu) | (d1 << 16), (d2 & 0xffffu) | (d3 << 16)};
-          u32x2_t vo =
-              u32x2_t{(d0 >> 16) | (d1 & 0xffff0000u), (d2 >> 16) | (d3 & 0xffff0000u)};
-          acc[beta * 8 + 2 * i] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              pa, __builtin_bit_cast(s16x4_t, ve), acc[beta * 8 + 2 * i], 0, 0, 0);
-          acc[beta * 8 + 2 * i + 1] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-              pa, __builtin_bit_cast(s16x4_t, vo), acc[beta * 8 + 2 * i + 1], 0, 0, 0);
-        }
-      }
-    };
-    u32x4_t ka[kQChunks], kb[kQChunks];
-    int u = u0 + wave;
-    int nv_a = 0, nv_b = 0;
-    const uint8_t* base_a = nullptr;
-    const uint8_t* base_b = nullptr;
-    if (u < u_end) {
-      base_a = unit_base(u, nv_a);
-      load_k(base_a, ka);
-    }
-    for (; u < u_end; u += kWaves) {
-      step(u, base_a, nv_a, ka, kb, base_b, nv_b);
-#pragma unroll
-      for (int s2 = 0; s2 < kQChunks; ++s2) ka[s2] = kb[s2];
-      base_a = base_b;
-      nv_a = nv_b;
-    }
-  } else {
-    // E4M3 cache: units go in pairs (u, u + kWaves) so that one P.V MFMA
-    // (K = 32) covers 32 tokens: k slots 0..3 of lane group g hold tokens
-    // 4 g .. 4 g + 3 of the first unit, slots 4..7 those of the second.
-    // Logit B operand: head c; 16-byte chunk j of the row feeds k-steps 2j
-    // (low 8 bytes) and 2j + 1 (high 8 bytes), lane group g taking bytes
-    // 64 j + 16 g .. + 15 of both operands alike.
-    const uint32_t* qrow = &sm.q[c * kQRowDwordsFp8 + 4 * g];
-    const uint32_t* qrow_lo = &sm.q[(kHeadTile + c) * kQRowDwordsFp8 + 4 * g];
-    for (int u = u0 + wave; u < u_end; u += 2 * kWaves) {
-      int nv[2];
-      const uint8_t* base[2] = {unit_base(u, nv[0]), unit_base(u + kWaves, nv[1])};
-      if (u + kWaves >= u_end) nv[1] = 0;
-      u32x4_t kf[2][kDK / 64];
-      u32x4_t vf[2][2][4];  // [unit][beta][r]: tokens 4 g + r, features 256 beta + 16 c ..
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const u32x4_t* kp = reinterpret_cast<const u32x4_t*>(base[h] + c * kRowBytesKv) + g;
-#pragma unroll
-        for (int j = 0; j < kDK / 64; ++j) kf[h][j] = kp[4 * j];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const u32x4_t* vp =
-              reinterpret_cast<const u32x4_t*>(base[h] + (4 * g + r) * kRowBytesKv) + c;
-#pragma unroll
-          for (int beta = 0; beta < 2; ++beta) vf[h][beta][r] = vp[16 * beta];
-        }
-      }
-      float x[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};     // K . q_hi
-        f32x4_t sc_lo = f32x4_t{0.f, 0.f, 0.f, 0.f};  // K . q_lo
-#pragma unroll
-        for (int j = 0; j < kDK / 64; ++j) {
-          const u32x4_t qv = *reinterpret_cast<const u32x4_t*>(qrow + 16 * j);
-          const u32x4_t qw = *reinterpret_cast<const u32x4_t*>(qrow_lo + 16 * j);
-          const long k_lo = __builtin_bit_cast(long, u32x2_t{kf[h][j][0], kf[h][j][1]});
-          const long k_hi = __builtin_bit_cast(long, u32x2_t{kf[h][j][2], kf[h][j][3]});
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-              k_lo, __builtin_bit_cast(long, u32x2_t{qv[0], qv[1]}), sc, 0, 0, 0);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-              k_hi, __builtin_bit_cast(long, u32x2_t{qv[2], qv[3]}), sc, 0, 0, 0);
-          sc_lo = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-              k_lo, __builtin_bit_cast(long, u32x2_t{qw[0], qw[1]}), sc_lo, 0, 0, 0);
-          sc_lo = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(
-              k_hi, __builtin_bit_cast(long, u32x2_t{qw[2], qw[3]}), sc_lo, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          x[h][r] = (4 * g + r < nv[h]) ? sc[r] * xscale + sc_lo[r] * xscale_lo : -INFINITY;
-      }
-      float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                       fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-      mt = fmaxf(mt, __shfl_xor(mt, 16));
-      mt = fmaxf(mt, __shfl_xor(mt, 32));
-      update_frame(mt);
-      const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-      float p[2][4];
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_use);
-      l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-               ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-      // P in E4M3 as two terms: the rounded p * 2^8 and its rounding residual
-      // (also E4M3), both multiplied into the same accumulator. A single E4M3
-      // weight carries up to 2^-4 relative error, which short or peaked
-      // softmax rows do not average away.
-      unsigned ph[2], pl[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float ps[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) ps[r] = p[h][r] * L::kPScale;
-        ph[h] = pack_e4m3x4(ps[0], ps[1], ps[2], ps[3]);
-        pl[h] = pack_e4m3x4(ps[0] - __builtin_amdgcn_cvt_f32_fp8(int(ph[h]), 0),
-                            ps[1] - __builtin_amdgcn_cvt_f32_fp8(int(ph[h]), 1),
-                            ps[2] - __builtin_amdgcn_cvt_f32_fp8(int(ph[h]), 2),
-                            ps[3] - __builtin_amdgcn_cvt_f32_fp8(int(ph[h]), 3));
-      }
-      const long pa_hi = __builtin_bit_cast(long, u32x2_t{ph[0], ph[1]});
-      const long pa_lo = __builtin_bit_cast(long, u32x2_t{pl[0], pl[1]});
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        if (nv[h] < kUnit) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const unsigned keep = (4 * g + r < nv[h]) ? 0xffffffffu : 0u;
-#pragma unroll
-            for (int beta = 0; beta < 2; ++beta) vf[h][beta][r] &= keep;
-          }
-        }
-      }
-      // P.V: feature 256 beta + 16 c + 4 i + k of the 4 tokens of each unit,
-      // gathered by a 4x4 byte transpose, forms one 8-byte B operand.
-#pragma unroll
-      for (int beta = 0; beta < 2; ++beta) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const unsigned w0 = gather_byte(vf[0][beta][0][i], vf[0][beta][1][i],
-                                            vf[0][beta][2][i], vf[0][beta][3][i], k);
-            const unsigned w1 = gather_byte(vf[1][beta][0][i], vf[1][beta][1][i],
-                                            vf[1][beta][2][i], vf[1][beta][3][i], k);
-            const int ai = beta * 16 + 4 * i + k;
-            const long vb = __builtin_bit_cast(long, u32x2_t{w0, w1});
-            acc[ai] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pa_hi, vb, acc[ai], 0, 0, 0);
-            acc[ai] = __builtin_amdgcn_mfma_f32_16x16x32_fp8_fp8(pa_lo, vb, acc[ai], 0, 0, 0);
-          }
-        }
-      }
-    }
-  }
-
-  // ---- merge the four waves through LDS ----
-  // Final fold: the wave's whole sum now sits in sm.o[wave], frame m_ref.
-  flush();
-  float l_c = l_run + __shfl_xor(l_run, 16);
-  l_c += __shfl_xor(l_c, 32);
-  if (g == 0) {
-    sm.m[wave][c] = m_ref;
-    sm.l[wave][c] = l_c;
-  }
-  __syncthreads();
-  {
-    const bool final_out = pieces == 1;
-    const int row = final_out ? 0 : a.row_ptr[b] + piece;
-    const float out_scale = KV_FP8 ? a.kv_scale / L::kPScale : 1.f;
-#pragma unroll
-    for (int j = 0; j < (kHeadTile * kDV / 4) / kThreads; ++j) {
-      const int qi = j * kThreads + tid;
-      const int hh = qi >> 7;           // 128 four-wide chunks per head
-      const int d = (qi & 127) << 2;
-      const int h = h0 + hh;
-      if (h >= H) continue;
-      float M = fmaxf(fmaxf(sm.m[0][hh], sm.m[1][hh]), fmaxf(sm.m[2][hh], sm.m[3][hh]));
-      float Lsum = 0.f;
-      f32x4_t sum = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm.m[w][hh];
-        if (mw == -INFINITY) continue;  // this wave saw no token of the piece
-        const float f = fast_exp2(mw - M);
-        Lsum += sm.l[w][hh] * f;
-        sum += *reinterpret_cast<const f32x4_t*>(&sm.o[w][hh][d]) * f;
-      }
-      const float inv = Lsum > 0.f ? out_scale / Lsum : 0.f;
-      const float lse_v = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : -INFINITY;
-      sum *= inv;
-      if (final_out) {
-        u32x2_t pk;
-        pk[0] = unsigned(bf16_bits(sum[0])) | (unsigned(bf16_bits(sum[1])) << 16);
-        pk[1] = unsigned(bf16_bits(sum[2])) | (unsigned(bf16_bits(sum[3])) << 16);
-        *reinterpret_cast<u32x2_t*>(a.out + (size_t(b) * H + h) * kDV + d) = pk;
-        if (d == 0 && a.lse) a.lse[size_t(b) * H + h] = lse_v;
-      } else {
-        *reinterpret_cast<f32x4_t*>(a.part_out + (size_t(row) * H + h) * kDV + d) = sum;
-        if (d == 0) a.part_lse[size_t(row) * H + h] = lse_v;
-      }
-    }
-  }
-  __syncthreads();  // LDS is reused by the next piece
-}
-
 // Partition -> pieces. Calls fn(b, u0, u1, piece, pieces) for every piece of
 // partition `part`: one piece in forced mode, every request overlapping the
 // partition's cost range in balanced mode. Uniform across the workgroup.
@@ -681,20 +214,6 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, Fn&&
     if (last) return;
     ++b;
   }
-}
-
-template <int KV_FP8>
-__global__ void __launch_bounds__(kThreads, 1) attn_kernel(AttnArgs a) {
-  __shared__ AttnSmem sm;
-  // Workgroups are dispatched to the 8 XCDs round robin. Give the head tiles
-  // of one partition the same XCD (shared L2) and adjacent dispatch slots.
-  const int lin = blockIdx.x;
-  const int xcd = lin & 7, slot = lin >> 3;
-  const int ht = slot % a.head_tiles;
-  const int part = (slot / a.head_tiles) * 8 + xcd;
-  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
-    attend_piece<KV_FP8>(a, sm, b, ht, u0, u1, piece, pieces);
-  });
 }
 
 // ----------------------------------------------------------------------------

@@ -34,15 +34,17 @@ def test_tiny(orc, num_splits, poison):
     _check(orc, wl, num_splits, what=f"tiny splits={num_splits} poison={poison}")
 
 
+@pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
 @pytest.mark.parametrize("block_size", [16, 32, 64, 128])
 @pytest.mark.parametrize("num_heads", [1, 5, 16, 20, 128])
-def test_ragged_edges(orc, block_size, num_heads):
-    lens = [0, 1, 15, 16, 17, 31, 33, 64, 129, 700]
+def test_ragged_edges(orc, block_size, num_heads, kv_dtype):
+    # lengths around unit (16), bf16 tile (32) and fp8 tile (64) boundaries
+    lens = [0, 1, 15, 16, 17, 31, 33, 63, 64, 65, 129, 700]
     wl = workloads.make_workload(batch=len(lens), num_heads=num_heads, seq=("fixed", lens),
                                  block_size=block_size, seed=100 + block_size + num_heads,
-                                 pool_blocks=None, poison=True)
+                                 kv_dtype=kv_dtype, pool_blocks=None, poison=True)
     for s in (0, 1, 4):
-        _check(orc, wl, s, what=f"edges bs={block_size} H={num_heads} splits={s}")
+        _check(orc, wl, s, what=f"edges {kv_dtype} bs={block_size} H={num_heads} splits={s}")
 
 
 @pytest.mark.parametrize("name", ["v2lite-1", "v2lite-8", "v2lite-64"])
@@ -138,6 +140,24 @@ def test_determinism_bitwise(num_splits):
         assert torch.equal(out_a, out_b) and torch.equal(lse_a, lse_b)
 
 
+def test_head_padding_to_128_fp8(orc):
+    wl = workloads.make_workload(batch=3, num_heads=16, seq=("fixed", [37, 130, 1000]),
+                                 block_size=64, seed=24, kv_dtype="fp8", poison=True)
+    out16, lse16 = to_np(*run_gpu(wl, 0))
+    q128 = torch.zeros((wl.batch, 128, 576), dtype=torch.bfloat16)
+    q128[:, :16] = wl.q
+    wl128 = workloads.Workload(name="fp8-pad128", q=q128, kv=wl.kv,
+                               block_table=wl.block_table, seq_lens=wl.seq_lens,
+                               block_size=wl.block_size, kv_dtype=wl.kv_dtype,
+                               kv_scale=wl.kv_scale)
+    out128, lse128 = to_np(*run_gpu(wl128, 0))
+    ref_out, ref_lse = run_oracle(orc, wl128)
+    compare(out128, lse128, ref_out, ref_lse, "fp8", what="fp8 padded to 128 heads")
+    compare(out16, lse16, ref_out[:, :16], ref_lse[:, :16], "fp8", what="fp8 16 heads")
+    for b in range(wl.batch):
+        np.testing.assert_allclose(lse128[b, 16:], np.log(int(wl.seq_lens[b])), atol=1e-3)
+
+
 def test_head_padding_to_128(orc):
     wl = workloads.make_config("tiny")
     out16, lse16 = to_np(*run_gpu(wl, 0))
@@ -158,13 +178,14 @@ def test_head_padding_to_128(orc):
         np.testing.assert_allclose(lse128[b, 16:], np.log(n), atol=1e-3)
 
 
-def test_split_counts_agree(orc):
-    wl = workloads.make_workload(batch=3, num_heads=16, seq=("fixed", [2000, 37, 4097]),
-                                 block_size=64, seed=23, poison=True)
+@pytest.mark.parametrize("kv_dtype,num_heads", [("bf16", 16), ("bf16", 64), ("fp8", 48)])
+def test_split_counts_agree(orc, kv_dtype, num_heads):
+    wl = workloads.make_workload(batch=3, num_heads=num_heads, seq=("fixed", [2000, 37, 4097]),
+                                 block_size=64, seed=23, kv_dtype=kv_dtype, poison=True)
     ref_out, ref_lse = run_oracle(orc, wl)
     for s in range(0, 17):
         out, lse = to_np(*run_gpu(wl, s))
-        compare(out, lse, ref_out, ref_lse, what=f"splits={s}")
+        compare(out, lse, ref_out, ref_lse, kv_dtype, what=f"{kv_dtype} H={num_heads} splits={s}")
 
 
 def test_small_workspace_auto_mode(orc):
