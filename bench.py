@@ -232,11 +232,11 @@ def main(argv=None) -> int:
     mfma_peak = PEAK_MFMA_TFLOPS["fp8" if wl.kv_dtype == "fp8" else "bf16"]
     traffic = measured_traffic(args.config, kernel_source_hash())
     if wl.kv_dtype == "fp8":
-        kernel_name = "mla::attn_fp8_kernel"
+        kernel_name = "mla::attn_mh_kernel<1>"
     elif wl.num_heads <= 16:
         kernel_name = "mla::attn_ws_kernel"
     else:
-        kernel_name = "mla::attn_heads_kernel"
+        kernel_name = "mla::attn_mh_kernel<0>"
     # The roof that bounds the call: whichever of HBM bytes and matrix-core
     # flops needs more time at peak.
     t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)

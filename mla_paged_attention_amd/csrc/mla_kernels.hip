@@ -21,8 +21,9 @@
 //     one-piece request is written as the final bf16 output and LSE, a piece
 //     of a split request as a normalised fp32 partial plus its LSE. Three
 //     variants: attn_ws_kernel (bf16, up to 16 heads: a logit wave feeds four
-//     P.V waves), attn_heads_kernel (bf16, more heads: four waves of 16
-//     heads each), attn_fp8_kernel (E4M3 cache, any head count).
+//     P.V waves), attn_mh_kernel<0> (bf16, more heads) and
+//     attn_mh_kernel<1> (E4M3 cache, any head count): four logit waves of
+//     16 heads each feed four P.V waves of 128 output features each.
 //
 //  3. combine_kernel: log-sum-exp merge of the partial rows of each split
 //     request (PR #20769, summary of changes: the reduction kernel that
@@ -620,265 +621,17 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// Many-head tile stream (bf16 cache, more than 16 heads). Each workgroup
-// covers up to four 16-head tiles: wave w owns head tile 4 hg + w (hg = the
-// workgroup's head group) with all 512 output features, so the logits of a
-// head tile are computed once and the KV tile in LDS feeds four head tiles.
-// Head groups of one partition run on the same XCD in adjacent dispatch
-// slots, so the second group's ring loads are L2 hits. Ring, DMA map and
-// waits as in the 16-head kernels.
-// Frame of the many-head kernel: set from the first tile's maxima and
+// Frame of the many-head kernel: set from each head's first-tile maximum and
 // never moved while weights 2^(x - frame) stay below 2^kHeadsSlack, so fp32
 // accumulators cannot overflow. A head whose logits ever rise further makes
 // the workgroup stream the piece a second time with the frame preset to the
-// true maximum observed in the first pass (the first pass's sums are
-// discarded), so the accumulators are only ever zeroed or MFMA-updated.
+// true maximum observed in the first pass (the first pass's sums of that
+// head tile are discarded), so the accumulators are only ever cleared or
+// updated by matrix ops.
 constexpr float kHeadsSlack = 64.f;
 
-__global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
-  __shared__ uint8_t ring[kStages][kTileBytesBf16];
-  __shared__ int redo_any;
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
-  const int c = lane & 15, g = lane >> 4;
-  const int H = a.num_heads;
-
-  const int lin = blockIdx.x;
-  const int xcd = lin & 7, slot = lin >> 3;
-  const int hg = slot % a.head_groups;
-  const int part = (slot / a.head_groups) * 8 + xcd;
-  const int ht = 4 * hg + wave;
-  const bool active = ht < a.head_tiles;  // inactive waves only stream the ring
-  const int h0 = ht * kHeadTile;
-
-  uint32_t dma_off[kDmaPerThread];
-  uint32_t dma_hi = 0;
-#pragma unroll
-  for (int i = 0; i < kDmaPerThread; ++i) {
-    const int pos = i * kThreads + tid;
-    const int t = pos / kRowChunks, sl = pos - (pos / kRowChunks) * kRowChunks;
-    const int ch = sl ^ (t & 7);
-    dma_off[i] = uint32_t((t & 15) * kRowBytes + ch * 16);
-    dma_hi |= uint32_t(t >> 4) << i;
-  }
-  const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
-      (void __attribute__((address_space(3)))*)(&ring[0][0])));
-  const int bs_mask = (1 << a.bs_log2) - 1;
-
-  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
-    const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
-    const int u_end = min(u1, (n + kUnit - 1) / kUnit);
-    const int ntiles = u_end > u0 ? (u_end - u0 + 1) / 2 : 0;
-    const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
-    auto tile_nv = [&](int k, int (&nv)[2]) {
-      const int t0 = (u0 + 2 * k) * kUnit;
-      nv[0] = min(kUnit, n - t0);
-      nv[1] = u0 + 2 * k + 1 < u_end ? min(kUnit, n - t0 - kUnit) : 0;
-    };
-    auto unit_rows = [&](int u) -> const uint8_t* {
-      const int t0 = u * kUnit;
-      int blk = scalar_load_i32(bt_row + (t0 >> a.bs_log2));
-      if (blk < 0 || blk >= a.num_blocks) blk = 0;
-      return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowBytes;
-    };
-    auto issue_tile = [&](int k) {
-      int nv[2];
-      tile_nv(k, nv);
-      const uint8_t* r0 = unit_rows(u0 + 2 * k);
-      const uint8_t* r1 = nv[1] > 0 ? unit_rows(u0 + 2 * k + 1) : r0;
-      uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
-#pragma unroll
-      for (int i = 0; i < kDmaPerThread; ++i) {
-        const uint8_t* src = ((dma_hi >> i) & 1 ? r1 : r0) + dma_off[i];
-        __builtin_amdgcn_global_load_lds(
-            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0, 0);
-      }
-    };
-
-    // q fragment of this wave's head tile (padded heads repeat head H - 1).
-    u32x4_t qf[kQChunks];
-    {
-      const int hq = min(h0 + c, H - 1);
-      const u32x4_t* qp = reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + hq) * kDK) + g;
-#pragma unroll
-      for (int s2 = 0; s2 < kQChunks; ++s2) qf[s2] = qp[4 * s2];
-    }
-
-    f32x4_t acc[32];      // acc[n][r]: head 4 g + r, feature 16 n + c
-    float m_ref = -INFINITY;  // frame of head c (log2 domain)
-    float m_seen = -INFINITY; // largest logit of head c seen in the first pass
-    float l_run = 0.f;        // lane's share of head c's denominator
-    bool redo = false;        // this wave's frame was exceeded in the first pass
-
-    for (int pass = 0; pass < 2; ++pass) {
-      // Pass 1 recomputes only the waves that asked for it; the others keep
-      // their pass-0 sums and frame.
-      const bool work = active && (pass == 0 || redo);
-      if (work) {
-        if (pass == 1) m_ref = m_seen;  // preset frame: no weight exceeds 1
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        l_run = 0.f;
-      }
-      redo = false;
-
-      wave_barrier_all();  // the ring of the previous pass or piece is consumed
-      wait_vmem<0>();      // q has landed; only ring loads are in flight from here
-      for (int k = 0; k < kStages - 1 && k < ntiles; ++k) issue_tile(k);
-
-      if (!work) {
-        // Waves without a head tile (or with nothing to redo) keep the ring
-        // moving: same waits, barriers and loads as the computing waves.
-        for (int j = 0; j < ntiles; ++j) {
-          wait_ring<kStages - 2>(ntiles - 1 - j);
-          wave_barrier_all();
-          if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
-        }
-      } else for (int j = 0; j < ntiles; ++j) {
-        wait_ring<kStages - 2>(ntiles - 1 - j);
-        wave_barrier_all();
-        if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
-
-        const uint32_t st = ring_lds + uint32_t(j % kStages) * kTileBytesBf16;
-        int nv[2];
-        tile_nv(j, nv);
-        float x[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int t = h * kUnit + c;
-          const uint32_t y = uint32_t(g ^ (c & 7));
-          const uint32_t row = st + uint32_t(t * kRowBytes);
-          u32x4_t kf[kQChunks];
-          lds_read_k(row + 16 * y, row + 16 * (y ^ 4), kf);
-          f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int s2 = 0; s2 < kQChunks; ++s2)
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, kf[s2]),
-                                                         __builtin_bit_cast(bf16x8_t, qf[s2]), sc,
-                                                         0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x[h][r] = (4 * g + r < nv[h]) ? sc[r] * a.scale_log2 : -INFINITY;
-        }
-        float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
-                         fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        m_seen = fmaxf(m_seen, mt);
-        if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): set the frame
-        // Once set, the pass's sums are discarded; they are still computed
-        // so that the accumulators see no branch.
-        if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
-        float p[2][4];
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_ref);
-        l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
-                 ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
-        bf16x8_t pa;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          pa[r] = (__bf16)p[0][r];
-          pa[4 + r] = (__bf16)p[1][r];
-        }
-        // P.V over 16-feature blocks n = 4 M + n' (features 16 n .. 16 n + 15).
-        // Lane s = 4 e + a of group g points at token row 4 g + e (and 16 more),
-        // features 16 n + 4 a .. + 3, so the transposing read hands lane c the
-        // B operand column of feature 16 n + c over tokens 4 g .. 4 g + 3 (and
-        // 16 + 4 g ..), the same token slots the P operand holds.
-        uint32_t vb[4];
-        {
-          const int s4 = lane & 15, av = s4 & 3, ev = s4 >> 2;
-          const int t0 = 4 * g + ev;
-#pragma unroll
-          for (int n2 = 0; n2 < 4; ++n2)
-            vb[n2] = st + uint32_t(t0 * kRowBytes) +
-                     16u * uint32_t((2 * n2 + (av >> 1)) ^ (t0 & 7)) + 8u * uint32_t(av & 1);
-        }
-        // Tokens past the end of a partial unit: zero their V elements (their
-        // P is zero, but unused rows may hold non-finite bit patterns).
-        uint64_t vkeep[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int kc = min(max(nv[h] - 4 * g, 0), 4);
-          vkeep[h] = kc >= 4 ? ~0ull : ((1ull << (16 * kc)) - 1ull);
-        }
-        const bool vmask = (nv[0] < kUnit) | (nv[1] < kUnit);
-        auto pv_group = [&](auto mc) {
-          constexpr int M = decltype(mc)::value;
-          u32x2_t t[4][2];
-          lds_read_tr8<M>(vb, t);
-          if (vmask) {
-#pragma unroll
-            for (int n2 = 0; n2 < 4; ++n2)
-#pragma unroll
-              for (int h = 0; h < 2; ++h)
-                t[n2][h] = __builtin_bit_cast(
-                    u32x2_t, __builtin_bit_cast(uint64_t, t[n2][h]) & vkeep[h]);
-          }
-#pragma unroll
-          for (int n2 = 0; n2 < 4; ++n2) {
-            const u32x4_t bv = u32x4_t{t[n2][0][0], t[n2][0][1], t[n2][1][0], t[n2][1][1]};
-            acc[4 * M + n2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                pa, __builtin_bit_cast(bf16x8_t, bv), acc[4 * M + n2], 0, 0, 0);
-          }
-        };
-        pv_group(std::integral_constant<int, 0>{});
-        pv_group(std::integral_constant<int, 1>{});
-        pv_group(std::integral_constant<int, 2>{});
-        pv_group(std::integral_constant<int, 3>{});
-        pv_group(std::integral_constant<int, 4>{});
-        pv_group(std::integral_constant<int, 5>{});
-        pv_group(std::integral_constant<int, 6>{});
-        pv_group(std::integral_constant<int, 7>{});
-      }
-      // Does any wave need a second pass?
-      if (tid == 0) redo_any = 0;
-      wave_barrier_lds();
-      if (work && redo && lane == 0) redo_any = 1;
-      wave_barrier_lds();
-      if (redo_any == 0) break;
-    }
-
-    if (active) {
-      float l_c = l_run + __shfl_xor(l_run, 16);
-      l_c += __shfl_xor(l_c, 32);
-      const bool final_out = pieces == 1;
-      const int row = final_out ? 0 : a.row_ptr[b] + piece;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hh = 4 * g + r;
-        const int h = h0 + hh;
-        const float lh = __shfl(l_c, hh);
-        const float inv = lh > 0.f ? 1.f / lh : 0.f;
-        if (h < H) {
-          // acc[n][r]: head 4 g + r, feature 16 n + c.
-          if (final_out) {
-            uint16_t* dst = a.out + (size_t(b) * H + h) * kDV + c;
-#pragma unroll
-            for (int n = 0; n < 32; ++n) dst[16 * n] = bf16_bits(acc[n][r] * inv);
-          } else {
-            float* dst = a.part_out + (size_t(row) * H + h) * kDV + c;
-#pragma unroll
-            for (int n = 0; n < 32; ++n) dst[16 * n] = acc[n][r] * inv;
-          }
-        }
-      }
-      if (g == 0 && h0 + c < H) {
-        const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
-        if (final_out) {
-          if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
-        } else {
-          a.part_lse[size_t(row) * H + h0 + c] = lse_v;
-        }
-      }
-    }
-  });
-}
-
 // ----------------------------------------------------------------------------
-// E4M3 cache: the many-head tile stream on scaled 16x16x128 E4M3 matrix ops.
+// E4M3 cache: scaled 16x16x128 E4M3 matrix ops (used by attn_mh_kernel<1>).
 //
 // A tile is 64 tokens (four 16-token units) of 576-byte rows, 36,864 bytes as
 // in the bf16 kernels, so ring, DMA map and waits are theirs. Chunk ch (16
@@ -886,10 +639,11 @@ __global__ void __launch_bounds__(kThreads, 1) attn_heads_kernel(AttnArgs a) {
 // aligned group of four chunks that keeps both read patterns below free of
 // LDS bank conflicts.
 //
-// Logits: one op covers 64 dimensions twice. A holds K's 16 bytes of the
-// lane's dimension group twice, B holds q's rounded E4M3 term and its
-// residual (both in q's per-head scale amax / 448), so one instruction sums
-// K . (q_hi + q_lo), q to about 2^-8 relative error as with bf16.
+// Logits: q is carried as its rounded E4M3 term and the term's residual,
+// both in q's per-head scale amax / 448 (about 2^-8 relative error, as with
+// bf16). One op covers 128 dimensions against q_hi and a second the same
+// K bytes against q_lo; the last 64 dimensions fill one op with K's bytes
+// twice against (q_hi, q_lo).
 // P.V: one op covers the tile's 64 tokens twice. A holds P_hi and P_lo (the
 // rounded weight times 2^8 and its E4M3 residual) of 16 tokens per lane
 // group, B the same V bytes twice, read with ds_read_b64_tr_b8.
@@ -907,8 +661,11 @@ static_assert(kTileFp8 * kRowChunksFp8 == kDmaPerThread * kThreads, "tile must s
 
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
+// Slot permutation of row t (measured free of bank conflicts for both the
+// K reads and the transposing V reads; depends on bits 1, 2 and 4 of t only,
+// so rows 32 apart and units of equal parity share it).
 __device__ __forceinline__ int fp8_swizzle(int t) {
-  return ((t >> 2) & 3) ^ (((t >> 4) & 1) << 1);
+  return ((t >> 1) ^ ((t >> 4) & 1)) & 3;
 }
 
 // E4M3 encoding without range clamp (callers guarantee |x| <= 448).
@@ -967,62 +724,117 @@ __device__ __forceinline__ f32x4_t mfma_e4m3_128(const i32x8_t& a, const i32x8_t
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, scale_a, 0, 127);
 }
 
-__global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
+// ----------------------------------------------------------------------------
+// Many-head wave-specialised tile stream (more than 16 heads, or an E4M3
+// cache): eight waves per workgroup, up to four 16-head tiles.
+//
+// Waves 4..7 are logit waves: wave 4 + t computes the logits and softmax of
+// head tile t (q in registers, K from LDS) for tile s of the stream and
+// leaves P, already in the A-operand layout, in LDS. Waves 0..3 are P.V
+// waves: wave f owns output features 128 f .. 128 f + 127 of all four head
+// tiles, reads its quarter of V once per tile and multiplies it against the
+// four tiles' P (four matrix ops per V fragment), and issues the ring's
+// direct-to-LDS loads. Waves f and 4 + f share a SIMD, so one wave's softmax,
+// LDS waits and barriers overlap the other's matrix ops. At step s the logit
+// waves work on tile s and the P.V waves on tile s - 1; P is handed over
+// through a single LDS buffer between two barriers per step.
+//
+// Frames as in the per-tile kernels: each head's frame is its first tile's
+// maximum; bf16 weights up to 2^64 are accumulated as they are, E4M3 weights
+// carry the tile's exponent rise in the op's E8M0 scale. A head tile whose
+// logits rise more than 64 above its frame is recomputed in a second pass
+// with the frame preset (the other tiles then contribute zero weights).
+constexpr int kMhWaves = 8;
+constexpr int kMhThreads = 64 * kMhWaves;
+
+template <int KV_FP8>
+__global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
+  constexpr int kTok = KV_FP8 ? 4 * kUnit : 2 * kUnit;   // tokens per tile
+  constexpr int kUnits = kTok / kUnit;
+  constexpr int kRowB = KV_FP8 ? kDK : 2 * kDK;          // bytes per cached row
+  constexpr int kRowCh = kRowB / 16;
+  constexpr int kPWords = KV_FP8 ? 2 : 1;                 // u32x4 per lane of P
+  static_assert(kTok * kRowB == kTileBytesBf16, "tile size");
+  static_assert(kTok * kRowCh == kDmaPerThread * kThreads, "tile must split evenly");
+
   __shared__ uint8_t ring[kStages][kTileBytesBf16];
+  __shared__ __attribute__((aligned(32))) u32x4_t pbuf[4][64][kPWords];  // P per head tile, lane
+  __shared__ int ebuf[4][kHeadTile];        // E4M3: E8M0 scale of P per head
+  __shared__ float lbuf[4][kHeadTile];      // final softmax denominators
+  __shared__ int redo_tile[4];
   __shared__ int redo_any;
+
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
+  const bool logit_wave = wave >= 4;
+  const int wq = wave & 3;  // logit waves: head tile; P.V waves: feature quarter
   const int H = a.num_heads;
 
   const int lin = blockIdx.x;
   const int xcd = lin & 7, slot = lin >> 3;
   const int hg = slot % a.head_groups;
   const int part = (slot / a.head_groups) * 8 + xcd;
-  const int ht = 4 * hg + wave;
-  const bool active = ht < a.head_tiles;  // inactive waves only stream the ring
-  const int h0 = ht * kHeadTile;
+  const int ht0 = 4 * hg;                                 // first head tile of the group
+  const bool lw_active = logit_wave && ht0 + wq < a.head_tiles;
+  const int h0 = (ht0 + wq) * kHeadTile;                  // logit wave's first head
 
-  // DMA map: load i fills LDS slot i * 256 + tid of the stage, which holds
-  // chunk (slot ^ swizzle) of row t of unit t >> 4.
+  // DMA map of the P.V waves (thread tid < 256): load i fills LDS slot
+  // i * 256 + tid of the stage.
   uint32_t dma_off[kDmaPerThread];
   uint32_t dma_unit = 0;  // two bits per load
 #pragma unroll
   for (int i = 0; i < kDmaPerThread; ++i) {
-    const int pos = i * kThreads + tid;
-    const int t = pos / kRowChunksFp8, sl = pos - (pos / kRowChunksFp8) * kRowChunksFp8;
-    const int ch = sl ^ fp8_swizzle(t);
-    dma_off[i] = uint32_t((t & 15) * kDK + ch * 16);
+    const int pos = i * kThreads + (tid & (kThreads - 1));
+    const int t = pos / kRowCh, sl = pos - (pos / kRowCh) * kRowCh;
+    const int ch = KV_FP8 ? (sl ^ fp8_swizzle(t)) : (sl ^ (t & 7));
+    dma_off[i] = uint32_t((t & 15) * kRowB + ch * 16);
     dma_unit |= uint32_t(t >> 4) << (2 * i);
   }
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (void __attribute__((address_space(3)))*)(&ring[0][0])));
   const int bs_mask = (1 << a.bs_log2) - 1;
 
-  // Per-lane LDS read bases that do not depend on the stage.
-  // K: row c of a unit, chunk 4 m + (g ^ swizzle): units 0, 2 and 1, 3.
-  const uint32_t k_even = uint32_t(c * kDK + 16 * (g ^ fp8_swizzle(c)));
-  const uint32_t k_odd = uint32_t(c * kDK + 16 * (g ^ fp8_swizzle(16 + c)));
-  // V: lane s = 2 e + a of group g points at row 16 (e >> 2) + 4 g + (e & 3)
-  // (and 32 rows further), bytes 16 n + 8 a.
+  // Stage-independent LDS offsets.
+  // Logit waves, K: bf16 row c of each unit at chunk pairs (g ^ (c & 7)) and
+  // its partner; E4M3 row c, chunk 4 m + (g ^ swizzle) (units of equal parity
+  // share the swizzle).
+  uint32_t k_off0, k_off1;
+  if constexpr (KV_FP8) {
+    k_off0 = uint32_t(c * kDK + 16 * (g ^ fp8_swizzle(c)));
+    k_off1 = uint32_t(c * kDK + 16 * (g ^ fp8_swizzle(16 + c)));
+  } else {
+    const uint32_t y = uint32_t(g ^ (c & 7));
+    k_off0 = uint32_t(c * kRowB) + 16 * y;
+    k_off1 = uint32_t(c * kRowB) + 16 * (y ^ 4);
+  }
+  // P.V waves, V: transposing reads of features 128 wq + 16 n' + ..,
+  // n' = 4 M + j; v_off[j] is the lane's address for j (M in the immediate).
   uint32_t v_off[4];
-  {
+  if constexpr (KV_FP8) {
     const int s4 = lane & 15, av = s4 & 1, ev = s4 >> 1;
     const int t = 16 * (ev >> 2) + 4 * g + (ev & 3);
 #pragma unroll
-    for (int n2 = 0; n2 < 4; ++n2)
-      v_off[n2] = uint32_t(t * kDK + 16 * (n2 ^ fp8_swizzle(t)) + 8 * av);
+    for (int j = 0; j < 4; ++j)
+      v_off[j] = uint32_t(t * kDK + 16 * (8 * wq + (j ^ fp8_swizzle(t))) + 8 * av);
+  } else {
+    const int s4 = lane & 15, av = s4 & 3, ev = s4 >> 2;
+    const int t0 = 4 * g + ev;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      v_off[j] = uint32_t(t0 * kRowB) +
+                 16u * uint32_t(16 * wq + ((2 * j + (av >> 1)) ^ (t0 & 7))) + 8u * uint32_t(av & 1);
   }
 
   for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
     const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
-    const int ntiles = u_end > u0 ? (u_end - u0 + 3) / 4 : 0;
+    const int ntiles = u_end > u0 ? (u_end - u0 + kUnits - 1) / kUnits : 0;
     const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
-    auto tile_nv = [&](int k, int (&nv)[4]) {
+    auto tile_nv = [&](int k, int (&nv)[kUnits]) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int uu = u0 + 4 * k + u;
+      for (int u = 0; u < kUnits; ++u) {
+        const int uu = u0 + kUnits * k + u;
         nv[u] = uu < u_end ? min(kUnit, n - uu * kUnit) : 0;
       }
     };
@@ -1030,253 +842,382 @@ __global__ void __launch_bounds__(kThreads, 1) attn_fp8_kernel(AttnArgs a) {
       const int t0 = u * kUnit;
       int blk = scalar_load_i32(bt_row + (t0 >> a.bs_log2));
       if (blk < 0 || blk >= a.num_blocks) blk = 0;
-      return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kDK;
+      return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowB;
     };
     auto issue_tile = [&](int k) {
-      const int uk = u0 + 4 * k;
-      const uint8_t* r0 = unit_rows(uk);
-      const uint8_t* r1 = uk + 1 < u_end ? unit_rows(uk + 1) : r0;
-      const uint8_t* r2 = uk + 2 < u_end ? unit_rows(uk + 2) : r0;
-      const uint8_t* r3 = uk + 3 < u_end ? unit_rows(uk + 3) : r0;
+      const int uk = u0 + kUnits * k;
+      const uint8_t* r[4];
+      r[0] = unit_rows(uk);
+#pragma unroll
+      for (int u = 1; u < 4; ++u) r[u] = (u < kUnits && uk + u < u_end) ? unit_rows(uk + u) : r[0];
       uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
 #pragma unroll
       for (int i = 0; i < kDmaPerThread; ++i) {
         const uint32_t us = (dma_unit >> (2 * i)) & 3u;
-        const uint8_t* base = (us & 2) ? ((us & 1) ? r3 : r2) : ((us & 1) ? r1 : r0);
+        const uint8_t* base = (us & 2) ? ((us & 1) ? r[3] : r[2]) : ((us & 1) ? r[1] : r[0]);
         __builtin_amdgcn_global_load_lds(
             base + dma_off[i], (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16),
             16, 0, 0);
       }
     };
 
-    // q of head h0 + c (padded heads repeat head H - 1), dimensions
-    // 64 m + 16 g .. + 15: qf[m] = 16 bytes of q_hi, then 16 bytes of q_lo.
-    i32x8_t qf[kKChunksFp8];
-    float xscale;  // logit scale of head c, log2 domain
-    {
-      const int hq = min(h0 + c, H - 1);
-      const u32x4_t* qp =
-          reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + hq) * kDK + 16 * g);
-      u32x4_t raw[kKChunksFp8][2];
+    const bool final_out = pieces == 1;
+    const int row = final_out ? 0 : a.row_ptr[b] + piece;
+    // Both roles pass the same barriers in the same order: per pass one
+    // opening barrier, two per step, two closing ones; then one before the
+    // epilogue's output stores.
+    if (logit_wave) {
+      // q of head h0 + c (padded heads repeat H - 1).
+      u32x4_t qf[kQChunks];                 // bf16: features 32 s + 8 g .. + 7
+      i32x8_t qb_hi[4], qb_lo[4], qb_last;  // E4M3: pairs of 64-dim blocks, hi / lo
+      float xscale = a.scale_log2;
+      {
+        const int hq = min(h0 + c, H - 1);
+        if constexpr (!KV_FP8) {
+          const u32x4_t* qp =
+              reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + hq) * kDK) + g;
 #pragma unroll
-      for (int m = 0; m < kKChunksFp8; ++m) {
-        raw[m][0] = qp[8 * m];
-        raw[m][1] = qp[8 * m + 1];
-      }
-      float amax = 0.f;
-#pragma unroll
-      for (int m = 0; m < kKChunksFp8; ++m)
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int w = 0; w < 4; ++w) {
-            const unsigned x = raw[m][h][w];
-            amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
-                                     fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
-          }
-      amax = fmaxf(amax, __shfl_xor(amax, 16));
-      amax = fmaxf(amax, __shfl_xor(amax, 32));
-      const float inv = amax > 0.f ? 448.f / amax : 0.f;
-      xscale = (amax / 448.f) * a.kv_scale * a.scale_log2;
-#pragma unroll
-      for (int m = 0; m < kKChunksFp8; ++m) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-          for (int w2 = 0; w2 < 2; ++w2) {
-            const unsigned x0 = raw[m][h][2 * w2], x1 = raw[m][h][2 * w2 + 1];
-            const float f0 = __builtin_bit_cast(float, x0 << 16) * inv;
-            const float f1 = __builtin_bit_cast(float, x0 & 0xffff0000u) * inv;
-            const float f2 = __builtin_bit_cast(float, x1 << 16) * inv;
-            const float f3 = __builtin_bit_cast(float, x1 & 0xffff0000u) * inv;
-            const unsigned hi = pack_e4m3x4_inrange(f0, f1, f2, f3);
-            const unsigned lo = pack_e4m3x4_inrange(
-                f0 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 0),
-                f1 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 1),
-                f2 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 2),
-                f3 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 3));
-            qf[m][2 * h + w2] = int(hi);
-            qf[m][4 + 2 * h + w2] = int(lo);
-          }
-        }
-      }
-    }
-
-    f32x4_t acc[32];          // acc[n][r]: head 4 g + r, feature 16 n + c (units 2^-8 / kv_scale)
-    float m_ref = -INFINITY;  // frame of head c (log2 domain)
-    float m_seen = -INFINITY; // largest logit of head c seen in the first pass
-    float l_run = 0.f;        // lane's share of head c's denominator (frame m_ref)
-    bool redo = false;
-
-    for (int pass = 0; pass < 2; ++pass) {
-      const bool work = active && (pass == 0 || redo);
-      if (work) {
-        if (pass == 1) m_ref = m_seen;
-#pragma unroll
-        for (int i = 0; i < 32; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        l_run = 0.f;
-      }
-      redo = false;
-
-      wave_barrier_all();  // the ring of the previous pass or piece is consumed
-      wait_vmem<0>();      // q has landed; only ring loads are in flight from here
-      for (int k = 0; k < kStages - 1 && k < ntiles; ++k) issue_tile(k);
-
-      if (!work) {
-        for (int j = 0; j < ntiles; ++j) {
-          wait_ring<kStages - 2>(ntiles - 1 - j);
-          wave_barrier_all();
-          if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
-        }
-      } else for (int j = 0; j < ntiles; ++j) {
-        wait_ring<kStages - 2>(ntiles - 1 - j);
-        wave_barrier_all();
-        if (j + kStages - 1 < ntiles) issue_tile(j + kStages - 1);
-
-        const uint32_t st = ring_lds + uint32_t(j % kStages) * kTileBytesBf16;
-        int nv[4];
-        tile_nv(j, nv);
-        // Logits of units u = 0..3: lane (c, g) gets tokens 16 u + 4 g + r of head c.
-        float x[4][4];
-        auto logits = [&](auto uc) {
-          constexpr int U = decltype(uc)::value;
-          u32x4_t kf[kKChunksFp8];
-          lds_read_k9<U * kUnit * kDK>(st + ((U & 1) ? k_odd : k_even), kf);
-          f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          for (int s2 = 0; s2 < kQChunks; ++s2) qf[s2] = qp[4 * s2];
+        } else {
+          const u32x4_t* qp =
+              reinterpret_cast<const u32x4_t*>(a.q + (size_t(b) * H + hq) * kDK + 16 * g);
+          u32x4_t raw[kKChunksFp8][2];
 #pragma unroll
           for (int m = 0; m < kKChunksFp8; ++m) {
-            const i32x8_t ka = i32x8_t{int(kf[m][0]), int(kf[m][1]), int(kf[m][2]), int(kf[m][3]),
-                                       int(kf[m][0]), int(kf[m][1]), int(kf[m][2]), int(kf[m][3])};
-            sc = mfma_e4m3_128(ka, qf[m], sc, 127);
+            raw[m][0] = qp[8 * m];
+            raw[m][1] = qp[8 * m + 1];
           }
+          float amax = 0.f;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            x[U][r] = (4 * g + r < nv[U]) ? sc[r] * xscale : -INFINITY;
-        };
-        logits(std::integral_constant<int, 0>{});
-        logits(std::integral_constant<int, 1>{});
-        logits(std::integral_constant<int, 2>{});
-        logits(std::integral_constant<int, 3>{});
-
-        float mt = -INFINITY;
+          for (int m = 0; m < kKChunksFp8; ++m)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          mt = fmaxf(mt, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
-        mt = fmaxf(mt, __shfl_xor(mt, 16));
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        m_seen = fmaxf(m_seen, mt);
-        if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): set the frame
-        if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
-        // Exponent carried by the op's A scale: 0 <= e <= 64.
-        const float rise = mt - m_ref;
-        const int e = rise > 0.f ? min(int(ceilf(rise)), int(kHeadsSlack)) : 0;
-        const float fe = m_ref + float(e);
-        unsigned ph[4], pl[4];
-        float lt = 0.f;
+            for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          float ps[4];
+              for (int w = 0; w < 4; ++w) {
+                const unsigned x = raw[m][h][w];
+                amax = fmaxf(amax, fmaxf(fabsf(__builtin_bit_cast(float, x << 16)),
+                                         fabsf(__builtin_bit_cast(float, x & 0xffff0000u))));
+              }
+          amax = fmaxf(amax, __shfl_xor(amax, 16));
+          amax = fmaxf(amax, __shfl_xor(amax, 32));
+          const float inv = amax > 0.f ? 448.f / amax : 0.f;
+          xscale = (amax / 448.f) * a.kv_scale * a.scale_log2;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = fast_exp2(x[u][r] - fe);
-            lt += p;
-            ps[r] = p * 256.f;
+          for (int m = 0; m < kKChunksFp8; ++m) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+#pragma unroll
+              for (int w2 = 0; w2 < 2; ++w2) {
+                const unsigned x0 = raw[m][h][2 * w2], x1 = raw[m][h][2 * w2 + 1];
+                const float f0 = __builtin_bit_cast(float, x0 << 16) * inv;
+                const float f1 = __builtin_bit_cast(float, x0 & 0xffff0000u) * inv;
+                const float f2 = __builtin_bit_cast(float, x1 << 16) * inv;
+                const float f3 = __builtin_bit_cast(float, x1 & 0xffff0000u) * inv;
+                const unsigned hi = pack_e4m3x4_inrange(f0, f1, f2, f3);
+                const unsigned lo = pack_e4m3x4_inrange(
+                    f0 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 0),
+                    f1 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 1),
+                    f2 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 2),
+                    f3 - __builtin_amdgcn_cvt_f32_fp8(int(hi), 3));
+                const int w = 2 * h + w2;
+                if (m < 8) {
+                  qb_hi[m >> 1][4 * (m & 1) + w] = int(hi);
+                  qb_lo[m >> 1][4 * (m & 1) + w] = int(lo);
+                } else {
+                  qb_last[w] = int(hi);
+                  qb_last[4 + w] = int(lo);
+                }
+              }
+            }
           }
-          ph[u] = pack_e4m3x4_inrange(ps[0], ps[1], ps[2], ps[3]);
-          pl[u] = pack_e4m3x4_inrange(ps[0] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 0),
-                                      ps[1] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 1),
-                                      ps[2] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 2),
-                                      ps[3] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 3));
         }
-        l_run += __builtin_amdgcn_ldexpf(lt, e);
-        const i32x8_t pa = i32x8_t{int(ph[0]), int(ph[1]), int(ph[2]), int(ph[3]),
-                                   int(pl[0]), int(pl[1]), int(pl[2]), int(pl[3])};
-        const int sa = 127 + e;
+      }
+      float m_ref = -INFINITY;   // frame of head c (log2 domain)
+      float m_seen = -INFINITY;  // largest logit of head c (first pass)
+      float l_run = 0.f;         // lane's share of head c's denominator
+      bool redo = false;         // frame exceeded in the first pass
 
-        // Tokens past the end of a partial unit: zero their V bytes (their
-        // weight is zero, but unused rows may hold NaN codes).
-        const bool vmask = (nv[0] < kUnit) | (nv[1] < kUnit) | (nv[2] < kUnit) | (nv[3] < kUnit);
-        uint64_t vkeep[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          uint64_t k2 = 0;
-#pragma unroll
-          for (int q2 = 0; q2 < 2; ++q2) {
-            const int kc = min(max(nv[2 * h + q2] - 4 * g, 0), 4);
-            const uint64_t m4 = kc >= 4 ? 0xffffffffull : ((1ull << (8 * kc)) - 1ull);
-            k2 |= m4 << (32 * q2);
-          }
-          vkeep[h] = k2;
+      for (int pass = 0; pass < 2; ++pass) {
+        // First pass: every active tile; second: only those that asked.
+        const bool work = lw_active && (pass == 0 || redo);
+        if (pass == 1 && work) {
+          m_ref = m_seen;
+          l_run = 0.f;
         }
-        uint32_t vb[4];
+        redo = false;
+        wave_barrier_all();  // ring and P buffer of the previous pass or piece are free
+        wait_vmem<0>();      // q
+        for (int s = 0; s <= ntiles; ++s) {
+          wave_barrier_lds();  // barrier 1: tile s is in the ring
+          wave_barrier_lds();  // barrier 2: the P.V waves hold P of tile s - 1
+          if (s == ntiles) continue;
+          u32x4_t pw[kPWords];
+          int e_scale = 127;
+          if (work) {
+            const uint32_t st = ring_lds + uint32_t(s % kStages) * kTileBytesBf16;
+            int nv[kUnits];
+            tile_nv(s, nv);
+            float x[kUnits][4];
+            if constexpr (!KV_FP8) {
 #pragma unroll
-        for (int n2 = 0; n2 < 4; ++n2) vb[n2] = st + v_off[n2];
-        auto pv_group = [&](auto mc) {
-          constexpr int M = decltype(mc)::value;
-          u32x2_t t[4][2];
-          lds_read_trb8<64 * M>(vb, t);
-          if (vmask) {
+              for (int h = 0; h < 2; ++h) {
+                const uint32_t rowa = st + uint32_t(h * kUnit * kRowB);
+                u32x4_t kf[kQChunks];
+                lds_read_k(rowa + k_off0, rowa + k_off1, kf);
+                f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int n2 = 0; n2 < 4; ++n2)
+                for (int s2 = 0; s2 < kQChunks; ++s2)
+                  sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(bf16x8_t, kf[s2]), __builtin_bit_cast(bf16x8_t, qf[s2]),
+                      sc, 0, 0, 0);
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  x[h][r] = (4 * g + r < nv[h]) ? sc[r] * xscale : -INFINITY;
+              }
+            } else {
+              auto logits = [&](auto uc) {
+                constexpr int U = decltype(uc)::value;
+                u32x4_t kf[kKChunksFp8];
+                lds_read_k9<U * kUnit * kDK>(st + ((U & 1) ? k_off1 : k_off0), kf);
+                f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int p2 = 0; p2 < 4; ++p2) {
+                  const i32x8_t ka = __builtin_bit_cast(
+                      i32x8_t,
+                      __builtin_shufflevector(kf[2 * p2], kf[2 * p2 + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+                  sc = mfma_e4m3_128(ka, qb_hi[p2], sc, 127);
+                  sc = mfma_e4m3_128(ka, qb_lo[p2], sc, 127);
+                }
+                {
+                  const i32x8_t ka = __builtin_bit_cast(
+                      i32x8_t, __builtin_shufflevector(kf[8], kf[8], 0, 1, 2, 3, 4, 5, 6, 7));
+                  sc = mfma_e4m3_128(ka, qb_last, sc, 127);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                  x[U][r] = (4 * g + r < nv[U]) ? sc[r] * xscale : -INFINITY;
+              };
+              logits(std::integral_constant<int, 0>{});
+              logits(std::integral_constant<int, 1>{});
+              logits(std::integral_constant<int, 2>{});
+              logits(std::integral_constant<int, 3>{});
+            }
+            float mt = -INFINITY;
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u)
+              mt = fmaxf(mt, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
+            mt = fmaxf(mt, __shfl_xor(mt, 16));
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            m_seen = fmaxf(m_seen, mt);
+            if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): the frame
+            if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
+            if constexpr (!KV_FP8) {
+              float p[2][4];
 #pragma unroll
               for (int h = 0; h < 2; ++h)
-                t[n2][h] = __builtin_bit_cast(
-                    u32x2_t, __builtin_bit_cast(uint64_t, t[n2][h]) & vkeep[h]);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_ref);
+              l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
+                       ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
+              bf16x8_t pa;
+#pragma unroll
+              for (int r = 0; r < 4; ++r) {
+                pa[r] = (__bf16)p[0][r];
+                pa[4 + r] = (__bf16)p[1][r];
+              }
+              pw[0] = __builtin_bit_cast(u32x4_t, pa);
+            } else {
+              const float rise = mt - m_ref;
+              const int e = rise > 0.f ? min(int(ceilf(rise)), int(kHeadsSlack)) : 0;
+              const float fe = m_ref + float(e);
+              unsigned ph[4], pl[4];
+              float lt = 0.f;
+#pragma unroll
+              for (int u = 0; u < 4; ++u) {
+                float ps[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                  const float pp = fast_exp2(x[u][r] - fe);
+                  lt += pp;
+                  ps[r] = pp * 256.f;
+                }
+                ph[u] = pack_e4m3x4_inrange(ps[0], ps[1], ps[2], ps[3]);
+                pl[u] = pack_e4m3x4_inrange(ps[0] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 0),
+                                            ps[1] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 1),
+                                            ps[2] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 2),
+                                            ps[3] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 3));
+              }
+              l_run += __builtin_amdgcn_ldexpf(lt, e);
+              pw[0] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
+              pw[kPWords - 1] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
+              e_scale = 127 + e;
+            }
+          } else {
+#pragma unroll
+            for (int w = 0; w < kPWords; ++w) pw[w] = u32x4_t{0u, 0u, 0u, 0u};
           }
 #pragma unroll
-          for (int n2 = 0; n2 < 4; ++n2) {
-            const i32x8_t bv = i32x8_t{int(t[n2][0][0]), int(t[n2][0][1]), int(t[n2][1][0]),
-                                       int(t[n2][1][1]), int(t[n2][0][0]), int(t[n2][0][1]),
-                                       int(t[n2][1][0]), int(t[n2][1][1])};
-            acc[4 * M + n2] = mfma_e4m3_128(pa, bv, acc[4 * M + n2], sa);
-          }
-        };
-        pv_group(std::integral_constant<int, 0>{});
-        pv_group(std::integral_constant<int, 1>{});
-        pv_group(std::integral_constant<int, 2>{});
-        pv_group(std::integral_constant<int, 3>{});
-        pv_group(std::integral_constant<int, 4>{});
-        pv_group(std::integral_constant<int, 5>{});
-        pv_group(std::integral_constant<int, 6>{});
-        pv_group(std::integral_constant<int, 7>{});
+          for (int w = 0; w < kPWords; ++w) pbuf[wq][lane][w] = pw[w];
+          if (KV_FP8 && g == 0) ebuf[wq][c] = e_scale;
+        }
+        wave_barrier_lds();  // closing barrier 1: redo_any cleared
+        if (lane == 0) {
+          redo_tile[wq] = (work && redo) ? 1 : 0;
+          if (work && redo) redo_any = 1;
+        }
+        wave_barrier_lds();  // closing barrier 2: redo flags complete
+        if (redo_any == 0) break;
       }
-      if (tid == 0) redo_any = 0;
-      wave_barrier_lds();
-      if (work && redo && lane == 0) redo_any = 1;
-      wave_barrier_lds();
-      if (redo_any == 0) break;
-    }
-
-    if (active) {
       float l_c = l_run + __shfl_xor(l_run, 16);
       l_c += __shfl_xor(l_c, 32);
-      const bool final_out = pieces == 1;
-      const int row = final_out ? 0 : a.row_ptr[b] + piece;
-      const float out_scale = a.kv_scale * (1.f / 256.f);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int hh = 4 * g + r;
-        const int h = h0 + hh;
-        const float lh = __shfl(l_c, hh);
-        const float inv = lh > 0.f ? out_scale / lh : 0.f;
-        if (h < H) {
+      if (g == 0) {
+        lbuf[wq][c] = l_c;
+        if (lw_active && h0 + c < H) {
+          const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
           if (final_out) {
-            uint16_t* dst = a.out + (size_t(b) * H + h) * kDV + c;
-#pragma unroll
-            for (int n2 = 0; n2 < 32; ++n2) dst[16 * n2] = bf16_bits(acc[n2][r] * inv);
+            if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
           } else {
-            float* dst = a.part_out + (size_t(row) * H + h) * kDV + c;
-#pragma unroll
-            for (int n2 = 0; n2 < 32; ++n2) dst[16 * n2] = acc[n2][r] * inv;
+            a.part_lse[size_t(row) * H + h0 + c] = lse_v;
           }
         }
       }
-      if (g == 0 && h0 + c < H) {
-        const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
-        if (final_out) {
-          if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
-        } else {
-          a.part_lse[size_t(row) * H + h0 + c] = lse_v;
+      wave_barrier_lds();  // lbuf complete
+    } else {
+      // acc[t][j]: head 16 t + 4 g + r of the group, feature 128 wq + 16 j + c.
+      f32x4_t acc[4][8];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[t][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int pass = 0; pass < 2; ++pass) {
+        if (pass == 1) {
+          // Clear the accumulators of recomputed head tiles (by selection:
+          // their first-pass sums may hold non-finite values).
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const bool clear = redo_tile[t] != 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+              for (int r = 0; r < 4; ++r) acc[t][j][r] = clear ? 0.f : acc[t][j][r];
+          }
+        }
+        wave_barrier_all();  // ring and P buffer of the previous pass or piece are free
+        for (int k = 0; k < 2 && k < ntiles; ++k) issue_tile(k);
+        for (int s = 0; s <= ntiles; ++s) {
+          if (s < ntiles) wait_ring<1>(ntiles - 1 - s);  // tile s landed
+          wave_barrier_lds();  // barrier 1: P of tile s - 1 is in pbuf
+          u32x4_t pv_p[4];   // bf16 A operands
+          i32x8_t pv_pa[4];  // E4M3 A operands
+          int pv_e[4];
+          if (s >= 1) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              if constexpr (KV_FP8) {
+                pv_pa[t] = *reinterpret_cast<const i32x8_t*>(&pbuf[t][lane][0]);
+                pv_e[t] = ebuf[t][c];
+              } else {
+                pv_p[t] = pbuf[t][lane][0];
+              }
+            }
+          }
+          wave_barrier_lds();  // barrier 2: P taken, pbuf may be overwritten
+          if (s + 2 < ntiles) issue_tile(s + 2);
+          if (s == 0) continue;
+          const int k = s - 1;
+          const uint32_t st = ring_lds + uint32_t(k % kStages) * kTileBytesBf16;
+          int nv[kUnits];
+          tile_nv(k, nv);
+          bool vmask = false;
+#pragma unroll
+          for (int u = 0; u < kUnits; ++u) vmask |= nv[u] < kUnit;
+          // Per read half h: which of the lane's 8-byte elements are tokens.
+          uint64_t vkeep[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            if constexpr (KV_FP8) {
+              uint64_t k2 = 0;
+#pragma unroll
+              for (int q2 = 0; q2 < 2; ++q2) {
+                const int kc = min(max(nv[2 * h + q2] - 4 * g, 0), 4);
+                const uint64_t m4 = kc >= 4 ? 0xffffffffull : ((1ull << (8 * kc)) - 1ull);
+                k2 |= m4 << (32 * q2);
+              }
+              vkeep[h] = k2;
+            } else {
+              const int kc = min(max(nv[h] - 4 * g, 0), 4);
+              vkeep[h] = kc >= 4 ? ~0ull : ((1ull << (16 * kc)) - 1ull);
+            }
+          }
+          uint32_t vb[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) vb[j] = st + v_off[j];
+          auto pv_group = [&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            u32x2_t tv[4][2];
+            if constexpr (KV_FP8)
+              lds_read_trb8<64 * M>(vb, tv);
+            else
+              lds_read_tr8<M>(vb, tv);
+            if (vmask) {
+#pragma unroll
+              for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                  tv[j][h] = __builtin_bit_cast(
+                      u32x2_t, __builtin_bit_cast(uint64_t, tv[j][h]) & vkeep[h]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if constexpr (KV_FP8) {
+                // One doubled V operand at a time keeps the copies' registers
+                // short-lived.
+                __builtin_amdgcn_sched_barrier(0);
+                const i32x8_t bv = i32x8_t{int(tv[j][0][0]), int(tv[j][0][1]), int(tv[j][1][0]),
+                                           int(tv[j][1][1]), int(tv[j][0][0]), int(tv[j][0][1]),
+                                           int(tv[j][1][0]), int(tv[j][1][1])};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  acc[t][4 * M + j] = mfma_e4m3_128(pv_pa[t], bv, acc[t][4 * M + j], pv_e[t]);
+              } else {
+                const u32x4_t bv = u32x4_t{tv[j][0][0], tv[j][0][1], tv[j][1][0], tv[j][1][1]};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  acc[t][4 * M + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                      __builtin_bit_cast(bf16x8_t, pv_p[t]), __builtin_bit_cast(bf16x8_t, bv),
+                      acc[t][4 * M + j], 0, 0, 0);
+              }
+            }
+          };
+          pv_group(std::integral_constant<int, 0>{});
+          pv_group(std::integral_constant<int, 1>{});
+        }
+        if (tid == 0) redo_any = 0;
+        wave_barrier_lds();  // closing barrier 1
+        wave_barrier_lds();  // closing barrier 2: redo flags complete
+        if (redo_any == 0) break;
+      }
+      wave_barrier_lds();  // lbuf complete
+      const float out_scale = KV_FP8 ? a.kv_scale * (1.f / 256.f) : 1.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int hh = 4 * g + r;
+          const int h = (ht0 + t) * kHeadTile + hh;
+          const float lh = lbuf[t][hh];
+          const float inv = lh > 0.f ? out_scale / lh : 0.f;
+          if (h < H) {
+            if (final_out) {
+              uint16_t* dst = a.out + (size_t(b) * H + h) * kDV + 128 * wq + c;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) dst[16 * j] = bf16_bits(acc[t][j][r] * inv);
+            } else {
+              float* dst = a.part_out + (size_t(row) * H + h) * kDV + 128 * wq + c;
+#pragma unroll
+              for (int j = 0; j < 8; ++j) dst[16 * j] = acc[t][j][r] * inv;
+            }
+          }
         }
       }
     }
@@ -1350,14 +1291,13 @@ hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_token
 hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_launched,
                             hipStream_t stream) {
   dim3 grid(unsigned(parts_launched) * unsigned(args.head_tiles));
+  const dim3 grid_mh(unsigned(parts_launched) * unsigned(args.head_groups));
   if (kv_fp8)
-    hipLaunchKernelGGL(attn_fp8_kernel, dim3(unsigned(parts_launched) * unsigned(args.head_groups)),
-                       dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL(attn_mh_kernel<1>, grid_mh, dim3(kMhThreads), 0, stream, args);
   else if (args.head_tiles == 1)
     hipLaunchKernelGGL(attn_ws_kernel, grid, dim3(kWsThreads), 0, stream, args);
   else
-    hipLaunchKernelGGL(attn_heads_kernel, dim3(unsigned(parts_launched) * unsigned(args.head_groups)),
-                       dim3(kThreads), 0, stream, args);
+    hipLaunchKernelGGL(attn_mh_kernel<0>, grid_mh, dim3(kMhThreads), 0, stream, args);
   return hipGetLastError();
 }
 
