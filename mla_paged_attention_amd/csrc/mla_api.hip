@@ -29,17 +29,19 @@ int bs_log2_of(int32_t bs) {
   }
 }
 
-// Partial rows the automatic plan may need with at most `parts` partitions:
-// every cut inside a request adds one piece, and a split request of p pieces
-// holds p rows, so at most 2 * (parts - 1) rows; never more than
-// batch * min(parts, units of the longest request).
+// Partial rows the automatic plan may need with at most `parts` partitions.
+// Contiguous plan: every cut inside a request adds one piece, and a split
+// request of p pieces holds p rows, so at most 2 * (parts - 1) rows. Snake
+// plan: only requests costing more than the per-partition target P are cut,
+// into ceil(cost / P) <= 2 cost / P pieces, so at most 2 * parts rows.
+// Never more than batch * min(parts, units of the longest request).
 int64_t auto_rows(int64_t batch, int64_t parts, int64_t max_seq_len) {
   if (parts <= 1 || batch <= 0) return 0;
   int64_t units = (max_seq_len + mla::kUnit - 1) / mla::kUnit;
   if (units < 1) units = 1;
   int64_t per_req = parts < units ? parts : units;
   if (per_req <= 1) return 0;
-  int64_t a = 2 * (parts - 1), b = batch * per_req;
+  int64_t a = 2 * parts, b = batch * per_req;
   return a < b ? a : b;
 }
 
@@ -112,11 +114,11 @@ mla_status_t validate_decode(const DecodeArgs& a) {
     return MLA_ERR_INVALID_ARG;
   if (a.lse && !aligned(a.lse, 4)) return MLA_ERR_INVALID_ARG;
   // Metadata alone must fit whatever the mode.
-  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.num_heads, 0).total)
+  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.num_heads, 0, 1).total)
     return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (a.num_splits > 0) {
     WorkspaceLayout w =
-        mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits));
+        mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits), 1);
     if (a.workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
   return MLA_OK;
@@ -137,21 +139,24 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   WorkspaceLayout w;
   int64_t max_parts = 0;
   if (a.num_splits > 0) {
-    w = mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits));
+    w = mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits), 1);
   } else {
-    // Largest partition count whose partial rows fit the given workspace.
+    // Largest partition count whose plan and partial rows fit the workspace.
     max_parts = mla::max_partitions(dev.cus, a.num_heads, a.kv_dtype == MLA_KV_FP8_E4M3);
-    while (max_parts > 1 &&
-           mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, max_parts, cap)).total >
-               a.workspace_bytes)
+    auto layout = [&](int64_t parts) {
+      return mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, parts, cap), parts);
+    };
+    while (max_parts > 1 && layout(max_parts).total > a.workspace_bytes)
       max_parts = max_parts * 3 / 4;
-    w = mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, max_parts, cap));
+    w = layout(max_parts);
     if (w.total > a.workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   int32_t* header = reinterpret_cast<int32_t*>(ws + w.header);
-  int32_t* cum = reinterpret_cast<int32_t*>(ws + w.cum);
   int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + w.row_ptr);
+  int32_t* part_ptr = reinterpret_cast<int32_t*>(ws + w.part_ptr);
+  int4* work = reinterpret_cast<int4*>(ws + w.work);
+  int32_t* split = reinterpret_cast<int32_t*>(ws + w.split);
   float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
   float* part_out = reinterpret_cast<float*>(ws + w.part_out);
 
@@ -161,8 +166,8 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   };
 
   if (!rec(0)) return MLA_ERR_HIP;
-  if (mla::launch_plan(a.seq_lens, a.batch, int32_t(cap), a.num_splits, int32_t(max_parts),
-                       header, cum, row_ptr, s) != hipSuccess)
+  if (mla::launch_plan(a.seq_lens, a.batch, int32_t(cap), a.num_splits, int32_t(max_parts), w,
+                       a.workspace, s) != hipSuccess)
     return MLA_ERR_HIP;
   if (!rec(1)) return MLA_ERR_HIP;
 
@@ -176,7 +181,8 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.part_out = part_out;
   args.part_lse = part_lse;
   args.header = header;
-  args.cum = cum;
+  args.part_ptr = part_ptr;
+  args.work = work;
   args.row_ptr = row_ptr;
   args.scale_log2 = a.scale * 1.4426950408889634f;
   args.kv_scale = a.kv_scale;
@@ -187,6 +193,9 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.bs_log2 = bs_log2_of(a.block_size);
   args.cap_tokens = int32_t(cap);
   args.num_splits = a.num_splits;
+  args.parts_cap = int32_t(max_parts);
+  args.items_cap = int32_t(a.batch + max_parts);
+  args.rows_cap = int32_t(w.rows);
   args.head_tiles = mla::head_tiles(a.num_heads);
   args.head_groups = (args.head_tiles + 3) / 4;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
@@ -197,10 +206,17 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   if (e != hipSuccess) return MLA_ERR_HIP;
   if (!rec(2)) return MLA_ERR_HIP;
 
-  const bool need_combine = a.num_splits > 1 || (a.num_splits == 0 && max_parts > 1);
-  if (need_combine) {
+  if (a.num_splits > 1) {
     if (mla::launch_combine(part_out, part_lse, row_ptr, static_cast<uint16_t*>(a.out), a.lse,
                             a.batch, a.num_heads, 0, s) != hipSuccess)
+      return MLA_ERR_HIP;
+  } else if (a.num_splits == 0 && max_parts > 1 && w.rows > 0) {
+    // Split requests are fewer than the partitions (each is costlier than
+    // a partition's share, or straddles one of the parts - 1 cuts).
+    const int64_t max_split = a.batch < max_parts ? a.batch : max_parts;
+    if (mla::launch_combine_split(part_out, part_lse, row_ptr, split, header,
+                                  static_cast<uint16_t*>(a.out), a.lse, int32_t(max_split),
+                                  a.num_heads, s) != hipSuccess)
       return MLA_ERR_HIP;
   }
   if (!rec(3)) return MLA_ERR_HIP;
@@ -218,10 +234,11 @@ size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_
   if (max_seq_len < 0 || max_seq_len > INT32_MAX / 2) return 0;
   if (num_splits < 0 || num_splits > MLA_MAX_FORCED_SPLITS) return 0;
   if (num_cus <= 0) num_cus = kDefaultCus;
-  int64_t rows = num_splits > 0
-                     ? forced_rows(batch, num_splits)
-                     : auto_rows(batch, mla::max_partitions(num_cus, num_heads, 0), max_seq_len);
-  return mla::workspace_layout(batch, num_heads, rows).total;
+  if (num_splits > 0)
+    return mla::workspace_layout(batch, num_heads, forced_rows(batch, num_splits), 1).total;
+  const int64_t parts = mla::max_partitions(num_cus, num_heads, 0);
+  return mla::workspace_layout(batch, num_heads, auto_rows(batch, parts, max_seq_len), parts)
+      .total;
 }
 
 mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,

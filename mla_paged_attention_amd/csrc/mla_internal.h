@@ -17,22 +17,32 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kOverheadUnits = 1;   // per-request fixed cost in the balanced plan
 constexpr int kMinPartUnits = 4;    // smallest partition: one unit per wave
 constexpr int kPlanThreads = 1024;
+constexpr int kMaxPlanParts = 2048;  // partitions of the automatic plan (work list bound)
 
-// Workspace layout. Offsets are 256-byte aligned.
+// Workspace layout. Offsets are 256-byte aligned. `parts` bounds the
+// partitions of the automatic plan (1 in forced-split mode, which needs no
+// work list).
 struct WorkspaceLayout {
-  size_t header;    // int32[64]: [0] partitions used, [1] cost units per partition
+  size_t header;    // int32[64]: [0] partitions, [1] cost units per partition,
+                    // [2] split requests, [3] plan mode
   size_t cum;       // int32[batch + 1]: exclusive prefix of per-request costs
   size_t row_ptr;   // int32[batch + 1]: first partial row of each request
+  size_t part_ptr;  // int32[parts + 1]: first work item of each partition
+  size_t work;      // int32x4[batch + parts]: (request, unit begin, unit end, row or -1)
+  size_t split;     // int32[parts]: requests with partial rows
   size_t part_lse;  // float[rows][num_heads]
   size_t part_out;  // float[rows][num_heads][512]
   size_t total;
   int64_t rows;
+  int64_t parts;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_t rows) {
+inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_t rows,
+                                        int64_t parts) {
   WorkspaceLayout w;
+  if (parts < 1) parts = 1;
   size_t off = 0;
   w.header = off;
   off += 256;
@@ -40,12 +50,19 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
   off += align256(size_t(batch + 1) * 4);
   w.row_ptr = off;
   off += align256(size_t(batch + 1) * 4);
+  w.part_ptr = off;
+  off += align256(size_t(parts + 1) * 4);
+  w.work = off;
+  off += align256(size_t(batch + parts) * 16);
+  w.split = off;
+  off += align256(size_t(parts) * 4);
   w.part_lse = off;
   off += align256(size_t(rows) * size_t(num_heads) * 4);
   w.part_out = off;
   off += align256(size_t(rows) * size_t(num_heads) * kDV * 4);
   w.total = off;
   w.rows = rows;
+  w.parts = parts;
   return w;
 }
 
@@ -62,6 +79,7 @@ inline int workgroups_per_partition(int num_heads, int kv_fp8) {
 // attention workgroup per CU at a time.
 inline int64_t max_partitions(int64_t num_cus, int64_t num_heads, int kv_fp8) {
   int64_t g = num_cus / workgroups_per_partition(int(num_heads), kv_fp8);
+  if (g > kMaxPlanParts) g = kMaxPlanParts;
   return g < 8 ? 8 : g;
 }
 
@@ -75,7 +93,8 @@ struct AttnArgs {
   float* part_out;
   float* part_lse;
   const int32_t* header;
-  const int32_t* cum;
+  const int32_t* part_ptr;   // automatic plan: work items of each partition
+  const int4* work;
   const int32_t* row_ptr;
   float scale_log2;          // logit scale * log2(e)
   float kv_scale;            // fp8 dequantisation scale (1 for bf16)
@@ -85,14 +104,19 @@ struct AttnArgs {
   int32_t num_blocks;
   int32_t bs_log2;
   int32_t cap_tokens;        // max_blocks * block_size
-  int32_t num_splits;        // 0 = balanced plan
+  int32_t num_splits;        // 0 = automatic plan
+  int32_t parts_cap;         // automatic plan: partitions in part_ptr
+  int32_t items_cap;         // automatic plan: entries of work
+  int32_t rows_cap;          // partial rows in part_out / part_lse
   int32_t head_tiles;        // ceil(num_heads / 16)
   int32_t head_groups;       // workgroups per partition of the many-head kernel
 };
 
+// Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
+// only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
-                       int32_t num_splits, int32_t max_parts, int32_t* header, int32_t* cum,
-                       int32_t* row_ptr, hipStream_t stream);
+                       int32_t num_splits, int32_t max_parts, const WorkspaceLayout& w,
+                       void* workspace, hipStream_t stream);
 
 // kv_fp8: 0 = bf16 cache, 1 = E4M3 cache. `parts_launched` is a multiple of 8.
 hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_launched,
@@ -101,5 +125,12 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
 hipError_t launch_combine(const float* part_out, const float* part_lse,
                           const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
                           int32_t num_heads, int zero_empty, hipStream_t stream);
+
+// Combine of the automatic plan: only the requests listed in `split`
+// (header[2] of them, at most `max_split`).
+hipError_t launch_combine_split(const float* part_out, const float* part_lse,
+                                const int32_t* row_ptr, const int32_t* split,
+                                const int32_t* header, uint16_t* out, float* lse,
+                                int32_t max_split, int32_t num_heads, hipStream_t stream);
 
 }  // namespace mla

@@ -100,120 +100,265 @@ __device__ __forceinline__ int units_of(int n) {
   return u < 1 ? 1 : u;  // an empty request still owns one (empty) unit
 }
 
-__global__ void __launch_bounds__(kPlanThreads) plan_kernel(const int32_t* seq_lens, int32_t batch,
-                                                            int32_t cap_tokens, int32_t num_splits,
-                                                            int32_t max_parts, int32_t* header,
-                                                            int32_t* cum, int32_t* row_ptr) {
+// Automatic plan modes (header[3]).
+constexpr int kPlanContiguous = 0;
+constexpr int kPlanSnake = 1;
+constexpr int kSnakeMaxBatch = 4096;   // largest batch the snake plan sorts
+constexpr int kCostBuckets = 4096;     // counting-sort buckets of piece costs
+
+__device__ __forceinline__ int block_max(int v, int* s_wave) {
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d));
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) s_wave[wave] = v;
+  __syncthreads();
+  int r = s_wave[0];
+  for (int i = 1; i < kPlanThreads / 64; ++i) r = max(r, s_wave[i]);
+  __syncthreads();
+  return r;
+}
+
+// Exclusive scan of s[0..n) in place (n <= kPlanThreads * 4), returns the total.
+__device__ int block_scan_lds(int* s, int n, int* s_wave) {
+  const int tid = threadIdx.x;
+  int v[4], sum = 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * tid + k;
+    v[k] = i < n ? s[i] : 0;
+    sum += v[k];
+  }
+  int tot;
+  int ex = block_exclusive_scan(sum, s_wave, &tot);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int i = 4 * tid + k;
+    if (i < n) s[i] = ex;
+    ex += v[k];
+  }
+  __syncthreads();
+  return tot;
+}
+
+// One workgroup. Forced mode (num_splits > 0): request b's partial rows
+// start at b * num_splits. Automatic mode: a list of work items
+// (request, unit begin, unit end, partial row or -1 when the item is the
+// whole request) per partition, at most max_parts partitions, with costs
+// balanced in units of 16 tokens plus a fixed per-request overhead:
+//  - snake (batch >= 2 * max_parts, batch <= kSnakeMaxBatch): requests above
+//    the per-partition target are cut into near-equal pieces, all pieces are
+//    ranked by cost (counting sort, largest first) and dealt to partitions
+//    in alternating direction, so large batches need no partial rows;
+//  - contiguous otherwise: the requests' costs laid end to end and cut into
+//    equal partitions; a request straddling a cut becomes several pieces.
+__global__ void __launch_bounds__(kPlanThreads) plan_kernel(
+    const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t num_splits,
+    int32_t max_parts, int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr,
+    int4* work, int32_t* split) {
   __shared__ int s_wave[40];
+  __shared__ int s_cnt[kMaxPlanParts + 1];
+  __shared__ int s_bucket[kCostBuckets];
+  __shared__ int s_pb[kSnakeMaxBatch + 1];
+  __shared__ short s_pq[kSnakeMaxBatch + kMaxPlanParts];
   const int tid = threadIdx.x;
   if (num_splits > 0) {
     for (int b = tid; b <= batch; b += kPlanThreads) row_ptr[b] = num_splits > 1 ? b * num_splits : 0;
     if (tid == 0) {
       header[0] = batch * num_splits;
       header[1] = 0;
+      header[2] = 0;
+      header[3] = -1;
     }
     return;
   }
-  // Pass 1: exclusive prefix of cost = overhead + units.
-  int carry = 0;
+  auto cost_of = [&](int b) {
+    return kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens));
+  };
+  // Costs: prefix (cum), total and largest.
+  int carry = 0, cmax = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
-    int b = base + tid;
-    int cost = b < batch ? kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens)) : 0;
+    const int b = base + tid;
+    const int cost = b < batch ? cost_of(b) : 0;
+    cmax = max(cmax, cost);
     int tot;
-    int ex = block_exclusive_scan(cost, s_wave, &tot);
+    const int ex = block_exclusive_scan(cost, s_wave, &tot);
     if (b < batch) cum[b] = carry + ex;
     carry += tot;
   }
   const int total = carry;
-  if (tid == 0) cum[batch] = total;
-  int part = (total + max_parts - 1) / max_parts;
-  if (part < kMinPartUnits) part = kMinPartUnits;
-  const int parts = (total + part - 1) / part;
-  // Pass 2: pieces per request and partial rows (requests with one piece need none).
-  carry = 0;
-  int rcarry = 0;
-  for (int base = 0; base < batch; base += kPlanThreads) {
-    int b = base + tid;
-    int cost = b < batch ? kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens)) : 0;
-    int tot;
-    int ex = block_exclusive_scan(cost, s_wave, &tot);
-    int rows = 0;
-    if (b < batch) {
-      int c0 = carry + ex;
-      int first = (c0 + kOverheadUnits) / part;
-      int last = (c0 + cost - 1) / part;
-      int pieces = last - first + 1;
-      rows = pieces > 1 ? pieces : 0;
+  cmax = block_max(cmax, s_wave);
+  int P = (total + max_parts - 1) / max_parts;
+  if (P < kMinPartUnits) P = kMinPartUnits;
+  const bool snake = batch >= 2 * max_parts && batch <= kSnakeMaxBatch;
+  for (int q = tid; q <= max_parts; q += kPlanThreads) s_cnt[q] = 0;
+  __syncthreads();
+
+  int parts, nitems = 0;
+  int rcarry = 0, scarry = 0;
+  if (!snake) {
+    parts = (total + P - 1) / P;
+    int icarry = 0;
+    for (int base = 0; base < batch; base += kPlanThreads) {
+      const int b = base + tid;
+      int k = 0, c0 = 0, cost = 0;
+      if (b < batch) {
+        cost = cost_of(b);
+        c0 = cum[b];
+        k = (c0 + cost - 1) / P - (c0 + kOverheadUnits) / P + 1;
+      }
+      int tot;
+      const int iex = block_exclusive_scan(k, s_wave, &tot);
+      const int ibase = icarry + iex;
+      icarry += tot;
+      const int rex = block_exclusive_scan(k > 1 ? k : 0, s_wave, &tot);
+      const int rbase = rcarry + rex;
+      rcarry += tot;
+      const int sex = block_exclusive_scan(k > 1 ? 1 : 0, s_wave, &tot);
+      if (b < batch) {
+        row_ptr[b] = rbase;
+        if (k > 1) split[scarry + sex] = b;
+        const int ub = c0 + kOverheadUnits, ue = c0 + cost;
+        const int first = ub / P;
+        for (int j = 0; j < k; ++j) {
+          const int q = first + j;
+          const int p0 = max(ub, q * P), p1 = min(ue, (q + 1) * P);
+          work[ibase + j] = make_int4(b, p0 - ub, p1 - ub, k > 1 ? rbase + j : -1);
+          atomicAdd(&s_cnt[q], 1);
+        }
+      }
+      scarry += tot;
     }
-    carry += tot;
-    int rtot;
-    int rex = block_exclusive_scan(rows, s_wave, &rtot);
-    if (b < batch) row_ptr[b] = rcarry + rex;
-    rcarry += rtot;
+    nitems = icarry;
+    __syncthreads();
+  } else {
+    // Pieces per request: k = ceil(cost / P) when the request exceeds the
+    // target, each a near-equal share of the request's units.
+    for (int base = 0; base < batch; base += kPlanThreads) {
+      const int b = base + tid;
+      int k = 0;
+      if (b < batch) {
+        const int cost = cost_of(b);
+        k = cost > P ? (cost + P - 1) / P : 1;
+      }
+      int tot;
+      const int iex = block_exclusive_scan(k, s_wave, &tot);
+      if (b < batch) s_pb[b] = nitems + iex;
+      nitems += tot;
+      const int rex = block_exclusive_scan(k > 1 ? k : 0, s_wave, &tot);
+      if (b < batch) row_ptr[b] = rcarry + rex;
+      rcarry += tot;
+      const int sex = block_exclusive_scan(k > 1 ? 1 : 0, s_wave, &tot);
+      if (b < batch && k > 1) split[scarry + sex] = b;
+      scarry += tot;
+    }
+    if (tid == 0) s_pb[batch] = nitems;
+    parts = min(max_parts, nitems);
+    int shift = 0;
+    while ((cmax >> shift) >= kCostBuckets) ++shift;
+    for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_bucket[i] = 0;
+    __syncthreads();
+    // piece i -> request (binary search over s_pb), units, cost bucket
+    auto piece = [&](int i, int& b, int& u0, int& u1, int& row) {
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pb[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      b = lo;
+      const int j = i - s_pb[b], k = s_pb[b + 1] - s_pb[b];
+      const int nu = units_of(clamp_len(seq_lens[b], cap_tokens));
+      u0 = int((long long)j * nu / k);
+      u1 = int((long long)(j + 1) * nu / k);
+      row = k > 1 ? row_ptr[b] + j : -1;
+    };
+    for (int i = tid; i < nitems; i += kPlanThreads) {
+      int b, u0, u1, row;
+      piece(i, b, u0, u1, row);
+      atomicAdd(&s_bucket[(kOverheadUnits + u1 - u0) >> shift], 1);
+    }
+    __syncthreads();
+    // rank base of each bucket, largest costs first
+    {
+      int v[4], sum = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[k] = s_bucket[kCostBuckets - 1 - (4 * tid + k)];
+        sum += v[k];
+      }
+      int tot;
+      int ex = block_exclusive_scan(sum, s_wave, &tot);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        s_bucket[kCostBuckets - 1 - (4 * tid + k)] = ex;
+        ex += v[k];
+      }
+    }
+    __syncthreads();
+    for (int i = tid; i < nitems; i += kPlanThreads) {
+      int b, u0, u1, row;
+      piece(i, b, u0, u1, row);
+      const int rank = atomicAdd(&s_bucket[(kOverheadUnits + u1 - u0) >> shift], 1);
+      const int round = rank / parts, pos = rank - round * parts;
+      const int q = (round & 1) ? parts - 1 - pos : pos;
+      s_pq[i] = short(q);
+      atomicAdd(&s_cnt[q], 1);
+    }
+    __syncthreads();
+  }
+  // part_ptr from the per-partition counts; s_cnt becomes the fill cursor.
+  block_scan_lds(s_cnt, max_parts + 1, s_wave);
+  for (int q = tid; q <= max_parts; q += kPlanThreads) part_ptr[q] = s_cnt[q];
+  __syncthreads();
+  if (snake) {
+    for (int i = tid; i < nitems; i += kPlanThreads) {
+      int lo = 0, hi = batch - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_pb[mid] <= i) lo = mid; else hi = mid - 1;
+      }
+      const int b = lo;
+      const int j = i - s_pb[b], k = s_pb[b + 1] - s_pb[b];
+      const int nu = units_of(clamp_len(seq_lens[b], cap_tokens));
+      const int pos = atomicAdd(&s_cnt[s_pq[i]], 1);
+      work[pos] = make_int4(b, int((long long)j * nu / k), int((long long)(j + 1) * nu / k),
+                            k > 1 ? row_ptr[b] + j : -1);
+    }
   }
   if (tid == 0) {
+    cum[batch] = total;
     row_ptr[batch] = rcarry;
     header[0] = parts;
-    header[1] = part;
+    header[1] = P;
+    header[2] = scarry;
+    header[3] = snake ? kPlanSnake : kPlanContiguous;
   }
 }
 
-// ----------------------------------------------------------------------------
-// Attention.
-
-// Partition -> pieces. Calls fn(b, u0, u1, piece, pieces) for every piece of
-// partition `part`: one piece in forced mode, every request overlapping the
-// partition's cost range in balanced mode. Uniform across the workgroup.
+// Partition -> work items. Calls fn(b, u0, u1, row) for every piece of
+// partition `part`: units [u0, u1) of request b, written as the final output
+// when row < 0, else as partial row `row`. Uniform across the workgroup.
 template <typename Fn>
 __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, Fn&& fn) {
-  int b, end = 0, P = 1;
   if (a.num_splits > 0) {
-    if (part >= a.batch * a.num_splits) return;
-    b = part / a.num_splits;
-  } else {
-    const int parts = a.header[0];
-    P = a.header[1];
-    if (part >= parts) return;
-    const int start = part * P;
-    end = start + P;
-    int lo = 0, hi = a.batch - 1;  // first request whose cost range reaches past start
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (a.cum[mid + 1] > start)
-        hi = mid;
-      else
-        lo = mid + 1;
-    }
-    b = lo;
+    // Forced split k of request b; an empty split still writes its
+    // (zero, -inf) partial because the combine reads every row.
+    const int S = a.num_splits;
+    if (part >= a.batch * S) return;
+    const int b = part / S, k = part - b * S;
+    const int nu = (clamp_len(a.seq_lens[b], a.cap_tokens) + kUnit - 1) / kUnit;
+    fn(b, int((long long)k * nu / S), int((long long)(k + 1) * nu / S), S > 1 ? part : -1);
+    return;
   }
-  for (;;) {
-    int u0, u1, piece, pieces;
-    bool last;
-    if (a.num_splits > 0) {
-      // Forced split k of request b; an empty split still writes its
-      // (zero, -inf) partial because the combine reads every row.
-      const int S = a.num_splits, k = part - b * S;
-      const int nu = (clamp_len(a.seq_lens[b], a.cap_tokens) + kUnit - 1) / kUnit;
-      u0 = int((long long)k * nu / S);
-      u1 = int((long long)(k + 1) * nu / S);
-      piece = k;
-      pieces = S;
-      last = true;
-    } else {
-      const int ub = a.cum[b] + kOverheadUnits;  // cost position of the request's first unit
-      if (ub >= end) return;
-      const int ue = a.cum[b + 1];
-      const int p0 = max(ub, part * P), p1 = min(ue, end);
-      if (p0 >= p1) return;
-      u0 = p0 - ub;
-      u1 = p1 - ub;
-      piece = p0 / P - ub / P;
-      pieces = (ue - 1) / P - ub / P + 1;
-      last = ue >= end || b + 1 >= a.batch;
-    }
-    fn(b, u0, u1, piece, pieces);
-    if (last) return;
-    ++b;
+  if (part >= a.parts_cap) return;
+  const int i0 = max(a.part_ptr[part], 0), i1 = min(a.part_ptr[part + 1], a.items_cap);
+  for (int i = i0; i < i1; ++i) {
+    const int4 it = a.work[i];
+    // Items that would address outside the buffers are skipped (never
+    // produced by the plan; a guard against a corrupted workspace).
+    if (unsigned(it.x) >= unsigned(a.batch) || it.y < 0 || it.z < it.y || it.w >= a.rows_cap)
+      continue;
+    fn(it.x, it.y, it.z, it.w);
   }
 }
 
@@ -390,7 +535,7 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
       (void __attribute__((address_space(3)))*)(&ring[0][0])));
   const int bs_mask = (1 << a.bs_log2) - 1;
 
-  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
+  for_each_piece(a, part, [&](int b, int u0, int u1, int out_row) {
     const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
     const int ntiles = u_end > u0 ? (u_end - u0 + 1) / 2 : 0;
@@ -506,10 +651,10 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
             lbuf[c] = l_c;
             if (h0 + c < H) {
               const float lse_v = l_c > 0.f ? (m_ref + __log2f(l_c)) * kLn2 : -INFINITY;
-              if (pieces == 1) {
+              if (out_row < 0) {
                 if (a.lse) a.lse[size_t(b) * H + h0 + c] = lse_v;
               } else {
-                a.part_lse[size_t(a.row_ptr[b] + piece) * H + h0 + c] = lse_v;
+                a.part_lse[size_t(out_row) * H + h0 + c] = lse_v;
               }
             }
           }
@@ -590,8 +735,8 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
 
     if (!logit_wave) {
       // Epilogue: heads 4 g + r, features 128 wave + 8 c .. + 7 in acc[0..7][r].
-      const bool final_out = pieces == 1;
-      const int row = final_out ? 0 : a.row_ptr[b] + piece;
+      const bool final_out = out_row < 0;
+      const int row = final_out ? 0 : out_row;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int hh = 4 * g + r;
@@ -718,6 +863,32 @@ __device__ __forceinline__ void lds_read_trb8(const uint32_t (&vb)[4], u32x2_t (
       : "memory");
 }
 
+// The four head tiles' E4M3 P operands (two 16-byte halves each, 2048
+// bytes apart per tile) and E8M0 scales (64 bytes apart per tile) of one
+// lane, read with an explicit wait (no wait on the ring's loads).
+__device__ __forceinline__ void lds_read_p4(uint32_t p_addr, uint32_t e_addr, u32x4_t (&p)[4][2],
+                                            int (&e)[4]) {
+  asm volatile(
+      "ds_read_b128 %0, %12 offset:0\n\t"
+      "ds_read_b128 %1, %12 offset:16\n\t"
+      "ds_read_b128 %2, %12 offset:2048\n\t"
+      "ds_read_b128 %3, %12 offset:2064\n\t"
+      "ds_read_b128 %4, %12 offset:4096\n\t"
+      "ds_read_b128 %5, %12 offset:4112\n\t"
+      "ds_read_b128 %6, %12 offset:6144\n\t"
+      "ds_read_b128 %7, %12 offset:6160\n\t"
+      "ds_read_b32 %8, %13 offset:0\n\t"
+      "ds_read_b32 %9, %13 offset:64\n\t"
+      "ds_read_b32 %10, %13 offset:128\n\t"
+      "ds_read_b32 %11, %13 offset:192\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(p[0][0]), "=&v"(p[0][1]), "=&v"(p[1][0]), "=&v"(p[1][1]), "=&v"(p[2][0]),
+        "=&v"(p[2][1]), "=&v"(p[3][0]), "=&v"(p[3][1]), "=&v"(e[0]), "=&v"(e[1]), "=&v"(e[2]),
+        "=&v"(e[3])
+      : "v"(p_addr), "v"(e_addr)
+      : "memory");
+}
+
 __device__ __forceinline__ f32x4_t mfma_e4m3_128(const i32x8_t& a, const i32x8_t& b,
                                                  const f32x4_t& c, int scale_a) {
   // Format code 0 = E4M3 for both operands; E8M0 scales (127 = 2^0).
@@ -826,7 +997,15 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
                  16u * uint32_t(16 * wq + ((2 * j + (av >> 1)) ^ (t0 & 7))) + 8u * uint32_t(av & 1);
   }
 
-  for_each_piece(a, part, [&](int b, int u0, int u1, int piece, int pieces) {
+  // P.V waves (E4M3): LDS addresses of this lane's P operands and scales.
+  const uint32_t p_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (void __attribute__((address_space(3)))*)(&pbuf[0][lane][0])));
+  const uint32_t e_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (void __attribute__((address_space(3)))*)(&ebuf[0][c])));
+  static_assert(!KV_FP8 || sizeof(pbuf[0]) == 2048, "P operand stride");
+  static_assert(sizeof(ebuf[0]) == 64, "scale stride");
+
+  for_each_piece(a, part, [&](int b, int u0, int u1, int out_row) {
     const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
     const int ntiles = u_end > u0 ? (u_end - u0 + kUnits - 1) / kUnits : 0;
@@ -861,8 +1040,8 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
       }
     };
 
-    const bool final_out = pieces == 1;
-    const int row = final_out ? 0 : a.row_ptr[b] + piece;
+    const bool final_out = out_row < 0;
+    const int row = final_out ? 0 : out_row;
     // Both roles pass the same barriers in the same order: per pass one
     // opening barrier, two per step, two closing ones; then one before the
     // epilogue's output stores.
@@ -958,12 +1137,20 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
             int nv[kUnits];
             tile_nv(s, nv);
             float x[kUnits][4];
+            // K through ordinary LDS loads: logit waves issue no ring loads,
+            // so the compiler's own waits cost nothing and it may overlap the
+            // reads with the matrix ops.
+            const uint8_t* stp = &ring[s % kStages][0];
             if constexpr (!KV_FP8) {
 #pragma unroll
               for (int h = 0; h < 2; ++h) {
-                const uint32_t rowa = st + uint32_t(h * kUnit * kRowB);
+                const uint8_t* rowp = stp + h * kUnit * kRowB;
                 u32x4_t kf[kQChunks];
-                lds_read_k(rowa + k_off0, rowa + k_off1, kf);
+#pragma unroll
+                for (int k2 = 0; k2 < kQChunks / 2; ++k2) {
+                  kf[2 * k2] = *reinterpret_cast<const u32x4_t*>(rowp + k_off0 + 128 * k2);
+                  kf[2 * k2 + 1] = *reinterpret_cast<const u32x4_t*>(rowp + k_off1 + 128 * k2);
+                }
                 f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s2 = 0; s2 < kQChunks; ++s2)
@@ -978,7 +1165,10 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
               auto logits = [&](auto uc) {
                 constexpr int U = decltype(uc)::value;
                 u32x4_t kf[kKChunksFp8];
-                lds_read_k9<U * kUnit * kDK>(st + ((U & 1) ? k_off1 : k_off0), kf);
+                const uint8_t* up = stp + U * kUnit * kDK + ((U & 1) ? k_off1 : k_off0);
+#pragma unroll
+                for (int m = 0; m < kKChunksFp8; ++m)
+                  kf[m] = *reinterpret_cast<const u32x4_t*>(up + 64 * m);
                 f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int p2 = 0; p2 < 4; ++p2) {
@@ -1002,6 +1192,15 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
               logits(std::integral_constant<int, 2>{});
               logits(std::integral_constant<int, 3>{});
             }
+            // Keep nine K reads in flight ahead of the matrix ops: 9 reads,
+            // then (1 op, 1 read) x 27, then the last 9 ops.
+            __builtin_amdgcn_sched_group_barrier(0x100, 9, 0);
+#pragma unroll
+            for (int i = 0; i < 27; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
             float mt = -INFINITY;
 #pragma unroll
             for (int u = 0; u < kUnits; ++u)
@@ -1111,14 +1310,18 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
           i32x8_t pv_pa[4];  // E4M3 A operands
           int pv_e[4];
           if (s >= 1) {
+            if constexpr (KV_FP8) {
+              // Ordinary loads here would make the compiler wait for every
+              // ring load in flight first (it cannot tell them apart).
+              u32x4_t ph[4][2];
+              lds_read_p4(p_lds, e_lds, ph, pv_e);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-              if constexpr (KV_FP8) {
-                pv_pa[t] = *reinterpret_cast<const i32x8_t*>(&pbuf[t][lane][0]);
-                pv_e[t] = ebuf[t][c];
-              } else {
-                pv_p[t] = pbuf[t][lane][0];
-              }
+              for (int t = 0; t < 4; ++t)
+                pv_pa[t] = __builtin_bit_cast(
+                    i32x8_t, __builtin_shufflevector(ph[t][0], ph[t][1], 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+#pragma unroll
+              for (int t = 0; t < 4; ++t) pv_p[t] = pbuf[t][lane][0];
             }
           }
           wave_barrier_lds();  // barrier 2: P taken, pbuf may be overwritten
@@ -1232,16 +1435,11 @@ constexpr int kCombineChunk = 64;
 constexpr int kCombineChunks = kDV / kCombineChunk;  // 8
 constexpr int kCombineUnroll = 8;
 
-__global__ void __launch_bounds__(256) combine_kernel(const float* part_out, const float* part_lse,
-                                                      const int32_t* row_ptr, uint16_t* out,
-                                                      float* lse, int32_t batch, int32_t H,
-                                                      int32_t tiles, int zero_empty) {
-  const int blk = blockIdx.x;
-  const int chunk = blk % kCombineChunks;
-  const int bt = blk / kCombineChunks;
-  const int b = bt / tiles, ht = bt - (bt / tiles) * tiles;
-  const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
-  if (nr <= 0 && !zero_empty) return;
+// Merge rows r0 .. r0 + nr - 1 of request b for head tile ht and 64-feature
+// chunk `chunk`: thread (head tid / 16, features 4 (tid % 16) ..) of 256.
+__device__ __forceinline__ void combine_rows(const float* part_out, const float* part_lse, int r0,
+                                             int nr, uint16_t* out, float* lse, int b, int H,
+                                             int ht, int chunk) {
   const int tid = threadIdx.x;
   const int h = ht * kHeadTile + (tid >> 4);
   if (h >= H) return;
@@ -1277,14 +1475,48 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* part_out, con
   if (chunk == 0 && (tid & 15) == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
+__global__ void __launch_bounds__(256) combine_kernel(const float* part_out, const float* part_lse,
+                                                      const int32_t* row_ptr, uint16_t* out,
+                                                      float* lse, int32_t batch, int32_t H,
+                                                      int32_t tiles, int zero_empty) {
+  const int blk = blockIdx.x;
+  const int chunk = blk % kCombineChunks;
+  const int bt = blk / kCombineChunks;
+  const int b = bt / tiles, ht = bt - (bt / tiles) * tiles;
+  const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
+  if (nr <= 0 && !zero_empty) return;
+  combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+}
+
+// The automatic plan's combine: block k merges request split[k] (header[2]
+// such requests); the rest exit at once.
+__global__ void __launch_bounds__(256) combine_split_kernel(
+    const float* part_out, const float* part_lse, const int32_t* row_ptr, const int32_t* split,
+    const int32_t* header, uint16_t* out, float* lse, int32_t H, int32_t tiles) {
+  const int blk = blockIdx.x;
+  const int per = tiles * kCombineChunks;
+  const int k = blk / per;
+  if (k >= header[2]) return;
+  const int rest = blk - k * per;
+  const int b = split[k];
+  const int chunk = rest % kCombineChunks, ht = rest / kCombineChunks;
+  const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
+  combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+}
+
 // ----------------------------------------------------------------------------
 // Host-side launchers.
 
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
-                       int32_t num_splits, int32_t max_parts, int32_t* header, int32_t* cum,
-                       int32_t* row_ptr, hipStream_t stream) {
+                       int32_t num_splits, int32_t max_parts, const WorkspaceLayout& w,
+                       void* workspace, hipStream_t stream) {
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch,
-                     cap_tokens, num_splits, max_parts, header, cum, row_ptr);
+                     cap_tokens, num_splits, max_parts, reinterpret_cast<int32_t*>(ws + w.header),
+                     reinterpret_cast<int32_t*>(ws + w.cum),
+                     reinterpret_cast<int32_t*>(ws + w.row_ptr),
+                     reinterpret_cast<int32_t*>(ws + w.part_ptr),
+                     reinterpret_cast<int4*>(ws + w.work), reinterpret_cast<int32_t*>(ws + w.split));
   return hipGetLastError();
 }
 
@@ -1308,6 +1540,19 @@ hipError_t launch_combine(const float* part_out, const float* part_lse,
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(batch) * unsigned(tiles) * kCombineChunks),
                      dim3(256), 0, stream,
                      part_out, part_lse, row_ptr, out, lse, batch, num_heads, tiles, zero_empty);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_split(const float* part_out, const float* part_lse,
+                                const int32_t* row_ptr, const int32_t* split,
+                                const int32_t* header, uint16_t* out, float* lse,
+                                int32_t max_split, int32_t num_heads, hipStream_t stream) {
+  const int tiles = head_tiles(num_heads);
+  if (max_split <= 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_split_kernel,
+                     dim3(unsigned(max_split) * unsigned(tiles) * kCombineChunks), dim3(256), 0,
+                     stream, part_out, part_lse, row_ptr, split, header, out, lse, num_heads,
+                     tiles);
   return hipGetLastError();
 }
 

@@ -72,9 +72,10 @@ def test_status_strings_and_version():
 
 # ------------------------------------------------------------------ workspace size
 
-def _layout(batch, heads, rows):
+def _layout(batch, heads, rows, parts=1):
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    return 256 + 2 * a((batch + 1) * 4) + a(rows * heads * 4) + a(rows * heads * 512 * 4)
+    return (256 + 2 * a((batch + 1) * 4) + a((parts + 1) * 4) + a((batch + parts) * 16)
+            + a(parts * 4) + a(rows * heads * 4) + a(rows * heads * 512 * 4))
 
 
 def test_workspace_size_forced_mode():
@@ -84,16 +85,16 @@ def test_workspace_size_forced_mode():
 
 
 def test_workspace_size_auto_mode():
-    # 256 CUs, 16 heads: up to 256 partitions -> at most 2 * 255 partial rows.
-    assert mla.get_workspace_size(512, 16, 3072, 0, 0) == _layout(512, 16, 510)
-    assert mla.get_workspace_size(512, 16, 3072, 0, 256) == _layout(512, 16, 510)
+    # 256 CUs, 16 heads: up to 256 partitions -> at most 2 * 256 partial rows.
+    assert mla.get_workspace_size(512, 16, 3072, 0, 0) == _layout(512, 16, 512, 256)
+    assert mla.get_workspace_size(512, 16, 3072, 0, 256) == _layout(512, 16, 512, 256)
     # 128 heads: two workgroups (four 16-head tiles each) per partition -> 128.
-    assert mla.get_workspace_size(128, 128, 32768, 0, 0) == _layout(128, 128, 254)
+    assert mla.get_workspace_size(128, 128, 32768, 0, 0) == _layout(128, 128, 256, 128)
     # 64 heads fit one workgroup per partition.
-    assert mla.get_workspace_size(128, 64, 32768, 0, 0) == _layout(128, 64, 510)
+    assert mla.get_workspace_size(128, 64, 32768, 0, 0) == _layout(128, 64, 512, 256)
     # Never more rows than every request split into one piece per 16-token unit.
-    assert mla.get_workspace_size(2, 16, 32, 0, 0) == _layout(2, 16, 4)
-    assert mla.get_workspace_size(2, 16, 16, 0, 0) == _layout(2, 16, 0)
+    assert mla.get_workspace_size(2, 16, 32, 0, 0) == _layout(2, 16, 4, 256)
+    assert mla.get_workspace_size(2, 16, 16, 0, 0) == _layout(2, 16, 0, 256)
 
 
 @pytest.mark.parametrize("args", [(-1, 16, 10, 0, 0), (1, 0, 10, 0, 0), (1, 129, 10, 0, 0),
