@@ -93,6 +93,49 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   return res;
 }
 
+// Block-wide exclusive scans of three values at once (same barriers).
+__device__ int3 block_exclusive_scan3(int3 v, int* s_wave, int3* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int3 inc = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int tx = __shfl_up(inc.x, d), ty = __shfl_up(inc.y, d), tz = __shfl_up(inc.z, d);
+    if (lane >= d) {
+      inc.x += tx;
+      inc.y += ty;
+      inc.z += tz;
+    }
+  }
+  if (lane == 63) {
+    s_wave[wave] = inc.x;
+    s_wave[16 + wave] = inc.y;
+    s_wave[32 + wave] = inc.z;
+  }
+  __syncthreads();
+  int3 base = make_int3(0, 0, 0), tot = make_int3(0, 0, 0);
+  for (int w = 0; w < kPlanThreads / 64; ++w) {
+    const int3 sw = make_int3(s_wave[w], s_wave[16 + w], s_wave[32 + w]);
+    if (w < wave) {
+      base.x += sw.x;
+      base.y += sw.y;
+      base.z += sw.z;
+    }
+    tot.x += sw.x;
+    tot.y += sw.y;
+    tot.z += sw.z;
+  }
+  __syncthreads();
+  *total = tot;
+  return make_int3(base.x + inc.x - v.x, base.y + inc.y - v.y, base.z + inc.z - v.z);
+}
+
+// Start of piece j when `units` are cut into k near-equal pieces (the first
+// units % k pieces one unit longer).
+__device__ __forceinline__ int piece_start(int j, int units, int k) {
+  const int q = units / k, r = units - q * k;
+  return j * q + min(j, r);
+}
+
 __device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 
 __device__ __forceinline__ int units_of(int n) {
@@ -156,7 +199,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
     const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t num_splits,
     int32_t max_parts, int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr,
     int4* work, int32_t* split) {
-  __shared__ int s_wave[40];
+  __shared__ int s_wave[48];
   __shared__ int s_cnt[kMaxPlanParts + 1];
   __shared__ int s_bucket[kCostBuckets];
   __shared__ int s_pb[kSnakeMaxBatch + 1];
@@ -172,166 +215,196 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
     }
     return;
   }
+  if (batch <= 4 * kPlanThreads) {
+    // Fast path: thread t owns requests 4 t .. 4 t + 3, kept in registers.
+    int units[4], cost[4], c0[4];
+    int csum = 0, cmax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * tid + i;
+      units[i] = b < batch ? units_of(clamp_len(seq_lens[b], cap_tokens)) : 0;
+      cost[i] = b < batch ? kOverheadUnits + units[i] : 0;
+      c0[i] = csum;
+      csum += cost[i];
+      cmax = max(cmax, cost[i]);
+    }
+    int total;
+    const int cex = block_exclusive_scan(csum, s_wave, &total);
+    cmax = block_max(cmax, s_wave);
+    int P = (total + max_parts - 1) / max_parts;
+    if (P < kMinPartUnits) P = kMinPartUnits;
+    const bool snake = batch >= 2 * max_parts && batch <= kSnakeMaxBatch;
+    int k[4];
+    int3 mine = make_int3(0, 0, 0);  // items, rows, split requests
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      c0[i] += cex;
+      const int b = 4 * tid + i;
+      if (b < batch) {
+        k[i] = snake ? (cost[i] > P ? (cost[i] + P - 1) / P : 1)
+                     : (c0[i] + cost[i] - 1) / P - (c0[i] + kOverheadUnits) / P + 1;
+      } else {
+        k[i] = 0;
+      }
+      mine.x += k[i];
+      mine.y += k[i] > 1 ? k[i] : 0;
+      mine.z += k[i] > 1 ? 1 : 0;
+    }
+    for (int q = tid; q <= max_parts; q += kPlanThreads) s_cnt[q] = 0;
+    if (snake)
+      for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_bucket[i] = 0;
+    int3 tot3;
+    const int3 ex3 = block_exclusive_scan3(mine, s_wave, &tot3);  // also orders the zeroing
+    const int nitems = tot3.x;
+    const int parts = snake ? min(max_parts, nitems) : (total + P - 1) / P;
+    int shift = 0;
+    while ((cmax >> shift) >= kCostBuckets) ++shift;
+    int ib = ex3.x, rb = ex3.y, sb = ex3.z;
+    int ibase[4], rbase[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int b = 4 * tid + i;
+      ibase[i] = ib;
+      rbase[i] = rb;
+      if (b < batch) {
+        cum[b] = c0[i];
+        row_ptr[b] = rb;
+        if (k[i] > 1) split[sb++] = b;
+        if (!snake) {
+          const int ub = c0[i] + kOverheadUnits, ue = c0[i] + cost[i];
+          const int first = ub / P;
+          for (int j = 0; j < k[i]; ++j) {
+            const int q = first + j;
+            const int p0 = max(ub, q * P), p1 = min(ue, (q + 1) * P);
+            work[ib + j] = make_int4(b, p0 - ub, p1 - ub, k[i] > 1 ? rb + j : -1);
+            atomicAdd(&s_cnt[q], 1);
+          }
+        } else {
+          // Piece lengths: q + 1 (first r pieces) and q.
+          const int q = units[i] / k[i], r = units[i] - q * k[i];
+          if (r > 0) atomicAdd(&s_bucket[(kOverheadUnits + q + 1) >> shift], r);
+          if (k[i] > r) atomicAdd(&s_bucket[(kOverheadUnits + q) >> shift], k[i] - r);
+        }
+      }
+      ib += k[i];
+      rb += k[i] > 1 ? k[i] : 0;
+    }
+    __syncthreads();
+    if (snake) {
+      // Rank base of each cost bucket, largest first.
+      {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = s_bucket[kCostBuckets - 1 - (4 * tid + i)];
+          sum += v[i];
+        }
+        int tot;
+        int ex = block_exclusive_scan(sum, s_wave, &tot);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          s_bucket[kCostBuckets - 1 - (4 * tid + i)] = ex;
+          ex += v[i];
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int q = units[i] / k[i], r = units[i] - q * k[i];
+        for (int j = 0; j < k[i]; ++j) {
+          const int len = q + (j < r ? 1 : 0);
+          const int rank = atomicAdd(&s_bucket[(kOverheadUnits + len) >> shift], 1);
+          const int round = rank / parts, pos = rank - round * parts;
+          const int q = (round & 1) ? parts - 1 - pos : pos;
+          s_pq[ibase[i] + j] = short(q);
+          atomicAdd(&s_cnt[q], 1);
+        }
+      }
+      __syncthreads();
+    }
+    block_scan_lds(s_cnt, max_parts + 1, s_wave);
+    for (int q = tid; q <= max_parts; q += kPlanThreads) part_ptr[q] = s_cnt[q];
+    __syncthreads();
+    if (snake) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int b = 4 * tid + i;
+        for (int j = 0; j < k[i]; ++j) {
+          const int pos = atomicAdd(&s_cnt[s_pq[ibase[i] + j]], 1);
+          work[pos] = make_int4(b, piece_start(j, units[i], k[i]),
+                                piece_start(j + 1, units[i], k[i]), k[i] > 1 ? rbase[i] + j : -1);
+        }
+      }
+    }
+    if (tid == 0) {
+      cum[batch] = total;
+      row_ptr[batch] = tot3.y;
+      header[0] = parts;
+      header[1] = P;
+      header[2] = tot3.z;
+      header[3] = snake ? kPlanSnake : kPlanContiguous;
+    }
+    return;
+  }
+  // Large batches: contiguous plan over the requests in chunks of
+  // kPlanThreads (costs re-read per pass).
   auto cost_of = [&](int b) {
     return kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens));
   };
-  // Costs: prefix (cum), total and largest.
-  int carry = 0, cmax = 0;
+  int carry = 0;
   for (int base = 0; base < batch; base += kPlanThreads) {
     const int b = base + tid;
     const int cost = b < batch ? cost_of(b) : 0;
-    cmax = max(cmax, cost);
     int tot;
     const int ex = block_exclusive_scan(cost, s_wave, &tot);
     if (b < batch) cum[b] = carry + ex;
     carry += tot;
   }
   const int total = carry;
-  cmax = block_max(cmax, s_wave);
   int P = (total + max_parts - 1) / max_parts;
   if (P < kMinPartUnits) P = kMinPartUnits;
-  const bool snake = batch >= 2 * max_parts && batch <= kSnakeMaxBatch;
+  const int parts = (total + P - 1) / P;
   for (int q = tid; q <= max_parts; q += kPlanThreads) s_cnt[q] = 0;
   __syncthreads();
-
-  int parts, nitems = 0;
-  int rcarry = 0, scarry = 0;
-  if (!snake) {
-    parts = (total + P - 1) / P;
-    int icarry = 0;
-    for (int base = 0; base < batch; base += kPlanThreads) {
-      const int b = base + tid;
-      int k = 0, c0 = 0, cost = 0;
-      if (b < batch) {
-        cost = cost_of(b);
-        c0 = cum[b];
-        k = (c0 + cost - 1) / P - (c0 + kOverheadUnits) / P + 1;
-      }
-      int tot;
-      const int iex = block_exclusive_scan(k, s_wave, &tot);
-      const int ibase = icarry + iex;
-      icarry += tot;
-      const int rex = block_exclusive_scan(k > 1 ? k : 0, s_wave, &tot);
-      const int rbase = rcarry + rex;
-      rcarry += tot;
-      const int sex = block_exclusive_scan(k > 1 ? 1 : 0, s_wave, &tot);
-      if (b < batch) {
-        row_ptr[b] = rbase;
-        if (k > 1) split[scarry + sex] = b;
-        const int ub = c0 + kOverheadUnits, ue = c0 + cost;
-        const int first = ub / P;
-        for (int j = 0; j < k; ++j) {
-          const int q = first + j;
-          const int p0 = max(ub, q * P), p1 = min(ue, (q + 1) * P);
-          work[ibase + j] = make_int4(b, p0 - ub, p1 - ub, k > 1 ? rbase + j : -1);
-          atomicAdd(&s_cnt[q], 1);
-        }
-      }
-      scarry += tot;
+  int3 carry3 = make_int3(0, 0, 0);
+  for (int base = 0; base < batch; base += kPlanThreads) {
+    const int b = base + tid;
+    int k = 0, c0 = 0, cost = 0;
+    if (b < batch) {
+      cost = cost_of(b);
+      c0 = cum[b];
+      k = (c0 + cost - 1) / P - (c0 + kOverheadUnits) / P + 1;
     }
-    nitems = icarry;
-    __syncthreads();
-  } else {
-    // Pieces per request: k = ceil(cost / P) when the request exceeds the
-    // target, each a near-equal share of the request's units.
-    for (int base = 0; base < batch; base += kPlanThreads) {
-      const int b = base + tid;
-      int k = 0;
-      if (b < batch) {
-        const int cost = cost_of(b);
-        k = cost > P ? (cost + P - 1) / P : 1;
-      }
-      int tot;
-      const int iex = block_exclusive_scan(k, s_wave, &tot);
-      if (b < batch) s_pb[b] = nitems + iex;
-      nitems += tot;
-      const int rex = block_exclusive_scan(k > 1 ? k : 0, s_wave, &tot);
-      if (b < batch) row_ptr[b] = rcarry + rex;
-      rcarry += tot;
-      const int sex = block_exclusive_scan(k > 1 ? 1 : 0, s_wave, &tot);
-      if (b < batch && k > 1) split[scarry + sex] = b;
-      scarry += tot;
-    }
-    if (tid == 0) s_pb[batch] = nitems;
-    parts = min(max_parts, nitems);
-    int shift = 0;
-    while ((cmax >> shift) >= kCostBuckets) ++shift;
-    for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_bucket[i] = 0;
-    __syncthreads();
-    // piece i -> request (binary search over s_pb), units, cost bucket
-    auto piece = [&](int i, int& b, int& u0, int& u1, int& row) {
-      int lo = 0, hi = batch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pb[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      b = lo;
-      const int j = i - s_pb[b], k = s_pb[b + 1] - s_pb[b];
-      const int nu = units_of(clamp_len(seq_lens[b], cap_tokens));
-      u0 = int((long long)j * nu / k);
-      u1 = int((long long)(j + 1) * nu / k);
-      row = k > 1 ? row_ptr[b] + j : -1;
-    };
-    for (int i = tid; i < nitems; i += kPlanThreads) {
-      int b, u0, u1, row;
-      piece(i, b, u0, u1, row);
-      atomicAdd(&s_bucket[(kOverheadUnits + u1 - u0) >> shift], 1);
-    }
-    __syncthreads();
-    // rank base of each bucket, largest costs first
-    {
-      int v[4], sum = 0;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        v[k] = s_bucket[kCostBuckets - 1 - (4 * tid + k)];
-        sum += v[k];
-      }
-      int tot;
-      int ex = block_exclusive_scan(sum, s_wave, &tot);
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        s_bucket[kCostBuckets - 1 - (4 * tid + k)] = ex;
-        ex += v[k];
+    int3 tot3;
+    const int3 ex3 = block_exclusive_scan3(make_int3(k, k > 1 ? k : 0, k > 1 ? 1 : 0), s_wave,
+                                           &tot3);
+    if (b < batch) {
+      const int ibase = carry3.x + ex3.x, rbase = carry3.y + ex3.y;
+      row_ptr[b] = rbase;
+      if (k > 1) split[carry3.z + ex3.z] = b;
+      const int ub = c0 + kOverheadUnits, ue = c0 + cost;
+      const int first = ub / P;
+      for (int j = 0; j < k; ++j) {
+        const int q = first + j;
+        const int p0 = max(ub, q * P), p1 = min(ue, (q + 1) * P);
+        work[ibase + j] = make_int4(b, p0 - ub, p1 - ub, k > 1 ? rbase + j : -1);
+        atomicAdd(&s_cnt[q], 1);
       }
     }
-    __syncthreads();
-    for (int i = tid; i < nitems; i += kPlanThreads) {
-      int b, u0, u1, row;
-      piece(i, b, u0, u1, row);
-      const int rank = atomicAdd(&s_bucket[(kOverheadUnits + u1 - u0) >> shift], 1);
-      const int round = rank / parts, pos = rank - round * parts;
-      const int q = (round & 1) ? parts - 1 - pos : pos;
-      s_pq[i] = short(q);
-      atomicAdd(&s_cnt[q], 1);
-    }
-    __syncthreads();
+    carry3.x += tot3.x;
+    carry3.y += tot3.y;
+    carry3.z += tot3.z;
   }
-  // part_ptr from the per-partition counts; s_cnt becomes the fill cursor.
+  __syncthreads();
   block_scan_lds(s_cnt, max_parts + 1, s_wave);
   for (int q = tid; q <= max_parts; q += kPlanThreads) part_ptr[q] = s_cnt[q];
-  __syncthreads();
-  if (snake) {
-    for (int i = tid; i < nitems; i += kPlanThreads) {
-      int lo = 0, hi = batch - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (s_pb[mid] <= i) lo = mid; else hi = mid - 1;
-      }
-      const int b = lo;
-      const int j = i - s_pb[b], k = s_pb[b + 1] - s_pb[b];
-      const int nu = units_of(clamp_len(seq_lens[b], cap_tokens));
-      const int pos = atomicAdd(&s_cnt[s_pq[i]], 1);
-      work[pos] = make_int4(b, int((long long)j * nu / k), int((long long)(j + 1) * nu / k),
-                            k > 1 ? row_ptr[b] + j : -1);
-    }
-  }
   if (tid == 0) {
     cum[batch] = total;
-    row_ptr[batch] = rcarry;
+    row_ptr[batch] = carry3.y;
     header[0] = parts;
     header[1] = P;
-    header[2] = scarry;
-    header[3] = snake ? kPlanSnake : kPlanContiguous;
+    header[2] = carry3.z;
+    header[3] = kPlanContiguous;
   }
 }
 
@@ -1434,6 +1507,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
 constexpr int kCombineChunk = 64;
 constexpr int kCombineChunks = kDV / kCombineChunk;  // 8
 constexpr int kCombineUnroll = 8;
+constexpr int kCombineGrid = 1 << 30;  // no cap: one workgroup per (request, tile, chunk)
 
 // Merge rows r0 .. r0 + nr - 1 of request b for head tile ht and 64-feature
 // chunk `chunk`: thread (head tid / 16, features 4 (tid % 16) ..) of 256.
@@ -1493,15 +1567,18 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* part_out, con
 __global__ void __launch_bounds__(256) combine_split_kernel(
     const float* part_out, const float* part_lse, const int32_t* row_ptr, const int32_t* split,
     const int32_t* header, uint16_t* out, float* lse, int32_t H, int32_t tiles) {
-  const int blk = blockIdx.x;
+  // Grid-stride over (split request, head tile, chunk): a plan without
+  // split requests costs one small launch.
   const int per = tiles * kCombineChunks;
-  const int k = blk / per;
-  if (k >= header[2]) return;
-  const int rest = blk - k * per;
-  const int b = split[k];
-  const int chunk = rest % kCombineChunks, ht = rest / kCombineChunks;
-  const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
-  combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+  const int n = header[2] * per;
+  for (int w = blockIdx.x; w < n; w += gridDim.x) {
+    const int k = w / per;
+    const int rest = w - k * per;
+    const int b = split[k];
+    const int chunk = rest % kCombineChunks, ht = rest / kCombineChunks;
+    const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
+    combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -1549,10 +1626,10 @@ hipError_t launch_combine_split(const float* part_out, const float* part_lse,
                                 int32_t max_split, int32_t num_heads, hipStream_t stream) {
   const int tiles = head_tiles(num_heads);
   if (max_split <= 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_split_kernel,
-                     dim3(unsigned(max_split) * unsigned(tiles) * kCombineChunks), dim3(256), 0,
-                     stream, part_out, part_lse, row_ptr, split, header, out, lse, num_heads,
-                     tiles);
+  const int64_t tuples = int64_t(max_split) * tiles * kCombineChunks;
+  const unsigned grid = unsigned(tuples < kCombineGrid ? tuples : kCombineGrid);
+  hipLaunchKernelGGL(combine_split_kernel, dim3(grid), dim3(256), 0, stream, part_out, part_lse,
+                     row_ptr, split, header, out, lse, num_heads, tiles);
   return hipGetLastError();
 }
 
