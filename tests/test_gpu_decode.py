@@ -101,6 +101,24 @@ def test_rising_logits(orc, num_heads, kv_dtype):
         _check(orc, wl, s, what=f"{wl.name} splits={s}")
 
 
+def test_large_batch_with_long_requests(orc):
+    # Large batch (more than twice the partitions): long requests are cut
+    # into pieces and merged, short ones run whole; all rows are checked.
+    lens = [37, 130, 700] * 172 + [30000, 25000, 9000, 4097]
+    wl = workloads.make_workload(batch=len(lens), num_heads=16, seq=("fixed", lens),
+                                 block_size=64, seed=41, poison=True)
+    _check(orc, wl, 0, what="large batch with long requests")
+
+
+def test_very_large_batch(orc):
+    # Beyond the register-resident plan's batch limit.
+    gen = np.random.default_rng(42)
+    lens = gen.integers(0, 80, size=5000).tolist()
+    wl = workloads.make_workload(batch=len(lens), num_heads=16, seq=("fixed", lens),
+                                 block_size=16, seed=42)
+    _check(orc, wl, 0, what="5000 short requests")
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_block_permutation_bitwise():
