@@ -15,8 +15,9 @@ constexpr int kHeadTile = 16;   // heads per workgroup (MFMA tile columns)
 constexpr int kWaves = 4;       // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;
 constexpr int kOverheadUnits = 1;   // per-request fixed cost in the balanced plan
-constexpr int kMinPartUnits = 4;    // smallest partition: one unit per wave
+constexpr int kMinPartUnits = 8;    // smallest partition (128 tokens): fewer, cheaper merges
 constexpr int kPlanThreads = 1024;
+constexpr int kPlanThreadsSmall = 256;
 constexpr int kMaxPlanParts = 2048;  // partitions of the automatic plan (work list bound)
 
 // Workspace layout. Offsets are 256-byte aligned. `parts` bounds the

@@ -64,7 +64,8 @@ __device__ __forceinline__ unsigned short bf16_bits(float x) {
 }
 
 // ----------------------------------------------------------------------------
-// Block-wide exclusive scan over kPlanThreads threads.
+// Block-wide exclusive scan over NT threads.
+template <int NT = kPlanThreads>
 __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int inc = v;
@@ -76,15 +77,15 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
   if (wave == 0) {
-    int w = lane < kPlanThreads / 64 ? s_wave[lane] : 0;
+    int w = lane < NT / 64 ? s_wave[lane] : 0;
     int winc = w;
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
       int t = __shfl_up(winc, d);
       if (lane >= d) winc += t;
     }
-    if (lane < kPlanThreads / 64) s_wave[16 + lane] = winc - w;
-    if (lane == kPlanThreads / 64 - 1) s_wave[32] = winc;
+    if (lane < NT / 64) s_wave[16 + lane] = winc - w;
+    if (lane == NT / 64 - 1) s_wave[32] = winc;
   }
   __syncthreads();
   int res = s_wave[16 + wave] + inc - v;
@@ -94,6 +95,7 @@ __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
 }
 
 // Block-wide exclusive scans of three values at once (same barriers).
+template <int NT>
 __device__ int3 block_exclusive_scan3(int3 v, int* s_wave, int3* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int3 inc = v;
@@ -113,7 +115,7 @@ __device__ int3 block_exclusive_scan3(int3 v, int* s_wave, int3* total) {
   }
   __syncthreads();
   int3 base = make_int3(0, 0, 0), tot = make_int3(0, 0, 0);
-  for (int w = 0; w < kPlanThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int3 sw = make_int3(s_wave[w], s_wave[16 + w], s_wave[32 + w]);
     if (w < wave) {
       base.x += sw.x;
@@ -147,8 +149,9 @@ __device__ __forceinline__ int units_of(int n) {
 constexpr int kPlanContiguous = 0;
 constexpr int kPlanSnake = 1;
 constexpr int kSnakeMaxBatch = 4096;   // largest batch the snake plan sorts
-constexpr int kCostBuckets = 4096;     // counting-sort buckets of piece costs
+// Counting-sort buckets of piece costs: 4 per plan thread.
 
+template <int NT>
 __device__ __forceinline__ int block_max(int v, int* s_wave) {
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d));
@@ -157,12 +160,13 @@ __device__ __forceinline__ int block_max(int v, int* s_wave) {
   if (lane == 0) s_wave[wave] = v;
   __syncthreads();
   int r = s_wave[0];
-  for (int i = 1; i < kPlanThreads / 64; ++i) r = max(r, s_wave[i]);
+  for (int i = 1; i < NT / 64; ++i) r = max(r, s_wave[i]);
   __syncthreads();
   return r;
 }
 
-// Exclusive scan of s[0..n) in place (n <= kPlanThreads * 4), returns the total.
+// Exclusive scan of s[0..n) in place (n <= NT * 4), returns the total.
+template <int NT>
 __device__ int block_scan_lds(int* s, int n, int* s_wave) {
   const int tid = threadIdx.x;
   int v[4], sum = 0;
@@ -173,7 +177,7 @@ __device__ int block_scan_lds(int* s, int n, int* s_wave) {
     sum += v[k];
   }
   int tot;
-  int ex = block_exclusive_scan(sum, s_wave, &tot);
+  int ex = block_exclusive_scan<NT>(sum, s_wave, &tot);
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
     const int i = 4 * tid + k;
@@ -195,18 +199,19 @@ __device__ int block_scan_lds(int* s, int n, int* s_wave) {
 //    in alternating direction, so large batches need no partial rows;
 //  - contiguous otherwise: the requests' costs laid end to end and cut into
 //    equal partitions; a request straddling a cut becomes several pieces.
-__global__ void __launch_bounds__(kPlanThreads) plan_kernel(
+template <int NT>
+__global__ void __launch_bounds__(NT) plan_kernel(
     const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t num_splits,
     int32_t max_parts, int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr,
     int4* work, int32_t* split) {
   __shared__ int s_wave[48];
   __shared__ int s_cnt[kMaxPlanParts + 1];
-  __shared__ int s_bucket[kCostBuckets];
+  __shared__ int s_bucket[4 * NT];
   __shared__ int s_pb[kSnakeMaxBatch + 1];
   __shared__ short s_pq[kSnakeMaxBatch + kMaxPlanParts];
   const int tid = threadIdx.x;
   if (num_splits > 0) {
-    for (int b = tid; b <= batch; b += kPlanThreads) row_ptr[b] = num_splits > 1 ? b * num_splits : 0;
+    for (int b = tid; b <= batch; b += NT) row_ptr[b] = num_splits > 1 ? b * num_splits : 0;
     if (tid == 0) {
       header[0] = batch * num_splits;
       header[1] = 0;
@@ -215,7 +220,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
     }
     return;
   }
-  if (batch <= 4 * kPlanThreads) {
+  if (batch <= 4 * NT) {
     // Fast path: thread t owns requests 4 t .. 4 t + 3, kept in registers.
     int units[4], cost[4], c0[4];
     int csum = 0, cmax = 0;
@@ -229,8 +234,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
       cmax = max(cmax, cost[i]);
     }
     int total;
-    const int cex = block_exclusive_scan(csum, s_wave, &total);
-    cmax = block_max(cmax, s_wave);
+    const int cex = block_exclusive_scan<NT>(csum, s_wave, &total);
+    cmax = block_max<NT>(cmax, s_wave);
     int P = (total + max_parts - 1) / max_parts;
     if (P < kMinPartUnits) P = kMinPartUnits;
     const bool snake = batch >= 2 * max_parts && batch <= kSnakeMaxBatch;
@@ -250,15 +255,15 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
       mine.y += k[i] > 1 ? k[i] : 0;
       mine.z += k[i] > 1 ? 1 : 0;
     }
-    for (int q = tid; q <= max_parts; q += kPlanThreads) s_cnt[q] = 0;
+    for (int q = tid; q <= max_parts; q += NT) s_cnt[q] = 0;
     if (snake)
-      for (int i = tid; i < kCostBuckets; i += kPlanThreads) s_bucket[i] = 0;
+      for (int i = tid; i < (4 * NT); i += NT) s_bucket[i] = 0;
     int3 tot3;
-    const int3 ex3 = block_exclusive_scan3(mine, s_wave, &tot3);  // also orders the zeroing
+    const int3 ex3 = block_exclusive_scan3<NT>(mine, s_wave, &tot3);  // also orders the zeroing
     const int nitems = tot3.x;
     const int parts = snake ? min(max_parts, nitems) : (total + P - 1) / P;
     int shift = 0;
-    while ((cmax >> shift) >= kCostBuckets) ++shift;
+    while ((cmax >> shift) >= (4 * NT)) ++shift;
     int ib = ex3.x, rb = ex3.y, sb = ex3.z;
     int ibase[4], rbase[4];
 #pragma unroll
@@ -296,14 +301,14 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
         int v[4], sum = 0;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] = s_bucket[kCostBuckets - 1 - (4 * tid + i)];
+          v[i] = s_bucket[(4 * NT) - 1 - (4 * tid + i)];
           sum += v[i];
         }
         int tot;
-        int ex = block_exclusive_scan(sum, s_wave, &tot);
+        int ex = block_exclusive_scan<NT>(sum, s_wave, &tot);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          s_bucket[kCostBuckets - 1 - (4 * tid + i)] = ex;
+          s_bucket[(4 * NT) - 1 - (4 * tid + i)] = ex;
           ex += v[i];
         }
       }
@@ -322,8 +327,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
       }
       __syncthreads();
     }
-    block_scan_lds(s_cnt, max_parts + 1, s_wave);
-    for (int q = tid; q <= max_parts; q += kPlanThreads) part_ptr[q] = s_cnt[q];
+    block_scan_lds<NT>(s_cnt, max_parts + 1, s_wave);
+    for (int q = tid; q <= max_parts; q += NT) part_ptr[q] = s_cnt[q];
     __syncthreads();
     if (snake) {
 #pragma unroll
@@ -347,16 +352,16 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
     return;
   }
   // Large batches: contiguous plan over the requests in chunks of
-  // kPlanThreads (costs re-read per pass).
+  // NT (costs re-read per pass).
   auto cost_of = [&](int b) {
     return kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens));
   };
   int carry = 0;
-  for (int base = 0; base < batch; base += kPlanThreads) {
+  for (int base = 0; base < batch; base += NT) {
     const int b = base + tid;
     const int cost = b < batch ? cost_of(b) : 0;
     int tot;
-    const int ex = block_exclusive_scan(cost, s_wave, &tot);
+    const int ex = block_exclusive_scan<NT>(cost, s_wave, &tot);
     if (b < batch) cum[b] = carry + ex;
     carry += tot;
   }
@@ -364,10 +369,10 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
   int P = (total + max_parts - 1) / max_parts;
   if (P < kMinPartUnits) P = kMinPartUnits;
   const int parts = (total + P - 1) / P;
-  for (int q = tid; q <= max_parts; q += kPlanThreads) s_cnt[q] = 0;
+  for (int q = tid; q <= max_parts; q += NT) s_cnt[q] = 0;
   __syncthreads();
   int3 carry3 = make_int3(0, 0, 0);
-  for (int base = 0; base < batch; base += kPlanThreads) {
+  for (int base = 0; base < batch; base += NT) {
     const int b = base + tid;
     int k = 0, c0 = 0, cost = 0;
     if (b < batch) {
@@ -376,7 +381,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
       k = (c0 + cost - 1) / P - (c0 + kOverheadUnits) / P + 1;
     }
     int3 tot3;
-    const int3 ex3 = block_exclusive_scan3(make_int3(k, k > 1 ? k : 0, k > 1 ? 1 : 0), s_wave,
+    const int3 ex3 = block_exclusive_scan3<NT>(make_int3(k, k > 1 ? k : 0, k > 1 ? 1 : 0), s_wave,
                                            &tot3);
     if (b < batch) {
       const int ibase = carry3.x + ex3.x, rbase = carry3.y + ex3.y;
@@ -396,8 +401,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_kernel(
     carry3.z += tot3.z;
   }
   __syncthreads();
-  block_scan_lds(s_cnt, max_parts + 1, s_wave);
-  for (int q = tid; q <= max_parts; q += kPlanThreads) part_ptr[q] = s_cnt[q];
+  block_scan_lds<NT>(s_cnt, max_parts + 1, s_wave);
+  for (int q = tid; q <= max_parts; q += NT) part_ptr[q] = s_cnt[q];
   if (tid == 0) {
     cum[batch] = total;
     row_ptr[batch] = carry3.y;
@@ -1506,7 +1511,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
 // with kCombineUnroll partial rows in flight.
 constexpr int kCombineChunk = 64;
 constexpr int kCombineChunks = kDV / kCombineChunk;  // 8
-constexpr int kCombineUnroll = 8;
+constexpr int kCombineUnroll = 16;
 constexpr int kCombineGrid = 1 << 30;  // no cap: one workgroup per (request, tile, chunk)
 
 // Merge rows r0 .. r0 + nr - 1 of request b for head tile ht and 64-feature
@@ -1518,26 +1523,34 @@ __device__ __forceinline__ void combine_rows(const float* part_out, const float*
   const int h = ht * kHeadTile + (tid >> 4);
   if (h >= H) return;
   const int d = chunk * kCombineChunk + 4 * (tid & 15);
+  // One pass with a running maximum, kCombineUnroll rows in flight:
+  // acc and W are kept relative to M and rescaled when M rises.
   float M = -INFINITY;
-  for (int s = 0; s < nr; ++s) M = fmaxf(M, part_lse[size_t(r0 + s) * H + h]);
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
-  if (M != -INFINITY) {
-    for (int s0 = 0; s0 < nr; s0 += kCombineUnroll) {
-      f32x4_t v[kCombineUnroll];
-      float w[kCombineUnroll];
+  for (int s0 = 0; s0 < nr; s0 += kCombineUnroll) {
+    f32x4_t v[kCombineUnroll];
+    float ls[kCombineUnroll];
 #pragma unroll
-      for (int k = 0; k < kCombineUnroll; ++k) {
-        const int s = min(s0 + k, nr - 1);
-        const float ls = part_lse[size_t(r0 + s) * H + h];
-        w[k] = (s0 + k < nr && ls != -INFINITY) ? fast_exp2((ls - M) * kLog2e) : 0.f;
-        v[k] = *reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s) * H + h) * kDV + d);
-      }
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      const int s = min(s0 + k, nr - 1);
+      ls[k] = s0 + k < nr ? part_lse[size_t(r0 + s) * H + h] : -INFINITY;
+      v[k] = *reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s) * H + h) * kDV + d);
+    }
+    float mb = ls[0];
 #pragma unroll
-      for (int k = 0; k < kCombineUnroll; ++k) {
-        if (w[k] != 0.f) acc += w[k] * v[k];  // an empty row's values are never used
-        W += w[k];
-      }
+    for (int k = 1; k < kCombineUnroll; ++k) mb = fmaxf(mb, ls[k]);
+    if (mb == -INFINITY) continue;  // only empty rows in this batch
+    const float Mn = fmaxf(M, mb);
+    const float a = M == -INFINITY ? 0.f : fast_exp2((M - Mn) * kLog2e);
+    acc *= a;
+    W *= a;
+    M = Mn;
+#pragma unroll
+    for (int k = 0; k < kCombineUnroll; ++k) {
+      const float w = ls[k] != -INFINITY ? fast_exp2((ls[k] - M) * kLog2e) : 0.f;
+      if (w != 0.f) acc += w * v[k];  // an empty row's values are never used
+      W += w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
@@ -1588,9 +1601,12 @@ hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_token
                        int32_t num_splits, int32_t max_parts, const WorkspaceLayout& w,
                        void* workspace, hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, seq_lens, batch,
-                     cap_tokens, num_splits, max_parts, reinterpret_cast<int32_t*>(ws + w.header),
-                     reinterpret_cast<int32_t*>(ws + w.cum),
+  // Small batches and partition counts: a quarter of the threads (cheaper barriers).
+  const bool small = batch <= 4 * kPlanThreadsSmall && max_parts < 4 * kPlanThreadsSmall;
+  auto kern = small ? plan_kernel<kPlanThreadsSmall> : plan_kernel<kPlanThreads>;
+  hipLaunchKernelGGL(kern, dim3(1), dim3(small ? kPlanThreadsSmall : kPlanThreads), 0, stream,
+                     seq_lens, batch, cap_tokens, num_splits, max_parts,
+                     reinterpret_cast<int32_t*>(ws + w.header), reinterpret_cast<int32_t*>(ws + w.cum),
                      reinterpret_cast<int32_t*>(ws + w.row_ptr),
                      reinterpret_cast<int32_t*>(ws + w.part_ptr),
                      reinterpret_cast<int4*>(ws + w.work), reinterpret_cast<int32_t*>(ws + w.split));
