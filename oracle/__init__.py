@@ -6,7 +6,7 @@ and its binding) never imports this package, and this package imports nothing
 from the product path.
 
 The arithmetic lives in ``mla_oracle.c`` (plain C, fp64, one sequential loop
-per (request, head), OpenMP across them). This module builds it with gcc and
+per (request, query token, head), OpenMP across them). This module builds it with gcc and
 marshals numpy arrays through ctypes. See the C file's header for what is
 computed and which passage of each page it follows.
 """
@@ -39,7 +39,7 @@ def build(source: str = SOURCE, output: str = LIBRARY) -> str:
 def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.oracle_mla_attend.argtypes = [vp, vp, i32, ctypes.c_float, vp, vp, i64, i64, i64,
-                                      i64, i64, ctypes.c_float, vp, vp, vp, i64, vp, vp]
+                                      i64, i64, i64, ctypes.c_float, vp, vp, vp, i64, vp, vp]
     lib.oracle_mla_attend.restype = i32
     lib.oracle_lse_merge.argtypes = [vp, vp, i64, i64, vp, vp]
     lib.oracle_lse_merge.restype = i32
@@ -75,18 +75,24 @@ class Oracle:
                kv_fp8=False, kv_scale=1.0, req=None, tok_begin=None, tok_end=None):
         """Exact attention of (request, token range) items.
 
-        q_bits      uint16 [B, H, 576]: bf16 bit patterns
+        q_bits      uint16 [B, H, 576] (one query token per request) or
+                    [B, q_len, H, 576] (q_len query tokens, causal): bf16 bits
         kv          uint16 [NB, bs, 576] bf16 bits, or uint8 E4M3FN codes if kv_fp8
         block_table int32 [B, max_blocks]; seq_lens int32 [B]
         req         int32 [n] request of each item (default: every request)
         tok_begin/end int64 [n] token range per item (default: whole request)
-        Returns (out float64 [n, H, 512], lse float64 [n, H]).
+        Returns (out float64 [n, H, 512], lse float64 [n, H]), with a q_len
+        axis after n when q_bits has one.
         """
         q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
         kv = np.ascontiguousarray(kv, dtype=np.uint8 if kv_fp8 else np.uint16)
         block_table = np.ascontiguousarray(block_table, dtype=np.int32)
         seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
-        batch, num_heads, dk = q_bits.shape
+        multi = q_bits.ndim == 4
+        if multi:
+            batch, q_len, num_heads, dk = q_bits.shape
+        else:
+            (batch, num_heads, dk), q_len = q_bits.shape, 1
         if dk != D_K or kv.shape[-1] != D_K or kv.shape[1] != block_size:
             raise ValueError("shape mismatch")
         if req is None:
@@ -99,14 +105,17 @@ class Oracle:
             tok_end = seq_lens[req].astype(np.int64)
         tok_begin = np.ascontiguousarray(tok_begin, dtype=np.int64)
         tok_end = np.ascontiguousarray(tok_end, dtype=np.int64)
-        out = np.empty((n, num_heads, D_V), dtype=np.float64)
-        lse = np.empty((n, num_heads), dtype=np.float64)
+        out = np.empty((n, q_len, num_heads, D_V), dtype=np.float64)
+        lse = np.empty((n, q_len, num_heads), dtype=np.float64)
         rc = self.lib.oracle_mla_attend(
             _ptr(q_bits), _ptr(kv), int(bool(kv_fp8)), float(kv_scale), _ptr(block_table),
-            _ptr(seq_lens), batch, num_heads, block_size, block_table.shape[1], kv.shape[0],
-            float(scale), _ptr(req), _ptr(tok_begin), _ptr(tok_end), n, _ptr(out), _ptr(lse))
+            _ptr(seq_lens), batch, num_heads, q_len, block_size, block_table.shape[1],
+            kv.shape[0], float(scale), _ptr(req), _ptr(tok_begin), _ptr(tok_end), n, _ptr(out),
+            _ptr(lse))
         if rc != 0:
             raise ValueError(f"oracle_mla_attend failed with status {rc}")
+        if not multi:
+            return out[:, 0], lse[:, 0]
         return out, lse
 
     def lse_merge(self, part_out, part_lse):

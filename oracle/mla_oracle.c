@@ -12,6 +12,14 @@
  *    (PR #20769 "SM100 Cutlass MLA decode with unrestricted num_heads (< 128)
  *    for DeepSeek TP", review of ensure_size: max_query_len = 1,
  *    batch_size = num_decodes).
+ *  - Or q_len > 1 query tokens per request, as speculative decoding verifies
+ *    draft tokens (PR #57428, measurement notes: speculative decoding named
+ *    as untested; PR #20769, the same review: the workspace follows
+ *    max_query_len). The pages do not define the mask, so the oracle takes
+ *    the usual causal reading: the q_len new tokens are the last q_len
+ *    positions of the request, already counted in seq_len, and query token
+ *    i (0-based) sees cache tokens 0 .. N - q_len + i. A query token with no
+ *    visible token gets out = 0, lse = -inf.
  *  - The cache is paged: a request's token t lives in physical block
  *    block_table[b][t / block_size], slot t % block_size
  *    (PR #21078 "Flashinfer MLA (trtllm-gen) decode kernel integration",
@@ -93,32 +101,35 @@ static void load_token(const void* kv_cache, int kv_fp8, double kv_scale, int64_
 /*
  * oracle_mla_attend: exact attention of selected (request, token range) items.
  *
- *  q           [batch][num_heads][576] bf16 bits
+ *  q           [batch][q_len][num_heads][576] bf16 bits
  *  kv_cache    [num_blocks][block_size][576] bf16 bits (kv_fp8 = 0) or
  *              E4M3FN codes (kv_fp8 = 1)
  *  kv_scale    per-tensor dequantisation scale for E4M3 (ignored for bf16)
  *  block_table [batch][max_blocks] physical block ids
  *  seq_lens    [batch]
  *  scale       the fp32 logit scale, widened exactly to fp64
+ *  q_len       query tokens per request (>= 1)
  *  items       n_items entries; item i covers request req[i], tokens
- *              [tok_begin[i], tok_end[i]) clipped to [0, seq_lens[req[i]])
- *  out         [n_items][num_heads][512] fp64: sum_t w_t v_t / sum_t w_t
- *  lse         [n_items][num_heads] fp64: natural log of sum_t exp(x_t)
+ *              [tok_begin[i], tok_end[i]) clipped to [0, seq_lens[req[i]]);
+ *              query token qi additionally sees only tokens
+ *              t < seq_lens[req[i]] - (q_len - 1 - qi)
+ *  out         [n_items][q_len][num_heads][512] fp64: sum_t w_t v_t / sum_t w_t
+ *  lse         [n_items][q_len][num_heads] fp64: natural log of sum_t exp(x_t)
  *
- * The work is spread over (item, head) with OpenMP; each (item, head) is a
+ * The work is spread over (item, query token, head) with OpenMP; each is a
  * plain sequential loop, so results do not depend on the thread count.
  */
 int oracle_mla_attend(const uint16_t* q, const void* kv_cache, int kv_fp8, float kv_scale,
                       const int32_t* block_table, const int32_t* seq_lens, int64_t batch,
-                      int64_t num_heads, int64_t block_size, int64_t max_blocks,
-                      int64_t num_blocks, float scale, const int32_t* req,
+                      int64_t num_heads, int64_t q_len, int64_t block_size,
+                      int64_t max_blocks, int64_t num_blocks, float scale, const int32_t* req,
                       const int64_t* tok_begin, const int64_t* tok_end, int64_t n_items,
                       double* out, double* lse) {
   if (!q || !kv_cache || !block_table || !seq_lens || !req || !tok_begin || !tok_end ||
       !out || !lse)
     return ORACLE_BAD_ARG;
-  if (batch < 0 || num_heads < 1 || block_size < 1 || max_blocks < 0 || num_blocks < 0 ||
-      n_items < 0)
+  if (batch < 0 || num_heads < 1 || q_len < 1 || block_size < 1 || max_blocks < 0 ||
+      num_blocks < 0 || n_items < 0)
     return ORACLE_BAD_ARG;
 
   /* Validate every block id that will be read, before any arithmetic. */
@@ -137,24 +148,28 @@ int oracle_mla_attend(const uint16_t* q, const void* kv_cache, int kv_fp8, float
 
   const double s = (double)scale;
   const double kvs = (double)kv_scale;
-  int64_t n_work = n_items * num_heads;
+  int64_t n_work = n_items * q_len * num_heads;
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t w = 0; w < n_work; ++w) {
-    int64_t i = w / num_heads, h = w % num_heads;
+    int64_t i = w / (q_len * num_heads);
+    int64_t qi = (w / num_heads) % q_len, h = w % num_heads;
     int64_t b = req[i];
     int64_t n = seq_lens[b];
+    int64_t visible = n - (q_len - 1 - qi); /* causal: tokens up to query qi's own */
     int64_t t0 = tok_begin[i] < 0 ? 0 : tok_begin[i];
     int64_t t1 = tok_end[i] > n ? n : tok_end[i];
-    double* o = out + (i * num_heads + h) * ORACLE_DV;
+    if (t1 > visible) t1 = visible;
+    int64_t row_out = (i * q_len + qi) * num_heads + h;
+    double* o = out + row_out * ORACLE_DV;
     double qv[ORACLE_D], k[ORACLE_D];
     for (int d = 0; d < ORACLE_DV; ++d) o[d] = 0.0;
     if (t1 <= t0) {
-      lse[i * num_heads + h] = -INFINITY;
+      lse[row_out] = -INFINITY;
       continue;
     }
     for (int d = 0; d < ORACLE_D; ++d)
-      qv[d] = bf16_bits_to_double(q[(b * num_heads + h) * ORACLE_D + d]);
+      qv[d] = bf16_bits_to_double(q[((b * q_len + qi) * num_heads + h) * ORACLE_D + d]);
 
     /* Pass 1: every logit x_t and their maximum. */
     int64_t len = t1 - t0;
@@ -181,7 +196,7 @@ int oracle_mla_attend(const uint16_t* q, const void* kv_cache, int kv_fp8, float
     }
     free(x);
     for (int d = 0; d < ORACLE_DV; ++d) o[d] /= l;
-    lse[i * num_heads + h] = m + log(l);
+    lse[row_out] = m + log(l);
   }
   return ORACLE_OK;
 }
@@ -226,4 +241,4 @@ int oracle_lse_merge(const double* part_out, const double* part_lse, int64_t n_p
   return ORACLE_OK;
 }
 
-int oracle_abi_version(void) { return 1; }
+int oracle_abi_version(void) { return 2; }

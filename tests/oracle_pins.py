@@ -1,7 +1,8 @@
 """Pins that tie the fp64 oracle to facts outside itself.
 
 Each pin checks the oracle against something it does not share code with:
-a library routine (torch's float64 scaled_dot_product_attention and logsumexp,
+a library routine (torch's float64 scaled_dot_product_attention, with its own
+causal mask for several query tokens, and logsumexp,
 torch's float8_e4m3fn and bfloat16 decoders, numpy's logaddexp), a closed form
 of softmax attention, or an invariant the pages fix (split-then-merge equals
 unsplit; zero-padding heads to 128 leaves the real heads alone; a physical
@@ -316,10 +317,83 @@ def pin_fp8_dequant(orc):
         assert _close(lse[b], ref_lse), f"fp8 lse differs (b={b})"
 
 
+def pin_multi_token_causal_sdpa(orc):
+    """q_len query tokens are the last q_len rows of square causal attention over
+    the request: torch's float64 SDPA with is_causal=True (the library's own
+    causal mask) fixes which cache tokens each query token sees. Query tokens
+    with no position in the request (q_len > N) see nothing: out 0, lse -inf."""
+    gen = torch.Generator().manual_seed(14)
+    H, bs = 3, 16
+    for n, q_len in ((1, 1), (5, 2), (40, 4), (77, 7), (3, 5), (33, 33)):
+        k = _bf16(torch.randn((n, 576), generator=gen))
+        q_all = _bf16(torch.randn((n, H, 576), generator=gen))
+        kv, table, seq = _paged_from_dense([k], bs, gen, extra_blocks=1)
+        q = torch.zeros((1, q_len, H, 576), dtype=torch.bfloat16)
+        first = max(0, n - q_len)           # request position of the first real query
+        pad = max(0, q_len - n)             # query tokens before position 0
+        q[0, pad:] = q_all[first:]
+        if pad:
+            q[0, :pad] = _bf16(torch.randn((pad, H, 576), generator=gen))
+        out, lse = orc.attend(_bits(q), _bits(kv), table.numpy(), seq.numpy(), bs, S)
+        qq = q_all.to(torch.float64).permute(1, 0, 2)[None]          # [1, H, n, 576]
+        kk = k.to(torch.float64)[None, None].expand(1, H, -1, -1)
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            qq, kk, kk[..., :512], is_causal=True, scale=S)[0]       # [H, n, 512]
+        logits = S * (qq[0] @ k.to(torch.float64).T)                  # [H, n, n]
+        causal = torch.ones((n, n), dtype=torch.bool).tril()
+        ref_lse = torch.logsumexp(logits.masked_fill(~causal, float("-inf")), -1)  # [H, n]
+        for i in range(q_len):
+            pos = i - pad + first
+            if i < pad:
+                assert (out[0, i] == 0).all() and np.isneginf(lse[0, i]).all(), \
+                    f"query before position 0 must be empty (n={n}, q_len={q_len}, i={i})"
+                continue
+            assert _close(out[0, i], ref[:, pos].numpy()), \
+                f"causal out differs (n={n}, q_len={q_len}, i={i})"
+            assert _close(lse[0, i], ref_lse[:, pos].numpy()), \
+                f"causal lse differs (n={n}, q_len={q_len}, i={i})"
+
+
+def pin_multi_token_rows_are_single_decodes(orc):
+    """Query token i of a paged, ragged, NaN-poisoned batch equals one-token decode
+    of the same request cut to its first N - q_len + 1 + i tokens."""
+    q_len = 3
+    wl = workloads.make_workload(batch=4, num_heads=2, seq=("fixed", [2, 17, 64, 130]),
+                                 block_size=16, seed=15, poison=True, q_len=q_len)
+    args = (wl.kv_bits(), wl.block_table.numpy())
+    out, lse = orc.attend(wl.q_bits(), *args, wl.seq_lens.numpy(), 16, wl.scale)
+    for i in range(q_len):
+        cut = np.maximum(wl.seq_lens.numpy() - (q_len - 1 - i), 0).astype(np.int32)
+        q1 = wl.q[:, i].contiguous()
+        o1, l1 = orc.attend(_bits(q1), *args, cut, 16, wl.scale)
+        assert (out[:, i] == o1).all() and (lse[:, i] == l1).all(), \
+            f"query token {i} differs from a one-token decode of its visible prefix"
+
+
+def pin_multi_token_split_merge(orc):
+    """With q_len query tokens, token ranges merged by LSE equal the unsplit result
+    (a range past a query token's position is empty for it)."""
+    q_len = 4
+    wl = workloads.make_workload(batch=2, num_heads=3, seq=("fixed", [6, 90]), block_size=16,
+                                 seed=16, poison=True, q_len=q_len)
+    args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(),
+            wl.block_size, wl.scale)
+    full_out, full_lse = orc.attend(*args)
+    for b in range(wl.batch):
+        n = int(wl.seq_lens[b])
+        edges = np.array([0, n // 3, n - 2, n - 1, n], np.int64)
+        req = np.full(len(edges) - 1, b, np.int32)
+        po, pl = orc.attend(*args, req=req, tok_begin=edges[:-1], tok_end=edges[1:])
+        mo, ml = orc.lse_merge(po.reshape(len(req), q_len * 3, 512), pl.reshape(len(req), -1))
+        assert _close(mo, full_out[b].reshape(q_len * 3, 512)), f"multi-token split-merge (b={b})"
+        assert _close(ml, full_lse[b].reshape(-1)), f"multi-token split-merge lse (b={b})"
+
+
 PINS = [pin_e4m3_decode, pin_bf16_widen, pin_sdpa_identity_table, pin_sdpa_shuffled_pages,
         pin_closed_forms, pin_empty_request, pin_split_merge, pin_merge_closed_form,
         pin_rope_shift, pin_head_padding, pin_block_permutation, pin_batch_independence,
-        pin_fp8_dequant]
+        pin_fp8_dequant, pin_multi_token_causal_sdpa, pin_multi_token_rows_are_single_decodes,
+        pin_multi_token_split_merge]
 
 
 def main(argv=None) -> int:

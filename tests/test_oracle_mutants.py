@@ -26,18 +26,27 @@ MUTANTS = [
     ("values_from_rope_side", "o[d] += wt * k[d];", "o[d] += wt * k[d + 64];"),
     ("scale_dropped", "x[t - t0] = s * dot;", "x[t - t0] = dot;"),
     ("weight_sign", "exp(x[t - t0] - m)", "exp(m - x[t - t0])"),
-    ("lse_log2", "lse[i * num_heads + h] = m + log(l);", "lse[i * num_heads + h] = m + log2(l);"),
-    ("lse_missing_max", "lse[i * num_heads + h] = m + log(l);", "lse[i * num_heads + h] = log(l);"),
+    ("lse_log2", "lse[row_out] = m + log(l);", "lse[row_out] = m + log2(l);"),
+    ("lse_missing_max", "lse[row_out] = m + log(l);", "lse[row_out] = log(l);"),
     ("no_normalise", "for (int d = 0; d < ORACLE_DV; ++d) o[d] /= l;", ""),
-    ("q_head_batch_transposed", "q[(b * num_heads + h) * ORACLE_D + d]",
-     "q[((h % batch) * num_heads + (b % num_heads)) * ORACLE_D + d]"),
+    ("q_head_batch_transposed", "q[((b * q_len + qi) * num_heads + h) * ORACLE_D + d]",
+     "q[(((h % batch) * q_len + qi) * num_heads + (b % num_heads)) * ORACLE_D + d]"),
+    ("q_token_head_transposed", "q[((b * q_len + qi) * num_heads + h) * ORACLE_D + d]",
+     "q[((b * num_heads + h) * q_len + qi) * ORACLE_D + d]"),
+    ("causal_off_by_one", "int64_t visible = n - (q_len - 1 - qi);",
+     "int64_t visible = n - (q_len - qi);"),
+    ("causal_reversed", "int64_t visible = n - (q_len - 1 - qi);",
+     "int64_t visible = n - qi;"),
+    ("causal_ignored", "if (t1 > visible) t1 = visible;", ""),
+    ("out_row_token_head_transposed", "int64_t row_out = (i * q_len + qi) * num_heads + h;",
+     "int64_t row_out = (i * num_heads + h) * q_len + qi;"),
     ("e4m3_bias", "exponent - 7);", "exponent - 8);"),
     ("e4m3_subnormal", "ldexp((double)mantissa / 8.0, -6)", "ldexp((double)mantissa / 8.0, -7)"),
     ("kv_scale_dropped", "oracle_e4m3_to_double(p[d]) * kv_scale;", "oracle_e4m3_to_double(p[d]);"),
     ("merge_weight_sign", "double w = exp(ls - M);", "double w = exp(M - ls);"),
     ("merge_unnormalised", "for (int d = 0; d < ORACLE_DV; ++d) o[d] /= wsum;", ""),
-    ("tail_overread", "int64_t t1 = tok_end[i] > n ? n : tok_end[i];\n    double* o",
-     "int64_t t1 = tok_end[i] > n ? n : tok_end[i];\n    if (t1 == n && t1 % block_size) t1 = (t1 / block_size + 1) * block_size;\n    double* o"),
+    ("tail_overread", "if (t1 > visible) t1 = visible;\n    int64_t row_out",
+     "if (t1 > visible) t1 = visible;\n    if (t1 == n && t1 % block_size) t1 = (t1 / block_size + 1) * block_size;\n    int64_t row_out"),
 ]
 
 

@@ -7,7 +7,9 @@ order: sequence lengths, then the physical block permutation, then q, then the
 KV pool.
 
 Shapes follow the decode workloads described by the pages:
-  * one query token per request (PR #20769, review of ensure_size);
+  * one query token per request (PR #20769, review of ensure_size), or q_len
+    tokens per request as in speculative decoding (q [B, q_len, H, 576]; the
+    new tokens are the last q_len positions counted in seq_lens);
   * a paged cache addressed through a per-request block table with block sizes
     of 16 to 128 tokens (PR #21078 E2E command uses --block-size 32);
   * 576-wide latent rows (512 kv_c + 64 rope) shared by all heads;
@@ -55,7 +57,7 @@ CONFIGS = {
 @dataclasses.dataclass
 class Workload:
     name: str
-    q: torch.Tensor            # [B, H, 576] bf16
+    q: torch.Tensor            # [B, H, 576] bf16, or [B, q_len, H, 576]
     kv: torch.Tensor           # [NB, bs, 576] bf16, or uint8 E4M3FN codes
     block_table: torch.Tensor  # [B, max_blocks] int32, -1 past each request's blocks
     seq_lens: torch.Tensor     # [B] int32
@@ -70,7 +72,11 @@ class Workload:
 
     @property
     def num_heads(self) -> int:
-        return self.q.shape[1]
+        return self.q.shape[-2]
+
+    @property
+    def q_len(self) -> int:
+        return 1 if self.q.dim() == 3 else self.q.shape[1]
 
     @property
     def num_blocks(self) -> int:
@@ -125,10 +131,12 @@ def _randn_bf16(gen: torch.Generator, n_rows: int, chunk_rows: int = 1 << 15) ->
 
 def make_workload(name: str = "custom", *, batch: int, num_heads: int, seq, block_size: int,
                   seed: int, kv_dtype: str = "bf16", pool_blocks: int | None = None,
-                  poison: bool = False) -> Workload:
+                  poison: bool = False, q_len: int = 1) -> Workload:
     """Draw one workload.
 
     seq          ("fixed", list) | ("uniform", lo, hi) | ("loguniform", lo, hi)
+    q_len        query tokens per request; q is [B, H, 576] for 1, else
+                 [B, q_len, H, 576] (the same draw order either way)
     pool_blocks  physical pool size (default: exactly the blocks the requests use)
     poison       put NaN in unused blocks and in tail slots past each seq_len
     """
@@ -146,8 +154,8 @@ def make_workload(name: str = "custom", *, batch: int, num_heads: int, seq, bloc
     for b, k in enumerate(nblk):
         table[b, :k] = perm[off:off + k]
         off += k
-    q = torch.randn((batch, num_heads, D_K), generator=gen, dtype=torch.float32).to(
-        torch.bfloat16)
+    q_shape = (batch, num_heads, D_K) if q_len == 1 else (batch, q_len, num_heads, D_K)
+    q = torch.randn(q_shape, generator=gen, dtype=torch.float32).to(torch.bfloat16)
     if kv_dtype == "bf16":
         kv = _randn_bf16(gen, pool * block_size).view(pool, block_size, D_K)
         kv_scale = 1.0
