@@ -71,14 +71,17 @@ def algorithmic_bytes(wl) -> int:
     e_kv = 1 if wl.kv_dtype == "fp8" else 2
     n_tok = wl.total_tokens
     nblk = sum((int(n) + wl.block_size - 1) // wl.block_size for n in wl.seq_lens)
-    b, h = wl.batch, wl.num_heads
+    b, h = wl.batch, wl.num_heads * wl.q_len   # query rows per request
     return (n_tok * D_K * e_kv + b * h * D_K * 2 + b * h * D_V * 2 + b * h * 4 + nblk * 4
             + b * 4)
 
 
 def algorithmic_flops(wl) -> int:
-    """Logits (2 * 576) and P.V (2 * 512) multiply-adds per head and token."""
-    return 2 * (D_K + D_V) * wl.num_heads * wl.total_tokens
+    """Logits (2 * 576) and P.V (2 * 512) multiply-adds per head and visible
+    token: query token i of q_len sees N - q_len + 1 + i of a request's N."""
+    visible = sum(max(0, int(n) - wl.q_len + 1 + i) for n in wl.seq_lens
+                  for i in range(wl.q_len))
+    return 2 * (D_K + D_V) * wl.num_heads * visible
 
 
 def cpu_baseline(wl, target_s: float) -> dict:
@@ -143,6 +146,8 @@ def main(argv=None) -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="r1tp8")
     ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--q-len", type=int, default=1,
+                    help="query tokens per request (speculative decoding, causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -170,17 +175,18 @@ def main(argv=None) -> int:
         return calib_copy(torch, dev, args.calib_copy << 20, max(args.steps, 1))
     mla.library()  # fail loudly now if the HIP library is missing
 
-    log(f"generating workload {args.config}")
-    wl = workloads.make_config(args.config)
+    label = args.config if args.q_len == 1 else f"{args.config}-q{args.q_len}"
+    log(f"generating workload {label}")
+    wl = workloads.make_config(args.config, q_len=args.q_len)
     cfg = workloads.CONFIGS[args.config]
     pool_bytes = wl.kv.numel() * wl.kv.element_size()
     copies = 1 if pool_bytes >= 2 * MALL_BYTES else max(4, math.ceil(ROTATE_MIN_BYTES / pool_bytes))
     q, bt, sl = wl.q.to(dev), wl.block_table.to(dev), wl.seq_lens.to(dev)
     kvs = [wl.kv.to(dev) for _ in range(copies)]
-    out = torch.empty((wl.batch, wl.num_heads, D_V), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((wl.batch, wl.num_heads), dtype=torch.float32, device=dev)
+    out = torch.empty(tuple(wl.q.shape[:-1]) + (D_V,), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty(tuple(wl.q.shape[:-1]), dtype=torch.float32, device=dev)
     nbytes = mla.get_workspace_size(wl.batch, wl.num_heads, wl.max_blocks * wl.block_size,
-                                    args.num_splits, 0)
+                                    args.num_splits, 0, q_len=wl.q_len)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     log(f"tokens={wl.total_tokens} pool={pool_bytes / 2**20:.0f} MiB copies={copies} "
@@ -230,10 +236,10 @@ def main(argv=None) -> int:
     alg_flops = algorithmic_flops(wl)
     achieved = alg_bytes / (attn_avg * 1e-3) / 1e9
     mfma_peak = PEAK_MFMA_TFLOPS["fp8" if wl.kv_dtype == "fp8" else "bf16"]
-    traffic = measured_traffic(args.config, kernel_source_hash())
+    traffic = measured_traffic(label, kernel_source_hash())
     if wl.kv_dtype == "fp8":
         kernel_name = "mla::attn_mh_kernel<1>"
-    elif wl.num_heads <= 16:
+    elif wl.num_heads * wl.q_len <= 16:
         kernel_name = "mla::attn_ws_kernel"
     else:
         kernel_name = "mla::attn_mh_kernel<0>"
@@ -269,7 +275,8 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "fp8" if wl.kv_dtype == "fp8" else "bf16",
         "data": "synthetic",
-        "config": {"workload": args.config, "batch": wl.batch, "num_heads": wl.num_heads,
+        "config": {"workload": label, "batch": wl.batch, "num_heads": wl.num_heads,
+                   "q_len": wl.q_len,
                    "seq_lens": list(cfg["seq"]) if cfg["seq"][0] != "fixed" else
                    sorted(set(cfg["seq"][1])), "total_tokens": wl.total_tokens,
                    "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,

@@ -20,6 +20,8 @@
  * multiple blocks/SMs plus a reduction kernel that combines the results).
  * Any head count 1..128 is accepted (PR #20769: num_heads below 128 is what
  * lets tensor parallelism shard heads); no padding to 128 is required.
+ * mla_decode_multi_token takes several query tokens per request under a
+ * causal mask (speculative decoding; see its comment).
  *
  * Conventions shared by every entry point:
  *  - All data pointers are caller-owned DEVICE memory on the current HIP
@@ -50,6 +52,7 @@ extern "C" {
 #define MLA_HEAD_DIM_K 576   /* key width: 512 kv_c + 64 rope */
 #define MLA_HEAD_DIM_V 512   /* value width: kv_c */
 #define MLA_MAX_HEADS 128
+#define MLA_MAX_QUERY_LEN 16   /* query tokens per request (mla_decode_multi_token) */
 #define MLA_MAX_FORCED_SPLITS 16
 
 typedef enum {
@@ -82,6 +85,15 @@ typedef enum {
  */
 size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_len,
                               int64_t num_splits, int64_t num_cus);
+
+/*
+ * Workspace bytes that mla_decode_multi_token needs: as mla_get_workspace_size
+ * with q_len (1..16) query tokens per request. q_len = 1 gives the same value
+ * as mla_get_workspace_size.
+ */
+size_t mla_get_workspace_size_multi_token(int64_t batch, int64_t num_heads, int64_t q_len,
+                                          int64_t max_seq_len, int64_t num_splits,
+                                          int64_t num_cus);
 
 /*
  * mla_decode: out, lse <- attention of q over the paged cache (formula above).
@@ -117,8 +129,8 @@ size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_
  *  kv_scale     per-tensor dequantisation scale: exactly 1.0 for MLA_KV_BF16,
  *               finite and > 0 for MLA_KV_FP8_E4M3. In the fp8 path q is
  *               quantised inside the kernel into two E4M3 rows per (request,
- *               head) (the rounded row and its scaled rounding residual, each
- *               with its own amax / 448 scale), P * 2^8 is carried the same
+ *               head): the rounded row and its rounding residual, both in
+ *               the row's one scale amax / 448; P * 2^8 is carried the same
  *               way as two E4M3 terms, and both products run on fp8 matrix
  *               cores.
  *  workspace    caller-owned device scratch of at least workspace_bytes,
@@ -139,23 +151,56 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
                         size_t workspace_bytes, void* stream);
 
 /*
- * mla_decode_profiled: exactly mla_decode, and additionally records the four
- * caller-created hipEvent_t handles in events[0..3] on `stream`: before the
- * split-plan kernel, before the attention kernel, after the attention kernel
- * and after the combine kernel. Used to time the attention kernel alone.
- * events must be non-NULL with four non-NULL entries.
+ * mla_decode_multi_token: q_len query tokens per request, as speculative
+ * decoding verifies draft tokens (PR #57428, measurement notes: speculative
+ * decoding named as not measured; PR #20769, review of ensure_size: the
+ * decode workspace follows max_query_len). The pages leave the mask open;
+ * this library takes the causal reading: the q_len new tokens are the last
+ * q_len positions of the request, already in the cache and counted in
+ * seq_lens[b] = N, and query token i (0-based) attends to cache tokens
+ * 0 .. N - q_len + i. A query token that sees no token (N - q_len + i < 0)
+ * gets out = 0, lse = -inf.
+ *
+ *  q            [batch][q_len][num_heads][576] bf16, contiguous, 16-byte aligned
+ *  out          [batch][q_len][num_heads][512] bf16, 16-byte aligned
+ *  lse          [batch][q_len][num_heads] fp32, or NULL
+ *  q_len        1..16; num_heads 1..128 as for mla_decode
+ *  workspace_bytes  >= mla_get_workspace_size_multi_token(batch, num_heads,
+ *               q_len, max_blocks_per_seq * block_size, num_splits, <CUs>)
+ *               (automatic mode again accepts less, with fewer partitions)
+ *
+ * Every other argument, the error behaviour and the ownership rules are
+ * those of mla_decode; q_len = 1 is exactly mla_decode. All q_len * num_heads
+ * query rows of a request share each cached token read.
+ */
+mla_status_t mla_decode_multi_token(const void* q, const void* kv_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    void* out, float* lse, float scale, int32_t num_heads,
+                                    int32_t q_len, int32_t block_size, int32_t num_splits,
+                                    int32_t batch, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, int32_t kv_dtype, float kv_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_profiled: exactly mla_decode_multi_token, and additionally
+ * records the four caller-created hipEvent_t handles in events[0..3] on
+ * `stream`: before the split-plan kernel, before the attention kernel, after
+ * the attention kernel and after the combine kernel. Used to time the
+ * attention kernel alone. events must be non-NULL with four non-NULL entries.
  */
 mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  void* out, float* lse, float scale, int32_t num_heads,
-                                 int32_t block_size, int32_t num_splits, int32_t batch,
-                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t q_len, int32_t block_size, int32_t num_splits,
+                                 int32_t batch, int32_t max_blocks_per_seq, int32_t num_blocks,
                                  int32_t kv_dtype, float kv_scale, void* workspace,
                                  size_t workspace_bytes, void* stream, void* const* events);
 
 /*
  * mla_combine: merge normalised split partials by log-sum-exp (PR #20769,
  * summary of changes: the reduction kernel that combines split-KV results).
+ * num_heads counts the rows of one request: the heads, or q_len * heads for
+ * partials of several query tokens (1..2048).
  *
  *  partial_out  [total_rows][num_heads][512] fp32, each row already divided
  *               by its own softmax denominator, 16-byte aligned

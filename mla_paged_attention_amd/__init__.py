@@ -13,6 +13,7 @@ from ._binding import (  # noqa: F401
     LIBRARY_PATH,
     MAX_FORCED_SPLITS,
     MAX_HEADS,
+    MAX_QUERY_LEN,
     MLA_ERR_HIP,
     MLA_ERR_INVALID_ARG,
     MLA_ERR_NO_DEVICE,

@@ -20,6 +20,7 @@ LIBRARY_PATH = os.path.join(HERE, "libmla_mi355x.so")
 HEAD_DIM_K = 576
 HEAD_DIM_V = 512
 MAX_HEADS = 128
+MAX_QUERY_LEN = 16
 MAX_FORCED_SPLITS = 16
 BLOCK_SIZES = (16, 32, 64, 128)
 
@@ -33,7 +34,8 @@ MLA_ERR_HIP = -5
 MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 
-EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_decode", "mla_decode_profiled",
+EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_get_workspace_size_multi_token",
+                    "mla_decode", "mla_decode_multi_token", "mla_decode_profiled",
                     "mla_combine", "mla_status_string", "mla_abi_version")
 
 _lib = None
@@ -51,11 +53,16 @@ def _bind(lib: ctypes.CDLL) -> None:
                              ctypes.c_size_t)
     lib.mla_get_workspace_size.argtypes = [i64, i64, i64, i64, i64]
     lib.mla_get_workspace_size.restype = sz
+    lib.mla_get_workspace_size_multi_token.argtypes = [i64, i64, i64, i64, i64, i64]
+    lib.mla_get_workspace_size_multi_token.restype = sz
     decode_args = [vp, vp, vp, vp, vp, vp, f32, i32, i32, i32, i32, i32, i32, i32, f32, vp, sz,
                    vp]
     lib.mla_decode.argtypes = decode_args
     lib.mla_decode.restype = i32
-    lib.mla_decode_profiled.argtypes = decode_args + [ctypes.POINTER(vp)]
+    multi_args = decode_args[:8] + [i32] + decode_args[8:]   # q_len after num_heads
+    lib.mla_decode_multi_token.argtypes = multi_args
+    lib.mla_decode_multi_token.restype = i32
+    lib.mla_decode_profiled.argtypes = multi_args + [ctypes.POINTER(vp)]
     lib.mla_decode_profiled.restype = i32
     lib.mla_combine.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp]
     lib.mla_combine.restype = i32
@@ -89,9 +96,12 @@ def abi_version() -> int:
 
 
 def get_workspace_size(batch: int, num_heads: int, max_seq_len: int, num_splits: int = 0,
-                       num_cus: int = 0) -> int:
-    return int(library().mla_get_workspace_size(batch, num_heads, max_seq_len, num_splits,
-                                                num_cus))
+                       num_cus: int = 0, q_len: int = 1) -> int:
+    if q_len == 1:
+        return int(library().mla_get_workspace_size(batch, num_heads, max_seq_len, num_splits,
+                                                    num_cus))
+    return int(library().mla_get_workspace_size_multi_token(batch, num_heads, q_len,
+                                                            max_seq_len, num_splits, num_cus))
 
 
 def _ptr(t) -> ctypes.c_void_p:
@@ -133,18 +143,22 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
            workspace: torch.Tensor | None = None, stream=None, events=None):
     """Absorbed MLA decode over a paged cache (see include/mla.h, mla_decode).
 
-    q [B, H, 576] bf16; kv_cache [num_blocks, block_size, 576] bf16 or E4M3
-    (uint8 / float8_e4m3fn) with per-tensor kv_scale; block_table [B, max_blocks]
-    int32; seq_lens [B] int32. Returns (out [B, H, 512] bf16, lse [B, H] fp32 or
-    None). `events`: four torch.cuda.Event(enable_timing=True) to record around
-    the split plan, attention and combine kernels (mla_decode_profiled).
+    q [B, H, 576] bf16, or [B, q_len, H, 576] for q_len query tokens per request
+    under the causal mask of mla_decode_multi_token; kv_cache [num_blocks,
+    block_size, 576] bf16 or E4M3 (uint8 / float8_e4m3fn) with per-tensor
+    kv_scale; block_table [B, max_blocks] int32; seq_lens [B] int32. Returns
+    (out [B, (q_len,) H, 512] bf16, lse [B, (q_len,) H] fp32 or None).
+    `events`: four torch.cuda.Event(enable_timing=True) to record around the
+    split plan, attention and combine kernels (mla_decode_profiled).
     """
-    if q.dim() != 3 or q.shape[2] != HEAD_DIM_K or q.dtype != torch.bfloat16:
-        raise ValueError("q must be [batch, num_heads, 576] bf16")
+    if q.dim() not in (3, 4) or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise ValueError("q must be [batch, num_heads, 576] or [batch, q_len, num_heads, 576] "
+                         "bf16")
     if kv_cache.dim() != 3 or kv_cache.shape[2] != HEAD_DIM_K:
         raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
     kv_dtype = _kv_dtype(kv_cache)
-    batch, num_heads, _ = q.shape
+    batch, num_heads = q.shape[0], q.shape[-2]
+    q_len = q.shape[1] if q.dim() == 4 else 1
     num_blocks, block_size, _ = kv_cache.shape
     if block_table.dim() != 2 or block_table.shape[0] != batch or block_table.dtype != torch.int32:
         raise ValueError("block_table must be [batch, max_blocks] int32")
@@ -155,28 +169,41 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
                     ("seq_lens", seq_lens)):
         if t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on {dev}")
+    lead = tuple(q.shape[:-1])                     # (B, H) or (B, q_len, H)
     if out is None:
-        out = torch.empty((batch, num_heads, HEAD_DIM_V), dtype=torch.bfloat16, device=dev)
+        out = torch.empty(lead + (HEAD_DIM_V,), dtype=torch.bfloat16, device=dev)
+    elif tuple(out.shape) != lead + (HEAD_DIM_V,) or out.dtype != torch.bfloat16 or \
+            out.device != dev or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous {lead + (HEAD_DIM_V,)} bf16 on {dev}")
     if lse is True:
-        lse = torch.empty((batch, num_heads), dtype=torch.float32, device=dev)
+        lse = torch.empty(lead, dtype=torch.float32, device=dev)
     elif lse is False:
         lse = None
+    elif lse is not None and (tuple(lse.shape) != lead or lse.dtype != torch.float32 or
+                              lse.device != dev or not lse.is_contiguous()):
+        raise ValueError(f"lse must be contiguous {lead} fp32 on {dev}")
     max_blocks = block_table.shape[1]
-    need = get_workspace_size(batch, num_heads, max_blocks * block_size, num_splits, 0)
+    need = get_workspace_size(batch, num_heads, max_blocks * block_size, num_splits, 0, q_len)
     if workspace is None:
         workspace = workspace_for(dev, stream, need)
-    args = (_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
-            float(scale), num_heads, block_size, num_splits, batch, max_blocks, num_blocks,
-            kv_dtype, float(kv_scale), _ptr(workspace), workspace.numel() * workspace.element_size(),
+    head = (_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+            float(scale), num_heads)
+    tail = (block_size, num_splits, batch, max_blocks, num_blocks, kv_dtype, float(kv_scale),
+            _ptr(workspace), workspace.numel() * workspace.element_size(),
             _stream_handle(stream))
     lib = library()
-    if events is None:
-        st = lib.mla_decode(*args)
-    else:
+    if events is not None:
         arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
-        st = lib.mla_decode_profiled(*args, arr)
+        st = lib.mla_decode_profiled(*head, q_len, *tail, arr)
+        what = "mla_decode_profiled"
+    elif q_len == 1 and q.dim() == 3:
+        st = lib.mla_decode(*head, *tail)
+        what = "mla_decode"
+    else:
+        st = lib.mla_decode_multi_token(*head, q_len, *tail)
+        what = "mla_decode_multi_token"
     if st != MLA_OK:
-        raise MLAError(st, "mla_decode")
+        raise MLAError(st, what)
     return out, lse
 
 

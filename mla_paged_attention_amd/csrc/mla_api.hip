@@ -82,16 +82,19 @@ struct DecodeArgs {
   void* out;
   float* lse;
   float scale;
-  int32_t num_heads, block_size, num_splits, batch, max_blocks, num_blocks, kv_dtype;
+  int32_t num_heads, q_len, block_size, num_splits, batch, max_blocks, num_blocks, kv_dtype;
   float kv_scale;
   void* workspace;
   size_t workspace_bytes;
   hipStream_t stream;
+
+  int32_t rows() const { return num_heads * q_len; }  // query rows per request
 };
 
 mla_status_t validate_decode(const DecodeArgs& a) {
   if (a.batch < 0) return MLA_ERR_INVALID_ARG;
   if (a.num_heads < 1 || a.num_heads > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (a.q_len < 1 || a.q_len > MLA_MAX_QUERY_LEN) return MLA_ERR_INVALID_ARG;
   if (bs_log2_of(a.block_size) < 0) return MLA_ERR_INVALID_ARG;
   if (a.num_splits < 0 || a.num_splits > MLA_MAX_FORCED_SPLITS) return MLA_ERR_INVALID_ARG;
   if (a.max_blocks < 1 || a.num_blocks < 1) return MLA_ERR_INVALID_ARG;
@@ -114,11 +117,17 @@ mla_status_t validate_decode(const DecodeArgs& a) {
     return MLA_ERR_INVALID_ARG;
   if (a.lse && !aligned(a.lse, 4)) return MLA_ERR_INVALID_ARG;
   // Metadata alone must fit whatever the mode.
-  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.num_heads, 0, 1).total)
+  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.rows(), 0, 1).total)
     return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (a.num_splits > 0) {
+    // One workgroup per (request, split, 16-row tile) and per (request, tile,
+    // 64-feature chunk) of the combine: grids stay within 2^31 - 1.
+    const int64_t tiles = mla::head_tiles(a.rows());
+    if (int64_t(a.batch) * a.num_splits * tiles > INT32_MAX ||
+        int64_t(a.batch) * tiles * (MLA_HEAD_DIM_V / 64) > INT32_MAX)
+      return MLA_ERR_INVALID_ARG;
     WorkspaceLayout w =
-        mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits), 1);
+        mla::workspace_layout(a.batch, a.rows(), forced_rows(a.batch, a.num_splits), 1);
     if (a.workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
   return MLA_OK;
@@ -138,13 +147,14 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   const int64_t cap = int64_t(a.max_blocks) * a.block_size;
   WorkspaceLayout w;
   int64_t max_parts = 0;
+  const int32_t rows = a.rows();
   if (a.num_splits > 0) {
-    w = mla::workspace_layout(a.batch, a.num_heads, forced_rows(a.batch, a.num_splits), 1);
+    w = mla::workspace_layout(a.batch, rows, forced_rows(a.batch, a.num_splits), 1);
   } else {
     // Largest partition count whose plan and partial rows fit the workspace.
-    max_parts = mla::max_partitions(dev.cus, a.num_heads, a.kv_dtype == MLA_KV_FP8_E4M3);
+    max_parts = mla::max_partitions(dev.cus, rows, a.kv_dtype == MLA_KV_FP8_E4M3);
     auto layout = [&](int64_t parts) {
-      return mla::workspace_layout(a.batch, a.num_heads, auto_rows(a.batch, parts, cap), parts);
+      return mla::workspace_layout(a.batch, rows, auto_rows(a.batch, parts, cap), parts);
     };
     while (max_parts > 1 && layout(max_parts).total > a.workspace_bytes)
       max_parts = max_parts * 3 / 4;
@@ -186,7 +196,9 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.row_ptr = row_ptr;
   args.scale_log2 = a.scale * 1.4426950408889634f;
   args.kv_scale = a.kv_scale;
-  args.num_heads = a.num_heads;
+  args.rows = rows;
+  args.heads = a.num_heads;
+  args.q_len = a.q_len;
   args.batch = a.batch;
   args.max_blocks = a.max_blocks;
   args.num_blocks = a.num_blocks;
@@ -196,7 +208,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.parts_cap = int32_t(max_parts);
   args.items_cap = int32_t(a.batch + max_parts);
   args.rows_cap = int32_t(w.rows);
-  args.head_tiles = mla::head_tiles(a.num_heads);
+  args.head_tiles = mla::head_tiles(rows);
   args.head_groups = (args.head_tiles + 3) / 4;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
   int64_t parts_launched = (parts + 7) / 8 * 8;
@@ -208,7 +220,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
 
   if (a.num_splits > 1) {
     if (mla::launch_combine(part_out, part_lse, row_ptr, static_cast<uint16_t*>(a.out), a.lse,
-                            a.batch, a.num_heads, 0, s) != hipSuccess)
+                            a.batch, rows, 0, s) != hipSuccess)
       return MLA_ERR_HIP;
   } else if (a.num_splits == 0 && max_parts > 1 && w.rows > 0) {
     // Split requests are fewer than the partitions (each is costlier than
@@ -216,7 +228,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
     const int64_t max_split = a.batch < max_parts ? a.batch : max_parts;
     if (mla::launch_combine_split(part_out, part_lse, row_ptr, split, header,
                                   static_cast<uint16_t*>(a.out), a.lse, int32_t(max_split),
-                                  a.num_heads, s) != hipSuccess)
+                                  rows, s) != hipSuccess)
       return MLA_ERR_HIP;
   }
   if (!rec(3)) return MLA_ERR_HIP;
@@ -227,18 +239,39 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
 
 extern "C" {
 
-size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_len,
-                              int64_t num_splits, int64_t num_cus) {
+size_t mla_get_workspace_size_multi_token(int64_t batch, int64_t num_heads, int64_t q_len,
+                                          int64_t max_seq_len, int64_t num_splits,
+                                          int64_t num_cus) {
   if (batch < 0 || batch > INT32_MAX / 2) return 0;
   if (num_heads < 1 || num_heads > MLA_MAX_HEADS) return 0;
+  if (q_len < 1 || q_len > MLA_MAX_QUERY_LEN) return 0;
   if (max_seq_len < 0 || max_seq_len > INT32_MAX / 2) return 0;
   if (num_splits < 0 || num_splits > MLA_MAX_FORCED_SPLITS) return 0;
   if (num_cus <= 0) num_cus = kDefaultCus;
+  const int64_t rows = num_heads * q_len;
   if (num_splits > 0)
-    return mla::workspace_layout(batch, num_heads, forced_rows(batch, num_splits), 1).total;
-  const int64_t parts = mla::max_partitions(num_cus, num_heads, 0);
-  return mla::workspace_layout(batch, num_heads, auto_rows(batch, parts, max_seq_len), parts)
-      .total;
+    return mla::workspace_layout(batch, rows, forced_rows(batch, num_splits), 1).total;
+  const int64_t parts = mla::max_partitions(num_cus, rows, 0);
+  return mla::workspace_layout(batch, rows, auto_rows(batch, parts, max_seq_len), parts).total;
+}
+
+size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_len,
+                              int64_t num_splits, int64_t num_cus) {
+  return mla_get_workspace_size_multi_token(batch, num_heads, 1, max_seq_len, num_splits,
+                                            num_cus);
+}
+
+mla_status_t mla_decode_multi_token(const void* q, const void* kv_cache,
+                                    const int32_t* block_table, const int32_t* seq_lens,
+                                    void* out, float* lse, float scale, int32_t num_heads,
+                                    int32_t q_len, int32_t block_size, int32_t num_splits,
+                                    int32_t batch, int32_t max_blocks_per_seq,
+                                    int32_t num_blocks, int32_t kv_dtype, float kv_scale,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, q_len,
+               block_size, num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype,
+               kv_scale, workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  return run_decode(a, nullptr);
 }
 
 mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* block_table,
@@ -247,30 +280,33 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
                         int32_t batch, int32_t max_blocks_per_seq, int32_t num_blocks,
                         int32_t kv_dtype, float kv_scale, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, block_size,
-               num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype, kv_scale,
-               workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
-  return run_decode(a, nullptr);
+  return mla_decode_multi_token(q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads,
+                                1, block_size, num_splits, batch, max_blocks_per_seq,
+                                num_blocks, kv_dtype, kv_scale, workspace, workspace_bytes,
+                                stream);
 }
 
 mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
                                  const int32_t* block_table, const int32_t* seq_lens,
                                  void* out, float* lse, float scale, int32_t num_heads,
-                                 int32_t block_size, int32_t num_splits, int32_t batch,
-                                 int32_t max_blocks_per_seq, int32_t num_blocks,
+                                 int32_t q_len, int32_t block_size, int32_t num_splits,
+                                 int32_t batch, int32_t max_blocks_per_seq, int32_t num_blocks,
                                  int32_t kv_dtype, float kv_scale, void* workspace,
                                  size_t workspace_bytes, void* stream, void* const* events) {
   if (!events) return MLA_ERR_INVALID_ARG;
-  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, block_size,
-               num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype, kv_scale,
-               workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, q_len,
+               block_size, num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype,
+               kv_scale, workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
   return run_decode(a, events);
 }
 
 mla_status_t mla_combine(const float* partial_out, const float* partial_lse,
                          const int32_t* split_indptr, void* out, float* lse, int32_t batch,
                          int32_t num_heads, void* stream) {
-  if (batch < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS) return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || num_heads < 1 || num_heads > MLA_MAX_HEADS * MLA_MAX_QUERY_LEN)
+    return MLA_ERR_INVALID_ARG;
+  if (int64_t(batch) * mla::head_tiles(num_heads) * (MLA_HEAD_DIM_V / 64) > INT32_MAX)
+    return MLA_ERR_INVALID_ARG;
   if (batch > 0) {
     if (!partial_out || !partial_lse || !split_indptr || !out) return MLA_ERR_INVALID_ARG;
     if (!aligned(partial_out, 16) || !aligned(partial_lse, 4) || !aligned(split_indptr, 4) ||
@@ -301,6 +337,6 @@ const char* mla_status_string(int32_t status) {
   }
 }
 
-int32_t mla_abi_version(void) { return 1; }
+int32_t mla_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -84,13 +84,17 @@ inline int64_t max_partitions(int64_t num_cus, int64_t num_heads, int kv_fp8) {
   return g < 8 ? 8 : g;
 }
 
+// Query rows: a request's q holds q_len query tokens of `heads` heads each,
+// row r = token (r / heads), head (r % heads); the kernels work on
+// rows = q_len * heads rows per request, and query token i sees the first
+// seq_len - (q_len - 1 - i) cache tokens.
 struct AttnArgs {
-  const uint16_t* q;         // [B][H][576] bf16 bits
+  const uint16_t* q;         // [B][rows][576] bf16 bits
   const uint8_t* kv;         // [NB][bs][576] bf16 or e4m3 bytes
   const int32_t* block_table;
   const int32_t* seq_lens;
-  uint16_t* out;             // [B][H][512] bf16 bits
-  float* lse;                // [B][H] or null
+  uint16_t* out;             // [B][rows][512] bf16 bits
+  float* lse;                // [B][rows] or null
   float* part_out;
   float* part_lse;
   const int32_t* header;
@@ -99,7 +103,9 @@ struct AttnArgs {
   const int32_t* row_ptr;
   float scale_log2;          // logit scale * log2(e)
   float kv_scale;            // fp8 dequantisation scale (1 for bf16)
-  int32_t num_heads;
+  int32_t rows;              // q_len * heads
+  int32_t heads;             // heads per query token
+  int32_t q_len;             // query tokens per request
   int32_t batch;
   int32_t max_blocks;
   int32_t num_blocks;
@@ -109,7 +115,7 @@ struct AttnArgs {
   int32_t parts_cap;         // automatic plan: partitions in part_ptr
   int32_t items_cap;         // automatic plan: entries of work
   int32_t rows_cap;          // partial rows in part_out / part_lse
-  int32_t head_tiles;        // ceil(num_heads / 16)
+  int32_t head_tiles;        // ceil(rows / 16)
   int32_t head_groups;       // workgroups per partition of the many-head kernel
 };
 

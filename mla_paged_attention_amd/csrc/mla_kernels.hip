@@ -590,13 +590,16 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
   const int wave = tid >> 6, lane = tid & 63;
   const int c = lane & 15, g = lane >> 4;
   const bool logit_wave = wave == kPvWaves;
-  const int H = a.num_heads;
+  const int H = a.rows;
 
   const int lin = blockIdx.x;
   const int xcd = lin & 7, slot = lin >> 3;
   const int ht = slot % a.head_tiles;
   const int part = (slot / a.head_tiles) * 8 + xcd;
   const int h0 = ht * kHeadTile;
+  // Logit wave: row h0 + c belongs to query token (h0 + c) / heads, which sees
+  // all but the last `back` tokens of the request.
+  const int back = a.q_len - 1 - min(h0 + c, H - 1) / a.heads;
 
   // Per-thread DMA map of the P.V waves: load i fills ring slot i * 256 + tid.
   uint32_t dma_off[kDmaPerThread];
@@ -673,9 +676,11 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
           const uint32_t st = ring_lds + uint32_t(s % kStages) * kTileBytesBf16;
           int nv[2];
           tile_nv(s, nv);
+          const int vis = n - back - (u0 + 2 * s) * kUnit;  // visible tokens of row c from here
           float x[2][4];
 #pragma unroll
           for (int h = 0; h < 2; ++h) {
+            const int nvh = min(nv[h], vis - h * kUnit);
             const int t = h * kUnit + c;
             const uint32_t y = uint32_t(g ^ (c & 7));
             const uint32_t row = st + uint32_t(t * kRowBytes);
@@ -689,7 +694,7 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
                   0, 0, 0);
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-              x[h][r] = (4 * g + r < nv[h]) ? sc[r] * a.scale_log2 : -INFINITY;
+              x[h][r] = (4 * g + r < nvh) ? sc[r] * a.scale_log2 : -INFINITY;
           }
           float mt = fmaxf(fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3])),
                            fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
@@ -1018,7 +1023,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
   const int c = lane & 15, g = lane >> 4;
   const bool logit_wave = wave >= 4;
   const int wq = wave & 3;  // logit waves: head tile; P.V waves: feature quarter
-  const int H = a.num_heads;
+  const int H = a.rows;
 
   const int lin = blockIdx.x;
   const int xcd = lin & 7, slot = lin >> 3;
@@ -1027,6 +1032,9 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
   const int ht0 = 4 * hg;                                 // first head tile of the group
   const bool lw_active = logit_wave && ht0 + wq < a.head_tiles;
   const int h0 = (ht0 + wq) * kHeadTile;                  // logit wave's first head
+  // Logit waves: row h0 + c belongs to query token (h0 + c) / heads, which
+  // sees all but the last `back` tokens of the request.
+  const int back = a.q_len - 1 - min(h0 + c, H - 1) / a.heads;
 
   // DMA map of the P.V waves (thread tid < 256): load i fills LDS slot
   // i * 256 + tid of the stage.
@@ -1214,6 +1222,10 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
             const uint32_t st = ring_lds + uint32_t(s % kStages) * kTileBytesBf16;
             int nv[kUnits];
             tile_nv(s, nv);
+            // Row c's visible tokens per unit (none once past its query token).
+            const int vis = n - back - (u0 + kUnits * s) * kUnit;
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) nv[u] = min(nv[u], vis - u * kUnit);
             float x[kUnits][4];
             // K through ordinary LDS loads: logit waves issue no ring loads,
             // so the compiler's own waits cost nothing and it may overlap the
@@ -1288,12 +1300,14 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
             m_seen = fmaxf(m_seen, mt);
             if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): the frame
             if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
+            // A row that has seen no token yet (all masked) keeps weight 0.
+            const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
             if constexpr (!KV_FP8) {
               float p[2][4];
 #pragma unroll
               for (int h = 0; h < 2; ++h)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_ref);
+                for (int r = 0; r < 4; ++r) p[h][r] = fast_exp2(x[h][r] - m_use);
               l_run += ((p[0][0] + p[0][1]) + (p[0][2] + p[0][3])) +
                        ((p[1][0] + p[1][1]) + (p[1][2] + p[1][3]));
               bf16x8_t pa;
@@ -1304,9 +1318,9 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
               }
               pw[0] = __builtin_bit_cast(u32x4_t, pa);
             } else {
-              const float rise = mt - m_ref;
+              const float rise = mt - m_use;
               const int e = rise > 0.f ? min(int(ceilf(rise)), int(kHeadsSlack)) : 0;
-              const float fe = m_ref + float(e);
+              const float fe = m_use + float(e);
               unsigned ph[4], pl[4];
               float lt = 0.f;
 #pragma unroll

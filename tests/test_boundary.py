@@ -55,6 +55,7 @@ def test_constants_match_header():
     assert int(defines["MLA_HEAD_DIM_V"]) == mla.HEAD_DIM_V == 512
     assert int(defines["MLA_MAX_HEADS"]) == mla.MAX_HEADS == 128
     assert int(defines["MLA_MAX_FORCED_SPLITS"]) == mla.MAX_FORCED_SPLITS == 16
+    assert int(defines["MLA_MAX_QUERY_LEN"]) == mla.MAX_QUERY_LEN == 16
     enums = dict((k, int(v)) for k, v in re.findall(r"(MLA_\w+) = (-?\d+)", text))
     for name in ("MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED",
                  "MLA_ERR_WORKSPACE_TOO_SMALL", "MLA_ERR_NO_DEVICE", "MLA_ERR_HIP",
@@ -67,7 +68,7 @@ def test_status_strings_and_version():
         s = mla.status_string(code)
         assert s.startswith("MLA_") and "UNKNOWN" not in s
     assert mla.status_string(7) == "MLA_ERR_UNKNOWN"
-    assert mla.abi_version() == 1
+    assert mla.abi_version() == 2
 
 
 # ------------------------------------------------------------------ workspace size
@@ -95,6 +96,22 @@ def test_workspace_size_auto_mode():
     # Never more rows than every request split into one piece per 16-token unit.
     assert mla.get_workspace_size(2, 16, 32, 0, 0) == _layout(2, 16, 4, 256)
     assert mla.get_workspace_size(2, 16, 16, 0, 0) == _layout(2, 16, 0, 256)
+
+
+def test_workspace_size_multi_token():
+    # q_len = 1 is the one-token query; rows are q_len * heads.
+    for args in ((512, 16, 3072, 0, 0), (7, 20, 4096, 2, 0), (128, 128, 32768, 0, 0)):
+        assert mla.get_workspace_size(*args, q_len=1) == mla.get_workspace_size(*args)
+    # 16 heads x 4 tokens = 64 rows: one workgroup per partition, 256 partitions.
+    assert mla.get_workspace_size(512, 16, 3072, 0, 0, q_len=4) == _layout(512, 64, 512, 256)
+    # 128 heads x 2 tokens = 256 rows: four workgroups per partition -> 64.
+    assert mla.get_workspace_size(128, 128, 32768, 0, 0, q_len=2) == _layout(128, 256, 128, 64)
+    # Forced splits: batch * splits partial rows of q_len * heads.
+    assert mla.get_workspace_size(3, 8, 100, 4, 0, q_len=3) == _layout(3, 24, 12)
+    # 16 tokens x 128 heads = 2048 rows: 32 workgroups per partition -> 8 partitions.
+    assert mla.get_workspace_size(4, 128, 1024, 0, 0, q_len=16) == _layout(4, 2048, 16, 8)
+    for bad in (0, 17, -1):
+        assert mla.get_workspace_size(2, 16, 100, 0, 0, q_len=bad) == 0
 
 
 @pytest.mark.parametrize("args", [(-1, 16, 10, 0, 0), (1, 0, 10, 0, 0), (1, 129, 10, 0, 0),
@@ -135,6 +152,37 @@ def test_decode_rejects_before_any_hip_call(over):
     assert _decode(**over) == mla.MLA_ERR_INVALID_ARG
 
 
+def _decode_multi(q_len, **over):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, scale=0.07, heads=16,
+             bs=32, splits=0, batch=2, max_blocks=4, num_blocks=8, kv_dtype=0, kv_scale=1.0,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return mla.library().mla_decode_multi_token(
+        vp(a["q"]), vp(a["kv"]), vp(a["bt"]), vp(a["sl"]), vp(a["out"]), vp(a["lse"]),
+        a["scale"], a["heads"], q_len, a["bs"], a["splits"], a["batch"], a["max_blocks"],
+        a["num_blocks"], a["kv_dtype"], a["kv_scale"], vp(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("q_len", [0, -1, 17])
+def test_decode_multi_token_rejects_q_len(q_len):
+    assert _decode_multi(q_len) == mla.MLA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("over", INVALID[:8] + [dict(heads=129), dict(splits=17)],
+                         ids=lambda d: str(d))
+def test_decode_multi_token_rejects_like_decode(over):
+    assert _decode_multi(2, **over) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_decode_multi_token_workspace_too_small():
+    need = mla.get_workspace_size(2, 16, 4 * 32, 4, 0, q_len=3)
+    assert need > mla.get_workspace_size(2, 16, 4 * 32, 4, 0)
+    assert _decode_multi(3, splits=4, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    if not HAS_GPU:
+        assert _decode_multi(3, splits=4, ws_bytes=need) == mla.MLA_ERR_NO_DEVICE
+
+
 def test_decode_workspace_too_small():
     assert _decode(ws_bytes=128) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
     need = mla.get_workspace_size(2, 16, 4 * 32, 4, 0)
@@ -151,7 +199,7 @@ def test_decode_without_device():
 
 def test_decode_profiled_requires_events():
     lib = mla.library()
-    args = [ctypes.c_void_p(FAKE)] * 5 + [None, 0.07, 16, 32, 0, 2, 4, 8, 0, 1.0,
+    args = [ctypes.c_void_p(FAKE)] * 5 + [None, 0.07, 16, 1, 32, 0, 2, 4, 8, 0, 1.0,
                                           ctypes.c_void_p(FAKE), 1 << 30, None]
     assert lib.mla_decode_profiled(*args, None) == mla.MLA_ERR_INVALID_ARG
     null_events = (ctypes.c_void_p * 4)(None, None, None, None)
@@ -168,6 +216,14 @@ def test_combine_rejects():
         mla.MLA_ERR_INVALID_ARG
     if not HAS_GPU:
         assert lib.mla_combine(f, f, f, f, None, 2, 16, None) == mla.MLA_ERR_NO_DEVICE
+
+
+def test_combine_accepts_multi_token_rows():
+    lib = mla.library()
+    f = ctypes.c_void_p(FAKE)
+    assert lib.mla_combine(f, f, f, f, None, 2, 2049, None) == mla.MLA_ERR_INVALID_ARG
+    if not HAS_GPU:
+        assert lib.mla_combine(f, f, f, f, None, 2, 2048, None) == mla.MLA_ERR_NO_DEVICE
 
 
 def test_binding_rejects_bad_tensors():

@@ -181,14 +181,16 @@ def quantize_e4m3(kv32: torch.Tensor):
     return codes.view(torch.uint8), kv_scale
 
 
-def make_rising(num_heads: int, kv_dtype: str, seed: int, block_size: int = 64) -> Workload:
+def make_rising(num_heads: int, kv_dtype: str, seed: int, block_size: int = 64,
+                q_len: int = 1) -> Workload:
     """Logits that climb far above the first tile's: past the first third of
     each request, key row t is alpha_t * q[b, 0] plus small noise, alpha_t
     ramping from 0.5 to 3.0, so head 0's logits rise from about 20 to about
-    125 (natural log units) while the other heads stay near N(0, 3)."""
+    125 (natural log units) while the other heads stay near N(0, 3). With
+    q_len > 1 the direction is head 0 of the last query token."""
     lens = [200, 900, 2100]
     wl = make_workload("rising", batch=len(lens), num_heads=num_heads, seq=("fixed", lens),
-                       block_size=block_size, seed=seed, kv_dtype="bf16")
+                       block_size=block_size, seed=seed, kv_dtype="bf16", q_len=q_len)
     gen = torch.Generator("cpu").manual_seed(seed + 1)
     kv32 = wl.kv.float().reshape(-1, D_K).clone()
     for b, n in enumerate(lens):
@@ -197,14 +199,15 @@ def make_rising(num_heads: int, kv_dtype: str, seed: int, block_size: int = 64) 
         rows = wl.block_table[b, t // block_size].long() * block_size + t % block_size
         alpha = 0.5 + 2.5 * (t - t0).float() / max(n - 1 - t0, 1)
         noise = 0.2 * torch.randn((len(t), D_K), generator=gen)
-        kv32[rows] = alpha[:, None] * wl.q[b, 0].float()[None, :] + noise
+        qdir = wl.q[b, 0] if wl.q_len == 1 else wl.q[b, -1, 0]
+        kv32[rows] = alpha[:, None] * qdir.float()[None, :] + noise
     if kv_dtype == "bf16":
         wl.kv = kv32.to(torch.bfloat16).view(wl.kv.shape)
     else:
         codes, wl.kv_scale = quantize_e4m3(kv32)
         wl.kv = codes.view(wl.kv.shape)
         wl.kv_dtype = "fp8"
-    wl.name = f"rising-{kv_dtype}-H{num_heads}"
+    wl.name = f"rising-{kv_dtype}-H{num_heads}-q{q_len}"
     return wl
 
 
