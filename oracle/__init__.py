@@ -41,6 +41,9 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_mla_attend.argtypes = [vp, vp, i32, ctypes.c_float, vp, vp, i64, i64, i64,
                                       i64, i64, i64, ctypes.c_float, vp, vp, vp, i64, vp, vp]
     lib.oracle_mla_attend.restype = i32
+    lib.oracle_mla_attend_sparse.argtypes = [vp, vp, i32, ctypes.c_float, vp, vp, i64, i64,
+                                             i64, i64, i64, ctypes.c_float, vp, i64, vp, vp]
+    lib.oracle_mla_attend_sparse.restype = i32
     lib.oracle_lse_merge.argtypes = [vp, vp, i64, i64, vp, vp]
     lib.oracle_lse_merge.restype = i32
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
@@ -116,6 +119,33 @@ class Oracle:
             raise ValueError(f"oracle_mla_attend failed with status {rc}")
         if not multi:
             return out[:, 0], lse[:, 0]
+        return out, lse
+
+    def attend_sparse(self, q_bits, kv, block_table, seq_lens, block_size, scale, indices,
+                      kv_fp8=False, kv_scale=1.0):
+        """Attention of each request over the token positions it lists.
+
+        q_bits   uint16 [B, H, 576] bf16 bits; indices int32 [B, topk] token
+                 positions (entries outside [0, seq_len) are skipped)
+        Returns (out float64 [B, H, 512], lse float64 [B, H]).
+        """
+        q_bits = np.ascontiguousarray(q_bits, dtype=np.uint16)
+        kv = np.ascontiguousarray(kv, dtype=np.uint8 if kv_fp8 else np.uint16)
+        block_table = np.ascontiguousarray(block_table, dtype=np.int32)
+        seq_lens = np.ascontiguousarray(seq_lens, dtype=np.int32)
+        indices = np.ascontiguousarray(indices, dtype=np.int32)
+        batch, num_heads, dk = q_bits.shape
+        if dk != D_K or kv.shape[-1] != D_K or kv.shape[1] != block_size or \
+                indices.ndim != 2 or indices.shape[0] != batch:
+            raise ValueError("shape mismatch")
+        out = np.empty((batch, num_heads, D_V), dtype=np.float64)
+        lse = np.empty((batch, num_heads), dtype=np.float64)
+        rc = self.lib.oracle_mla_attend_sparse(
+            _ptr(q_bits), _ptr(kv), int(bool(kv_fp8)), float(kv_scale), _ptr(block_table),
+            _ptr(seq_lens), batch, num_heads, block_size, block_table.shape[1], kv.shape[0],
+            float(scale), _ptr(indices), indices.shape[1], _ptr(out), _ptr(lse))
+        if rc != 0:
+            raise ValueError(f"oracle_mla_attend_sparse failed with status {rc}")
         return out, lse
 
     def lse_merge(self, part_out, part_lse):

@@ -202,6 +202,94 @@ int oracle_mla_attend(const uint16_t* q, const void* kv_cache, int kv_fp8, float
 }
 
 /*
+ * oracle_mla_attend_sparse: attention of each request over a listed subset of
+ * its cached tokens (sparse MLA decode). The pages name a sparse MLA backend
+ * next to the fp8 cache (PR #57428, deployment command and test result:
+ * FLASHINFER_MLA_SPARSE_DSV41 with --kv-cache-dtype fp8) without defining
+ * it; the oracle takes the plain reading: request b attends to the tokens
+ * whose positions indices[b][0..topk) lists, each listed entry counted once
+ * per appearance, and entries outside [0, seq_lens[b]) are skipped (they
+ * pad short lists). With no listed token: out = 0, lse = -inf.
+ *
+ *  q        [batch][num_heads][576] bf16 bits (one query token per request)
+ *  indices  [batch][topk] token positions within each request
+ *  out      [batch][num_heads][512] fp64; lse [batch][num_heads] fp64
+ * Other arguments as for oracle_mla_attend.
+ */
+int oracle_mla_attend_sparse(const uint16_t* q, const void* kv_cache, int kv_fp8,
+                             float kv_scale, const int32_t* block_table,
+                             const int32_t* seq_lens, int64_t batch, int64_t num_heads,
+                             int64_t block_size, int64_t max_blocks, int64_t num_blocks,
+                             float scale, const int32_t* indices, int64_t topk, double* out,
+                             double* lse) {
+  if (!q || !kv_cache || !block_table || !seq_lens || !indices || !out || !lse)
+    return ORACLE_BAD_ARG;
+  if (batch < 0 || num_heads < 1 || block_size < 1 || max_blocks < 0 || num_blocks < 0 ||
+      topk < 0)
+    return ORACLE_BAD_ARG;
+  for (int64_t b = 0; b < batch; ++b) {
+    int64_t n = seq_lens[b];
+    if (n < 0 || n > max_blocks * block_size) return ORACLE_BAD_ARG;
+    for (int64_t j = 0; j < topk; ++j) {
+      int64_t t = indices[b * topk + j];
+      if (t < 0 || t >= n) continue;
+      int64_t blk = block_table[b * max_blocks + t / block_size];
+      if (blk < 0 || blk >= num_blocks) return ORACLE_BAD_BLOCK;
+    }
+  }
+  const double s = (double)scale;
+  const double kvs = (double)kv_scale;
+
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t w = 0; w < batch * num_heads; ++w) {
+    int64_t b = w / num_heads, h = w % num_heads;
+    int64_t n = seq_lens[b];
+    double* o = out + w * ORACLE_DV;
+    double qv[ORACLE_D], k[ORACLE_D];
+    for (int d = 0; d < ORACLE_DV; ++d) o[d] = 0.0;
+    for (int d = 0; d < ORACLE_D; ++d)
+      qv[d] = bf16_bits_to_double(q[(b * num_heads + h) * ORACLE_D + d]);
+    double* x = (double*)malloc((size_t)(topk > 0 ? topk : 1) * sizeof(double));
+    /* Pass 1: the logit of every listed token and their maximum. */
+    double m = -INFINITY;
+    int64_t listed = 0;
+    for (int64_t j = 0; j < topk; ++j) {
+      int64_t t = indices[b * topk + j];
+      if (t < 0 || t >= n) continue;
+      int64_t row = (int64_t)block_table[b * max_blocks + t / block_size] * block_size +
+                    t % block_size;
+      load_token(kv_cache, kv_fp8, kvs, row, k);
+      double dot = 0.0;
+      for (int d = 0; d < ORACLE_D; ++d) dot += qv[d] * k[d];
+      x[j] = s * dot;
+      if (x[j] > m) m = x[j];
+      ++listed;
+    }
+    if (listed == 0) {
+      free(x);
+      lse[w] = -INFINITY;
+      continue;
+    }
+    /* Pass 2: weights, their sum and the weighted value rows. */
+    double l = 0.0;
+    for (int64_t j = 0; j < topk; ++j) {
+      int64_t t = indices[b * topk + j];
+      if (t < 0 || t >= n) continue;
+      int64_t row = (int64_t)block_table[b * max_blocks + t / block_size] * block_size +
+                    t % block_size;
+      load_token(kv_cache, kv_fp8, kvs, row, k);
+      double wt = exp(x[j] - m);
+      l += wt;
+      for (int d = 0; d < ORACLE_DV; ++d) o[d] += wt * k[d];
+    }
+    free(x);
+    for (int d = 0; d < ORACLE_DV; ++d) o[d] /= l;
+    lse[w] = m + log(l);
+  }
+  return ORACLE_OK;
+}
+
+/*
  * oracle_lse_merge: merge n_parts normalised partial results of one request.
  *
  *  part_out [n_parts][num_heads][512], part_lse [n_parts][num_heads]

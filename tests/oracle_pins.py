@@ -389,11 +389,94 @@ def pin_multi_token_split_merge(orc):
         assert _close(ml, full_lse[b].reshape(-1)), f"multi-token split-merge lse (b={b})"
 
 
+def pin_sparse_all_positions_is_dense(orc):
+    """Listing every position in order (padded with -1) is exactly dense decode."""
+    wl = workloads.make_workload(batch=4, num_heads=3, seq=("fixed", [0, 5, 33, 100]),
+                                 block_size=16, seed=17, poison=True)
+    idx = np.full((4, 120), -1, np.int32)
+    for b, n in enumerate(wl.seq_lens.tolist()):
+        idx[b, :n] = np.arange(n)
+    args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(), 16,
+            wl.scale)
+    out, lse = orc.attend_sparse(*args, idx)
+    ref_out, ref_lse = orc.attend(*args)
+    assert (out == ref_out).all() and np.array_equal(lse, ref_lse), "all positions != dense"
+
+
+def pin_sparse_sdpa_on_gathered_rows(orc):
+    """Random lists with repeats, any order, and skipped entries equal float64 SDPA
+    over the gathered rows (repeats included), for bf16 and E4M3 caches."""
+    rng = np.random.default_rng(18)
+    for kv_dtype in ("bf16", "fp8"):
+        wl = workloads.make_workload(batch=3, num_heads=4, seq=("fixed", [1, 40, 150]),
+                                     block_size=16, seed=18, kv_dtype=kv_dtype, poison=True)
+        topk = 24
+        idx = np.full((3, topk), -1, np.int32)
+        for b, n in enumerate(wl.seq_lens.tolist()):
+            pick = rng.integers(0, n, size=topk - 4)
+            junk = np.array([-1, n, n + 7, -3])                 # skipped entries
+            row = np.concatenate([pick, junk])
+            rng.shuffle(row)
+            idx[b] = row
+        fp8 = kv_dtype == "fp8"
+        out, lse = orc.attend_sparse(wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(),
+                                     wl.seq_lens.numpy(), 16, wl.scale, idx, kv_fp8=fp8,
+                                     kv_scale=wl.kv_scale)
+        if fp8:
+            deq = wl.kv.view(torch.float8_e4m3fn).to(torch.float64) * wl.kv_scale
+        else:
+            deq = wl.kv.to(torch.float64)
+        for b, n in enumerate(wl.seq_lens.tolist()):
+            keep = [int(t) for t in idx[b] if 0 <= t < n]
+            rows = torch.stack([deq[int(wl.block_table[b, t // 16]), t % 16] for t in keep])
+            q = wl.q[b].to(torch.float64)
+            kk = rows[None, None].expand(1, q.shape[0], -1, -1)
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                q[None, :, None, :], kk, kk[..., :512], scale=wl.scale)[0, :, 0].numpy()
+            ref_lse = torch.logsumexp(wl.scale * (q @ rows.T), -1).numpy()
+            assert _close(out[b], ref), f"sparse out vs SDPA ({kv_dtype}, b={b})"
+            assert _close(lse[b], ref_lse), f"sparse lse vs logsumexp ({kv_dtype}, b={b})"
+
+
+def pin_sparse_closed_forms(orc):
+    """A position listed twice: out is its value row, lse its logit + ln 2; only
+    skipped entries: out 0, lse -inf."""
+    wl = workloads.make_workload(batch=2, num_heads=2, seq=("fixed", [20, 20]), block_size=16,
+                                 seed=19)
+    idx = np.array([[7, 7, -1, 25], [-1, 20, 21, -5]], np.int32)
+    out, lse = orc.attend_sparse(wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(),
+                                 wl.seq_lens.numpy(), 16, wl.scale, idx)
+    k7 = wl.kv[int(wl.block_table[0, 0]), 7].to(torch.float64)
+    x7 = (wl.scale * (wl.q[0].to(torch.float64) @ k7)).numpy()
+    assert (out[0] == k7[:512].numpy()[None]).all(), "repeated position: out = its value row"
+    assert _close(lse[0], x7 + math.log(2)), "repeated position: lse = logit + ln 2"
+    assert (out[1] == 0).all() and np.isneginf(lse[1]).all(), "no listed token: out 0, lse -inf"
+
+
+def pin_sparse_split_merge(orc):
+    """Cutting each list into consecutive sub-lists and merging by LSE equals the
+    whole list."""
+    wl = workloads.make_workload(batch=2, num_heads=3, seq=("fixed", [70, 300]), block_size=16,
+                                 seed=20, topk=64, poison=True)
+    args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(), 16,
+            wl.scale)
+    idx = wl.indices.numpy()
+    full_out, full_lse = orc.attend_sparse(*args, idx)
+    cuts = [0, 5, 6, 40, 64]
+    parts = [orc.attend_sparse(*args, np.ascontiguousarray(idx[:, a:b]))
+             for a, b in zip(cuts[:-1], cuts[1:])]
+    for b in range(2):
+        mo, ml = orc.lse_merge(np.stack([p[0][b] for p in parts]),
+                               np.stack([p[1][b] for p in parts]))
+        assert _close(mo, full_out[b]) and _close(ml, full_lse[b]), f"sparse split-merge b={b}"
+
+
 PINS = [pin_e4m3_decode, pin_bf16_widen, pin_sdpa_identity_table, pin_sdpa_shuffled_pages,
         pin_closed_forms, pin_empty_request, pin_split_merge, pin_merge_closed_form,
         pin_rope_shift, pin_head_padding, pin_block_permutation, pin_batch_independence,
         pin_fp8_dequant, pin_multi_token_causal_sdpa, pin_multi_token_rows_are_single_decodes,
-        pin_multi_token_split_merge]
+        pin_multi_token_split_merge, pin_sparse_all_positions_is_dense,
+        pin_sparse_sdpa_on_gathered_rows, pin_sparse_closed_forms, pin_sparse_split_merge]
 
 
 def main(argv=None) -> int:

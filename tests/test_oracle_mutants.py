@@ -38,6 +38,12 @@ MUTANTS = [
     ("causal_reversed", "int64_t visible = n - (q_len - 1 - qi);",
      "int64_t visible = n - qi;"),
     ("causal_ignored", "if (t1 > visible) t1 = visible;", ""),
+    ("sparse_skip_bound", "if (t < 0 || t >= n) continue;\n      int64_t row",
+     "if (t < 0 || t > n) continue;\n      int64_t row"),
+    ("sparse_weight_index", "double wt = exp(x[j] - m);", "double wt = exp(x[0] - m);"),
+    ("sparse_q_row", "qv[d] = bf16_bits_to_double(q[(b * num_heads + h) * ORACLE_D + d]);",
+     "qv[d] = bf16_bits_to_double(q[((h % batch) * num_heads + (b % num_heads)) * ORACLE_D + d]);"),
+    ("sparse_scale_dropped", "x[j] = s * dot;", "x[j] = dot;"),
     ("out_row_token_head_transposed", "int64_t row_out = (i * q_len + qi) * num_heads + h;",
      "int64_t row_out = (i * num_heads + h) * q_len + qi;"),
     ("e4m3_bias", "exponent - 7);", "exponent - 8);"),

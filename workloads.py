@@ -22,6 +22,8 @@ Named configurations:
   r1tp8     B=512, H=16,  seq_lens U[1024, 3072], bs=32
   fullhead  B=128, H=128, seq_lens log-uniform [512, 32768], bs=64
   fp8       B=64,  H=128, seq_lens 8192, bs=64, E4M3 cache + per-tensor scale
+  sparse-r1tp8  B=512, H=16, seq_lens U[4096, 16384], bs=32, 2048 listed tokens each
+  sparse-fp8    B=64, H=128, seq_lens 16384, bs=64, E4M3, 2048 listed tokens each
 """
 from __future__ import annotations
 
@@ -51,6 +53,12 @@ CONFIGS = {
                      seed=5, kv_dtype="bf16"),
     "fp8": dict(batch=64, num_heads=128, seq=("fixed", [8192] * 64), block_size=64,
                 seed=6, kv_dtype="fp8"),
+    # Sparse decode: each request attends to 2048 listed positions of a longer
+    # context (synthetic top-k lists).
+    "sparse-r1tp8": dict(batch=512, num_heads=16, seq=("uniform", 4096, 16384), block_size=32,
+                         seed=7, kv_dtype="bf16", topk=2048),
+    "sparse-fp8": dict(batch=64, num_heads=128, seq=("fixed", [16384] * 64), block_size=64,
+                       seed=8, kv_dtype="fp8", topk=2048),
 }
 
 
@@ -65,6 +73,7 @@ class Workload:
     kv_dtype: str              # "bf16" | "fp8"
     kv_scale: float            # per-tensor E4M3 scale (1.0 for bf16)
     scale: float = SCALE
+    indices: torch.Tensor | None = None  # sparse decode: [B, topk] int32 token positions
 
     @property
     def batch(self) -> int:
@@ -131,7 +140,7 @@ def _randn_bf16(gen: torch.Generator, n_rows: int, chunk_rows: int = 1 << 15) ->
 
 def make_workload(name: str = "custom", *, batch: int, num_heads: int, seq, block_size: int,
                   seed: int, kv_dtype: str = "bf16", pool_blocks: int | None = None,
-                  poison: bool = False, q_len: int = 1) -> Workload:
+                  poison: bool = False, q_len: int = 1, topk: int | None = None) -> Workload:
     """Draw one workload.
 
     seq          ("fixed", list) | ("uniform", lo, hi) | ("loguniform", lo, hi)
@@ -139,6 +148,9 @@ def make_workload(name: str = "custom", *, batch: int, num_heads: int, seq, bloc
                  [B, q_len, H, 576] (the same draw order either way)
     pool_blocks  physical pool size (default: exactly the blocks the requests use)
     poison       put NaN in unused blocks and in tail slots past each seq_len
+    topk         sparse decode: draw indices [B, topk], per request a sorted
+                 sample without replacement of min(topk, N) positions of [0, N),
+                 padded with -1 (drawn last, after the KV pool)
     """
     gen = torch.Generator("cpu").manual_seed(seed)
     seq_lens = draw_seq_lens(gen, batch, seq)
@@ -168,9 +180,23 @@ def make_workload(name: str = "custom", *, batch: int, num_heads: int, seq, bloc
         raise ValueError(f"unknown kv dtype {kv_dtype}")
     wl = Workload(name=name, q=q, kv=kv, block_table=table, seq_lens=seq_lens,
                   block_size=block_size, kv_dtype=kv_dtype, kv_scale=kv_scale)
+    if topk is not None:
+        wl.indices = draw_indices(gen, seq_lens, topk)
     if poison:
         poison_unused(wl)
     return wl
+
+
+def draw_indices(gen: torch.Generator, seq_lens: torch.Tensor, topk: int) -> torch.Tensor:
+    """Synthetic top-k lists: per request a sorted sample without replacement
+    of min(topk, N) positions of [0, N), padded with -1."""
+    out = torch.full((seq_lens.numel(), topk), -1, dtype=torch.int32)
+    for b, n in enumerate(seq_lens.tolist()):
+        k = min(topk, n)
+        if k:
+            pick = torch.randperm(n, generator=gen)[:k].sort().values
+            out[b, :k] = pick.to(torch.int32)
+    return out
 
 
 def quantize_e4m3(kv32: torch.Tensor):
