@@ -65,20 +65,33 @@ def measured_traffic(config: str, khash: str):
     return None
 
 
+def listed_tokens(wl) -> int:
+    """Sparse decode: list entries that name a token of their request."""
+    n = wl.seq_lens[:, None].long()
+    idx = wl.indices.long()
+    return int(((idx >= 0) & (idx < n)).sum())
+
+
 def algorithmic_bytes(wl) -> int:
     """Bytes a decode call must move at least once: the cache rows of every
-    token, q, out, lse, the used block-table entries and seq_lens."""
+    token (sparse: of every listed token), q, out, lse, the block-table
+    entries used (sparse: one per listed token, plus the lists) and seq_lens."""
     e_kv = 1 if wl.kv_dtype == "fp8" else 2
-    n_tok = wl.total_tokens
-    nblk = sum((int(n) + wl.block_size - 1) // wl.block_size for n in wl.seq_lens)
     b, h = wl.batch, wl.num_heads * wl.q_len   # query rows per request
-    return (n_tok * D_K * e_kv + b * h * D_K * 2 + b * h * D_V * 2 + b * h * 4 + nblk * 4
-            + b * 4)
+    io = b * h * D_K * 2 + b * h * D_V * 2 + b * h * 4 + b * 4
+    if wl.indices is not None:
+        n_tok = listed_tokens(wl)
+        return n_tok * D_K * e_kv + io + n_tok * 4 + wl.indices.numel() * 4
+    nblk = sum((int(n) + wl.block_size - 1) // wl.block_size for n in wl.seq_lens)
+    return wl.total_tokens * D_K * e_kv + io + nblk * 4
 
 
 def algorithmic_flops(wl) -> int:
     """Logits (2 * 576) and P.V (2 * 512) multiply-adds per head and visible
-    token: query token i of q_len sees N - q_len + 1 + i of a request's N."""
+    token: query token i of q_len sees N - q_len + 1 + i of a request's N
+    (sparse: the listed tokens)."""
+    if wl.indices is not None:
+        return 2 * (D_K + D_V) * wl.num_heads * listed_tokens(wl)
     visible = sum(max(0, int(n) - wl.q_len + 1 + i) for n in wl.seq_lens
                   for i in range(wl.q_len))
     return 2 * (D_K + D_V) * wl.num_heads * visible
@@ -90,27 +103,41 @@ def cpu_baseline(wl, target_s: float) -> dict:
 
     import oracle
     orc = oracle.load()
-    lens = wl.seq_lens.numpy().astype(np.int64)
-    args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(),
-            wl.block_size, wl.scale)
     kw = dict(kv_fp8=wl.kv_dtype == "fp8", kv_scale=wl.kv_scale)
+    if wl.indices is not None:
+        idx = wl.indices.numpy()
+        lens = ((idx >= 0) & (idx < wl.seq_lens.numpy()[:, None])).sum(1).astype(np.int64)
+        total = int(lens.sum())
+
+        def run(n):
+            orc.attend_sparse(wl.q_bits()[:n], wl.kv_bits(), wl.block_table.numpy()[:n],
+                              wl.seq_lens.numpy()[:n], wl.block_size, wl.scale,
+                              np.ascontiguousarray(idx[:n]), **kw)
+    else:
+        lens = wl.seq_lens.numpy().astype(np.int64)
+        total = wl.total_tokens
+        args = (wl.q_bits(), wl.kv_bits(), wl.block_table.numpy(), wl.seq_lens.numpy(),
+                wl.block_size, wl.scale)
+
+        def run(n):
+            orc.attend(*args, req=np.arange(n, dtype=np.int32), **kw)
     n_probe = min(wl.batch, 4)
     t0 = time.perf_counter()
-    orc.attend(*args, req=np.arange(n_probe, dtype=np.int32), **kw)
+    run(n_probe)
     probe = time.perf_counter() - t0
     per_tok = probe / max(1, lens[:n_probe].sum())
     want_tok = target_s / max(per_tok, 1e-12)
     n_req = int(np.searchsorted(np.cumsum(lens), want_tok) + 1)
     n_req = max(n_probe, min(wl.batch, n_req))
     t0 = time.perf_counter()
-    orc.attend(*args, req=np.arange(n_req, dtype=np.int32), **kw)
+    run(n_req)
     dt = time.perf_counter() - t0
     tok = int(lens[:n_req].sum())
-    full_s = dt * wl.total_tokens / tok
+    full_s = dt * total / tok
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     return {"value": round(full_s * 1e6, 1), "unit": "us/call", "cores": threads,
             "kind": "oracle",
-            "sample": (f"first {n_req} of {wl.batch} requests ({tok} of {wl.total_tokens} "
+            "sample": (f"first {n_req} of {wl.batch} requests ({tok} of {total} "
                        f"tokens, all heads) in {dt:.2f} s, scaled to the whole batch"),
             "tokens_per_s": round(tok / dt, 1)}
 
@@ -185,14 +212,26 @@ def main(argv=None) -> int:
     kvs = [wl.kv.to(dev) for _ in range(copies)]
     out = torch.empty(tuple(wl.q.shape[:-1]) + (D_V,), dtype=torch.bfloat16, device=dev)
     lse = torch.empty(tuple(wl.q.shape[:-1]), dtype=torch.float32, device=dev)
-    nbytes = mla.get_workspace_size(wl.batch, wl.num_heads, wl.max_blocks * wl.block_size,
-                                    args.num_splits, 0, q_len=wl.q_len)
+    if wl.indices is not None:
+        if args.q_len != 1:
+            raise SystemExit("sparse workloads take one query token per request")
+        nbytes = mla.get_workspace_size_sparse(wl.batch, wl.num_heads, wl.indices.shape[1],
+                                               args.num_splits, 0)
+        idx = wl.indices.to(dev)
+    else:
+        nbytes = mla.get_workspace_size(wl.batch, wl.num_heads, wl.max_blocks * wl.block_size,
+                                        args.num_splits, 0, q_len=wl.q_len)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     log(f"tokens={wl.total_tokens} pool={pool_bytes / 2**20:.0f} MiB copies={copies} "
         f"workspace={nbytes / 2**20:.1f} MiB")
 
     def call(i, events=None):
+        if wl.indices is not None:
+            mla.decode_sparse(q, kvs[i % copies], bt, sl, idx, scale=wl.scale,
+                              num_splits=args.num_splits, kv_scale=wl.kv_scale, out=out, lse=lse,
+                              workspace=ws, stream=stream, events=events)
+            return
         mla.decode(q, kvs[i % copies], bt, sl, scale=wl.scale, num_splits=args.num_splits,
                    kv_scale=wl.kv_scale, out=out, lse=lse, workspace=ws, stream=stream,
                    events=events)
@@ -237,12 +276,13 @@ def main(argv=None) -> int:
     achieved = alg_bytes / (attn_avg * 1e-3) / 1e9
     mfma_peak = PEAK_MFMA_TFLOPS["fp8" if wl.kv_dtype == "fp8" else "bf16"]
     traffic = measured_traffic(label, kernel_source_hash())
+    sparse = int(wl.indices is not None)
     if wl.kv_dtype == "fp8":
-        kernel_name = "mla::attn_mh_kernel<1>"
-    elif wl.num_heads * wl.q_len <= 16:
+        kernel_name = f"mla::attn_mh_kernel<1, {sparse}>"
+    elif wl.num_heads * wl.q_len <= 16 and not sparse:
         kernel_name = "mla::attn_ws_kernel"
     else:
-        kernel_name = "mla::attn_mh_kernel<0>"
+        kernel_name = f"mla::attn_mh_kernel<0, {sparse}>"
     # The roof that bounds the call: whichever of HBM bytes and matrix-core
     # flops needs more time at peak.
     t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)
@@ -277,11 +317,13 @@ def main(argv=None) -> int:
         "data": "synthetic",
         "config": {"workload": label, "batch": wl.batch, "num_heads": wl.num_heads,
                    "q_len": wl.q_len,
+                   "topk": None if wl.indices is None else wl.indices.shape[1],
                    "seq_lens": list(cfg["seq"]) if cfg["seq"][0] != "fixed" else
                    sorted(set(cfg["seq"][1])), "total_tokens": wl.total_tokens,
                    "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
                    "num_splits": args.num_splits or "auto", "parallelism": "single-gpu"},
-        "tokens_per_s": round(wl.total_tokens / (ms_per_step * 1e-3), 1),
+        "tokens_per_s": round((wl.total_tokens if wl.indices is None else listed_tokens(wl))
+                              / (ms_per_step * 1e-3), 1),
         "hbm_GBps_algorithmic": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "mfma_pct": round(100 * alg_flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak, 2),
         "kernels_us": {"plan": round(statistics.fmean(plan_ms) * 1e3, 2),

@@ -21,7 +21,8 @@
  * Any head count 1..128 is accepted (PR #20769: num_heads below 128 is what
  * lets tensor parallelism shard heads); no padding to 128 is required.
  * mla_decode_multi_token takes several query tokens per request under a
- * causal mask (speculative decoding; see its comment).
+ * causal mask (speculative decoding; see its comment), and mla_decode_sparse
+ * attends to a listed subset of each request's tokens.
  *
  * Conventions shared by every entry point:
  *  - All data pointers are caller-owned DEVICE memory on the current HIP
@@ -54,6 +55,7 @@ extern "C" {
 #define MLA_MAX_HEADS 128
 #define MLA_MAX_QUERY_LEN 16   /* query tokens per request (mla_decode_multi_token) */
 #define MLA_MAX_FORCED_SPLITS 16
+#define MLA_MAX_TOPK 65536     /* listed positions per request (mla_decode_sparse) */
 
 typedef enum {
   MLA_OK = 0,
@@ -195,6 +197,54 @@ mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
                                  int32_t batch, int32_t max_blocks_per_seq, int32_t num_blocks,
                                  int32_t kv_dtype, float kv_scale, void* workspace,
                                  size_t workspace_bytes, void* stream, void* const* events);
+
+/*
+ * mla_decode_sparse: each request attends to a listed subset of its cached
+ * tokens (sparse MLA decode; PR #57428 deploys a sparse MLA attention
+ * backend with the fp8 cache, deployment command and test result). The
+ * pages do not define the operation; this library takes the plain reading:
+ *
+ *   request b attends to the tokens at positions indices[b][0..topk), each
+ *   entry counted once per appearance (a repeated position weighs twice);
+ *   entries outside [0, seq_lens[b]) are skipped, so short lists are padded
+ *   with -1; a list with no valid entry gives out = 0, lse = -inf.
+ *
+ *  indices      [batch][topk] int32 token positions within each request
+ *               (device, 4-byte aligned); the order is free
+ *  topk         1..65536 entries per request
+ *  q, out, lse  as for mla_decode (one query token per request)
+ *  workspace_bytes  >= mla_get_workspace_size_sparse(batch, num_heads, topk,
+ *               num_splits, <CUs>) (automatic mode accepts less, as above)
+ *
+ * Every other argument, the error behaviour and the ownership rules are
+ * those of mla_decode. Also MLA_ERR_INVALID_ARG if num_blocks * block_size
+ * exceeds 2^31 - 1. A prepass turns each entry into a physical row id through
+ * block_table; the attention kernel then gathers the listed rows.
+ */
+mla_status_t mla_decode_sparse(const void* q, const void* kv_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* indices, int32_t topk,
+                               void* out, float* lse, float scale, int32_t num_heads,
+                               int32_t block_size, int32_t num_splits, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, int32_t kv_dtype,
+                               float kv_scale, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/* Workspace bytes that mla_decode_sparse needs (pure host arithmetic; 0 when
+ * an argument is out of range). */
+size_t mla_get_workspace_size_sparse(int64_t batch, int64_t num_heads, int64_t topk,
+                                     int64_t num_splits, int64_t num_cus);
+
+/* mla_decode_sparse, recording events[0..3] as mla_decode_profiled does
+ * (events[0] precedes the sparse prepass). */
+mla_status_t mla_decode_sparse_profiled(const void* q, const void* kv_cache,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const int32_t* indices, int32_t topk, void* out,
+                                        float* lse, float scale, int32_t num_heads,
+                                        int32_t block_size, int32_t num_splits, int32_t batch,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks,
+                                        int32_t kv_dtype, float kv_scale, void* workspace,
+                                        size_t workspace_bytes, void* stream,
+                                        void* const* events);
 
 /*
  * mla_combine: merge normalised split partials by log-sum-exp (PR #20769,

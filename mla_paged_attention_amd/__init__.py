@@ -14,6 +14,7 @@ from ._binding import (  # noqa: F401
     MAX_FORCED_SPLITS,
     MAX_HEADS,
     MAX_QUERY_LEN,
+    MAX_TOPK,
     MLA_ERR_HIP,
     MLA_ERR_INVALID_ARG,
     MLA_ERR_NO_DEVICE,
@@ -26,7 +27,9 @@ from ._binding import (  # noqa: F401
     abi_version,
     combine,
     decode,
+    decode_sparse,
     get_workspace_size,
+    get_workspace_size_sparse,
     library,
     status_string,
     workspace_for,

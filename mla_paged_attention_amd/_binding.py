@@ -22,6 +22,7 @@ HEAD_DIM_V = 512
 MAX_HEADS = 128
 MAX_QUERY_LEN = 16
 MAX_FORCED_SPLITS = 16
+MAX_TOPK = 65536
 BLOCK_SIZES = (16, 32, 64, 128)
 
 MLA_OK = 0
@@ -35,7 +36,8 @@ MLA_KV_BF16 = 0
 MLA_KV_FP8_E4M3 = 1
 
 EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_get_workspace_size_multi_token",
-                    "mla_decode", "mla_decode_multi_token", "mla_decode_profiled",
+                    "mla_get_workspace_size_sparse", "mla_decode", "mla_decode_multi_token",
+                    "mla_decode_profiled", "mla_decode_sparse", "mla_decode_sparse_profiled",
                     "mla_combine", "mla_status_string", "mla_abi_version")
 
 _lib = None
@@ -64,6 +66,13 @@ def _bind(lib: ctypes.CDLL) -> None:
     lib.mla_decode_multi_token.restype = i32
     lib.mla_decode_profiled.argtypes = multi_args + [ctypes.POINTER(vp)]
     lib.mla_decode_profiled.restype = i32
+    sparse_args = decode_args[:4] + [vp, i32] + decode_args[4:]  # indices, topk after seq_lens
+    lib.mla_decode_sparse.argtypes = sparse_args
+    lib.mla_decode_sparse.restype = i32
+    lib.mla_decode_sparse_profiled.argtypes = sparse_args + [ctypes.POINTER(vp)]
+    lib.mla_decode_sparse_profiled.restype = i32
+    lib.mla_get_workspace_size_sparse.argtypes = [i64, i64, i64, i64, i64]
+    lib.mla_get_workspace_size_sparse.restype = sz
     lib.mla_combine.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp]
     lib.mla_combine.restype = i32
     lib.mla_status_string.argtypes = [i32]
@@ -102,6 +111,12 @@ def get_workspace_size(batch: int, num_heads: int, max_seq_len: int, num_splits:
                                                     num_cus))
     return int(library().mla_get_workspace_size_multi_token(batch, num_heads, q_len,
                                                             max_seq_len, num_splits, num_cus))
+
+
+def get_workspace_size_sparse(batch: int, num_heads: int, topk: int, num_splits: int = 0,
+                              num_cus: int = 0) -> int:
+    return int(library().mla_get_workspace_size_sparse(batch, num_heads, topk, num_splits,
+                                                       num_cus))
 
 
 def _ptr(t) -> ctypes.c_void_p:
@@ -204,6 +219,65 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         what = "mla_decode_multi_token"
     if st != MLA_OK:
         raise MLAError(st, what)
+    return out, lse
+
+
+def decode_sparse(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                  seq_lens: torch.Tensor, indices: torch.Tensor, *, scale: float,
+                  num_splits: int = 0, kv_scale: float = 1.0, out: torch.Tensor | None = None,
+                  lse: torch.Tensor | bool | None = True, workspace: torch.Tensor | None = None,
+                  stream=None, events=None):
+    """Sparse MLA decode (see include/mla.h, mla_decode_sparse): request b attends
+    to the token positions indices[b] lists ([B, topk] int32; entries outside
+    [0, seq_len) are skipped). Other arguments and results as for decode()
+    with one query token per request."""
+    if q.dim() != 3 or q.shape[2] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise ValueError("q must be [batch, num_heads, 576] bf16")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != HEAD_DIM_K:
+        raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
+    kv_dtype = _kv_dtype(kv_cache)
+    batch, num_heads, _ = q.shape
+    num_blocks, block_size, _ = kv_cache.shape
+    if block_table.dim() != 2 or block_table.shape[0] != batch or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be [batch, max_blocks] int32")
+    if seq_lens.shape != (batch,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be [batch] int32")
+    if indices.dim() != 2 or indices.shape[0] != batch or indices.dtype != torch.int32:
+        raise ValueError("indices must be [batch, topk] int32")
+    topk = indices.shape[1]
+    dev = q.device
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens), ("indices", indices)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if out is None:
+        out = torch.empty((batch, num_heads, HEAD_DIM_V), dtype=torch.bfloat16, device=dev)
+    elif tuple(out.shape) != (batch, num_heads, HEAD_DIM_V) or out.dtype != torch.bfloat16 or \
+            out.device != dev or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous [{batch}, {num_heads}, 512] bf16 on {dev}")
+    if lse is True:
+        lse = torch.empty((batch, num_heads), dtype=torch.float32, device=dev)
+    elif lse is False:
+        lse = None
+    elif lse is not None and (tuple(lse.shape) != (batch, num_heads) or
+                              lse.dtype != torch.float32 or lse.device != dev or
+                              not lse.is_contiguous()):
+        raise ValueError(f"lse must be contiguous [{batch}, {num_heads}] fp32 on {dev}")
+    if workspace is None:
+        need = get_workspace_size_sparse(batch, num_heads, max(topk, 1), num_splits, 0)
+        workspace = workspace_for(dev, stream, need)
+    args = (_ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(indices), topk,
+            _ptr(out), _ptr(lse), float(scale), num_heads, block_size, num_splits, batch,
+            block_table.shape[1], num_blocks, kv_dtype, float(kv_scale), _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream_handle(stream))
+    lib = library()
+    if events is None:
+        st = lib.mla_decode_sparse(*args)
+    else:
+        arr = (ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in events])
+        st = lib.mla_decode_sparse_profiled(*args, arr)
+    if st != MLA_OK:
+        raise MLAError(st, "mla_decode_sparse")
     return out, lse
 
 

@@ -87,6 +87,8 @@ struct DecodeArgs {
   void* workspace;
   size_t workspace_bytes;
   hipStream_t stream;
+  const int32_t* indices = nullptr;  // sparse decode: [batch][topk] token positions
+  int32_t topk = 0;                  // > 0: sparse decode
 
   int32_t rows() const { return num_heads * q_len; }  // query rows per request
 };
@@ -109,15 +111,23 @@ mla_status_t validate_decode(const DecodeArgs& a) {
   } else {
     return MLA_ERR_INVALID_ARG;
   }
+  if (a.topk < 0 || a.topk > MLA_MAX_TOPK) return MLA_ERR_INVALID_ARG;
+  if (a.topk > 0) {
+    if (a.q_len != 1) return MLA_ERR_INVALID_ARG;
+    // Row ids are int32; the prepass indexes batch * stride entries.
+    if (int64_t(a.num_blocks) * a.block_size > INT32_MAX) return MLA_ERR_INVALID_ARG;
+    if (int64_t(a.batch) * mla::sparse_stride(a.topk) > INT32_MAX) return MLA_ERR_INVALID_ARG;
+  }
   if (a.batch == 0) return MLA_OK;
   if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out || !a.workspace)
     return MLA_ERR_INVALID_ARG;
+  if (a.topk > 0 && (!a.indices || !aligned(a.indices, 4))) return MLA_ERR_INVALID_ARG;
   if (!aligned(a.q, 16) || !aligned(a.kv_cache, 16) || !aligned(a.out, 16) ||
       !aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) || !aligned(a.workspace, 256))
     return MLA_ERR_INVALID_ARG;
   if (a.lse && !aligned(a.lse, 4)) return MLA_ERR_INVALID_ARG;
   // Metadata alone must fit whatever the mode.
-  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.rows(), 0, 1).total)
+  if (a.workspace_bytes < mla::workspace_layout(a.batch, a.rows(), 0, 1, a.topk).total)
     return MLA_ERR_WORKSPACE_TOO_SMALL;
   if (a.num_splits > 0) {
     // One workgroup per (request, split, 16-row tile) and per (request, tile,
@@ -127,7 +137,7 @@ mla_status_t validate_decode(const DecodeArgs& a) {
         int64_t(a.batch) * tiles * (MLA_HEAD_DIM_V / 64) > INT32_MAX)
       return MLA_ERR_INVALID_ARG;
     WorkspaceLayout w =
-        mla::workspace_layout(a.batch, a.rows(), forced_rows(a.batch, a.num_splits), 1);
+        mla::workspace_layout(a.batch, a.rows(), forced_rows(a.batch, a.num_splits), 1, a.topk);
     if (a.workspace_bytes < w.total) return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
   return MLA_OK;
@@ -144,17 +154,20 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
   if (a.batch == 0) return MLA_OK;
 
-  const int64_t cap = int64_t(a.max_blocks) * a.block_size;
+  // Tokens per request the kernels walk: the cache (dense) or the list (sparse).
+  const int64_t cache_cap = int64_t(a.max_blocks) * a.block_size;
+  const bool sparse = a.topk > 0;
+  const int64_t cap = sparse ? a.topk : cache_cap;
   WorkspaceLayout w;
   int64_t max_parts = 0;
   const int32_t rows = a.rows();
   if (a.num_splits > 0) {
-    w = mla::workspace_layout(a.batch, rows, forced_rows(a.batch, a.num_splits), 1);
+    w = mla::workspace_layout(a.batch, rows, forced_rows(a.batch, a.num_splits), 1, a.topk);
   } else {
     // Largest partition count whose plan and partial rows fit the workspace.
     max_parts = mla::max_partitions(dev.cus, rows, a.kv_dtype == MLA_KV_FP8_E4M3);
     auto layout = [&](int64_t parts) {
-      return mla::workspace_layout(a.batch, rows, auto_rows(a.batch, parts, cap), parts);
+      return mla::workspace_layout(a.batch, rows, auto_rows(a.batch, parts, cap), parts, a.topk);
     };
     while (max_parts > 1 && layout(max_parts).total > a.workspace_bytes)
       max_parts = max_parts * 3 / 4;
@@ -176,7 +189,19 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   };
 
   if (!rec(0)) return MLA_ERR_HIP;
-  if (mla::launch_plan(a.seq_lens, a.batch, int32_t(cap), a.num_splits, int32_t(max_parts), w,
+  // The plan sees every sparse request as topk tokens long.
+  const int32_t* lens = a.seq_lens;
+  if (sparse) {
+    int32_t* sp_len = reinterpret_cast<int32_t*>(ws + w.sp_len);
+    if (mla::launch_sparse_rows(a.indices, a.topk, a.block_table, a.seq_lens, a.batch,
+                                a.max_blocks, a.num_blocks, bs_log2_of(a.block_size),
+                                int32_t(cache_cap), int32_t(mla::sparse_stride(a.topk)),
+                                reinterpret_cast<int32_t*>(ws + w.sp_rows), sp_len,
+                                ws + w.zero_row, s) != hipSuccess)
+      return MLA_ERR_HIP;
+    lens = sp_len;
+  }
+  if (mla::launch_plan(lens, a.batch, int32_t(cap), a.num_splits, int32_t(max_parts), w,
                        a.workspace, s) != hipSuccess)
     return MLA_ERR_HIP;
   if (!rec(1)) return MLA_ERR_HIP;
@@ -185,7 +210,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.q = static_cast<const uint16_t*>(a.q);
   args.kv = static_cast<const uint8_t*>(a.kv_cache);
   args.block_table = a.block_table;
-  args.seq_lens = a.seq_lens;
+  args.seq_lens = lens;
   args.out = static_cast<uint16_t*>(a.out);
   args.lse = a.lse;
   args.part_out = part_out;
@@ -210,6 +235,9 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.rows_cap = int32_t(w.rows);
   args.head_tiles = mla::head_tiles(rows);
   args.head_groups = (args.head_tiles + 3) / 4;
+  args.sparse_rows = sparse ? reinterpret_cast<const int32_t*>(ws + w.sp_rows) : nullptr;
+  args.sparse_stride = sparse ? int32_t(mla::sparse_stride(a.topk)) : 0;
+  args.zero_row = sparse ? ws + w.zero_row : nullptr;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
   int64_t parts_launched = (parts + 7) / 8 * 8;
   if (parts_launched * args.head_tiles > INT32_MAX) return MLA_ERR_INVALID_ARG;
@@ -297,6 +325,50 @@ mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,
   DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, q_len,
                block_size, num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype,
                kv_scale, workspace, workspace_bytes, static_cast<hipStream_t>(stream)};
+  return run_decode(a, events);
+}
+
+size_t mla_get_workspace_size_sparse(int64_t batch, int64_t num_heads, int64_t topk,
+                                     int64_t num_splits, int64_t num_cus) {
+  if (batch < 0 || batch > INT32_MAX / 2) return 0;
+  if (num_heads < 1 || num_heads > MLA_MAX_HEADS) return 0;
+  if (topk < 1 || topk > MLA_MAX_TOPK) return 0;
+  if (num_splits < 0 || num_splits > MLA_MAX_FORCED_SPLITS) return 0;
+  if (num_cus <= 0) num_cus = kDefaultCus;
+  if (num_splits > 0)
+    return mla::workspace_layout(batch, num_heads, forced_rows(batch, num_splits), 1, topk).total;
+  const int64_t parts = mla::max_partitions(num_cus, num_heads, 0);
+  return mla::workspace_layout(batch, num_heads, auto_rows(batch, parts, topk), parts, topk)
+      .total;
+}
+
+mla_status_t mla_decode_sparse(const void* q, const void* kv_cache, const int32_t* block_table,
+                               const int32_t* seq_lens, const int32_t* indices, int32_t topk,
+                               void* out, float* lse, float scale, int32_t num_heads,
+                               int32_t block_size, int32_t num_splits, int32_t batch,
+                               int32_t max_blocks_per_seq, int32_t num_blocks, int32_t kv_dtype,
+                               float kv_scale, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+  if (topk < 1) return MLA_ERR_INVALID_ARG;
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, 1, block_size,
+               num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype, kv_scale,
+               workspace, workspace_bytes, static_cast<hipStream_t>(stream), indices, topk};
+  return run_decode(a, nullptr);
+}
+
+mla_status_t mla_decode_sparse_profiled(const void* q, const void* kv_cache,
+                                        const int32_t* block_table, const int32_t* seq_lens,
+                                        const int32_t* indices, int32_t topk, void* out,
+                                        float* lse, float scale, int32_t num_heads,
+                                        int32_t block_size, int32_t num_splits, int32_t batch,
+                                        int32_t max_blocks_per_seq, int32_t num_blocks,
+                                        int32_t kv_dtype, float kv_scale, void* workspace,
+                                        size_t workspace_bytes, void* stream,
+                                        void* const* events) {
+  if (topk < 1 || !events) return MLA_ERR_INVALID_ARG;
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, 1, block_size,
+               num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype, kv_scale,
+               workspace, workspace_bytes, static_cast<hipStream_t>(stream), indices, topk};
   return run_decode(a, events);
 }
 

@@ -33,6 +33,9 @@ struct WorkspaceLayout {
   size_t split;     // int32[parts]: requests with partial rows
   size_t part_lse;  // float[rows][num_heads]
   size_t part_out;  // float[rows][num_heads][512]
+  size_t sp_rows;   // sparse: int32[batch][sparse_stride] physical row ids
+  size_t sp_len;    // sparse: int32[batch] list length per request
+  size_t zero_row;  // sparse: 1152 zero bytes
   size_t total;
   int64_t rows;
   int64_t parts;
@@ -40,8 +43,12 @@ struct WorkspaceLayout {
 
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Row-id entries per request of the sparse prepass: the list rounded up to
+// whole units plus one 64-token tile, so every tile's id load stays inside.
+inline int64_t sparse_stride(int64_t topk) { return (topk + kUnit - 1) / kUnit * kUnit + 64; }
+
 inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_t rows,
-                                        int64_t parts) {
+                                        int64_t parts, int64_t topk = 0) {
   WorkspaceLayout w;
   if (parts < 1) parts = 1;
   size_t off = 0;
@@ -61,6 +68,15 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
   off += align256(size_t(rows) * size_t(num_heads) * 4);
   w.part_out = off;
   off += align256(size_t(rows) * size_t(num_heads) * kDV * 4);
+  w.sp_rows = w.sp_len = w.zero_row = off;
+  if (topk > 0) {
+    w.sp_rows = off;
+    off += align256(size_t(batch) * size_t(sparse_stride(topk)) * 4);
+    w.sp_len = off;
+    off += align256(size_t(batch) * 4);
+    w.zero_row = off;
+    off += align256(size_t(kDK) * 2);
+  }
   w.total = off;
   w.rows = rows;
   w.parts = parts;
@@ -117,6 +133,11 @@ struct AttnArgs {
   int32_t rows_cap;          // partial rows in part_out / part_lse
   int32_t head_tiles;        // ceil(rows / 16)
   int32_t head_groups;       // workgroups per partition of the many-head kernel
+  // Sparse decode (null otherwise): physical row id (-1: none) of each listed
+  // position, sparse_stride ids per request, and a zeroed row to read instead.
+  const int32_t* sparse_rows;
+  int32_t sparse_stride;
+  const uint8_t* zero_row;
 };
 
 // Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
@@ -132,6 +153,14 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
 hipError_t launch_combine(const float* part_out, const float* part_lse,
                           const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
                           int32_t num_heads, int zero_empty, hipStream_t stream);
+
+// Sparse decode prepass: rows[b * stride + k] = physical row of listed
+// position k of request b, or -1; eff_len[b] = topk; zero_row = 1152 zero bytes.
+hipError_t launch_sparse_rows(const int32_t* indices, int32_t topk, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t batch, int32_t max_blocks,
+                              int32_t num_blocks, int32_t bs_log2, int32_t cap_tokens,
+                              int32_t stride, int32_t* rows, int32_t* eff_len, void* zero_row,
+                              hipStream_t stream);
 
 // Combine of the automatic plan: only the requests listed in `split`
 // (header[2] of them, at most `max_split`).

@@ -972,6 +972,27 @@ __device__ __forceinline__ void lds_read_p4(uint32_t p_addr, uint32_t e_addr, u3
       : "memory");
 }
 
+// Nine LDS dword reads at per-lane addresses, with an explicit wait (no wait
+// on the ring's loads in flight).
+__device__ __forceinline__ void lds_read_ids9(const uint32_t (&ad)[9], int (&v)[9]) {
+  asm volatile(
+      "ds_read_b32 %0, %9\n\t"
+      "ds_read_b32 %1, %10\n\t"
+      "ds_read_b32 %2, %11\n\t"
+      "ds_read_b32 %3, %12\n\t"
+      "ds_read_b32 %4, %13\n\t"
+      "ds_read_b32 %5, %14\n\t"
+      "ds_read_b32 %6, %15\n\t"
+      "ds_read_b32 %7, %16\n\t"
+      "ds_read_b32 %8, %17\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+        "=&v"(v[6]), "=&v"(v[7]), "=&v"(v[8])
+      : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+        "v"(ad[7]), "v"(ad[8])
+      : "memory");
+}
+
 __device__ __forceinline__ f32x4_t mfma_e4m3_128(const i32x8_t& a, const i32x8_t& b,
                                                  const f32x4_t& c, int scale_a) {
   // Format code 0 = E4M3 for both operands; E8M0 scales (127 = 2^0).
@@ -998,10 +1019,18 @@ __device__ __forceinline__ f32x4_t mfma_e4m3_128(const i32x8_t& a, const i32x8_t
 // carry the tile's exponent rise in the op's E8M0 scale. A head tile whose
 // logits rise more than 64 above its frame is recomputed in a second pass
 // with the frame preset (the other tiles then contribute zero weights).
+//
+// SPARSE: a request's tokens are the positions of its top-k list, already
+// turned into physical row ids (-1: no token) by sparse_rows_kernel. Each
+// P.V wave fetches a quarter of tile k's ids into an eight-slot LDS ring two
+// tiles ahead of tile k's rows (one extra ring load per tile and wave; the
+// order per step is rows of tile s + 2, then ids of tile s + 4) and reads
+// its nine row ids back when it issues the tile. A missing token is read
+// from a zero row in the workspace and its logit is masked.
 constexpr int kMhWaves = 8;
 constexpr int kMhThreads = 64 * kMhWaves;
 
-template <int KV_FP8>
+template <int KV_FP8, int SPARSE>
 __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
   constexpr int kTok = KV_FP8 ? 4 * kUnit : 2 * kUnit;   // tokens per tile
   constexpr int kUnits = kTok / kUnit;
@@ -1017,6 +1046,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
   __shared__ float lbuf[4][kHeadTile];      // final softmax denominators
   __shared__ int redo_tile[4];
   __shared__ int redo_any;
+  __shared__ __attribute__((aligned(16))) int32_t sp_ids[SPARSE ? 8 : 1][kTok];  // row ids
 
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
@@ -1045,9 +1075,13 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
     const int pos = i * kThreads + (tid & (kThreads - 1));
     const int t = pos / kRowCh, sl = pos - (pos / kRowCh) * kRowCh;
     const int ch = KV_FP8 ? (sl ^ fp8_swizzle(t)) : (sl ^ (t & 7));
-    dma_off[i] = uint32_t((t & 15) * kRowB + ch * 16);
+    // Sparse: (token of the tile << 16) | byte offset in its row.
+    dma_off[i] = SPARSE ? (uint32_t(t) << 16) | uint32_t(ch * 16)
+                        : uint32_t((t & 15) * kRowB + ch * 16);
     dma_unit |= uint32_t(t >> 4) << (2 * i);
   }
+  const uint32_t ids_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (void __attribute__((address_space(3)))*)(&sp_ids[0][0])));
   const uint32_t ring_lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
       (void __attribute__((address_space(3)))*)(&ring[0][0])));
   const int bs_mask = (1 << a.bs_log2) - 1;
@@ -1123,6 +1157,33 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
         __builtin_amdgcn_global_load_lds(
             base + dma_off[i], (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16),
             16, 0, 0);
+      }
+    };
+    // Sparse: ids of tile k (a quarter per P.V wave) into slot k % 8.
+    auto issue_ids = [&](int k) {
+      constexpr int kPer = kTok / 4;
+      if (lane < kPer) {
+        const int32_t* src = a.sparse_rows + size_t(b) * a.sparse_stride + size_t(u0) * kUnit +
+                             size_t(k) * kTok + wave * kPer + lane;
+        __builtin_amdgcn_global_load_lds(
+            src, (void __attribute__((address_space(3)))*)(&sp_ids[k & 7][wave * kPer]), 4, 0, 0);
+      }
+    };
+    // Sparse: rows of tile k from its ids (already in LDS).
+    auto issue_tile_sparse = [&](int k) {
+      uint32_t ad[kDmaPerThread];
+      int rid[kDmaPerThread];
+      const uint32_t slot = ids_lds + uint32_t((k & 7) * kTok * 4);
+#pragma unroll
+      for (int i = 0; i < kDmaPerThread; ++i) ad[i] = slot + ((dma_off[i] >> 16) << 2);
+      lds_read_ids9(ad, rid);
+      uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
+#pragma unroll
+      for (int i = 0; i < kDmaPerThread; ++i) {
+        const uint32_t ch16 = dma_off[i] & 0xffffu;
+        const uint8_t* src = rid[i] >= 0 ? a.kv + size_t(rid[i]) * kRowB + ch16 : a.zero_row + ch16;
+        __builtin_amdgcn_global_load_lds(
+            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0, 0);
       }
     };
 
@@ -1212,6 +1273,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
         redo = false;
         wave_barrier_all();  // ring and P buffer of the previous pass or piece are free
         wait_vmem<0>();      // q
+        if constexpr (SPARSE) wave_barrier_all();  // the P.V waves' first ids are in LDS
         for (int s = 0; s <= ntiles; ++s) {
           wave_barrier_lds();  // barrier 1: tile s is in the ring
           wave_barrier_lds();  // barrier 2: the P.V waves hold P of tile s - 1
@@ -1291,6 +1353,17 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
               __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             }
             __builtin_amdgcn_sched_group_barrier(0x008, 9, 0);
+            if constexpr (SPARSE) {
+              // Listed positions that name no token get no weight.
+#pragma unroll
+              for (int u = 0; u < kUnits; ++u) {
+                const int4 id = *reinterpret_cast<const int4*>(&sp_ids[s & 7][16 * u + 4 * g]);
+                if (id.x < 0) x[u][0] = -INFINITY;
+                if (id.y < 0) x[u][1] = -INFINITY;
+                if (id.z < 0) x[u][2] = -INFINITY;
+                if (id.w < 0) x[u][3] = -INFINITY;
+              }
+            }
             float mt = -INFINITY;
 #pragma unroll
             for (int u = 0; u < kUnits; ++u)
@@ -1394,9 +1467,30 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
           }
         }
         wave_barrier_all();  // ring and P buffer of the previous pass or piece are free
-        for (int k = 0; k < 2 && k < ntiles; ++k) issue_tile(k);
+        if constexpr (SPARSE) {
+          for (int k = 0; k < 2 && k < ntiles; ++k) issue_ids(k);
+          wait_vmem<0>();
+          wave_barrier_all();  // ids of tiles 0 and 1 from every P.V wave
+          for (int k = 0; k < 2 && k < ntiles; ++k) {
+            issue_tile_sparse(k);
+            if (k + 2 < ntiles) issue_ids(k + 2);
+          }
+        } else {
+          for (int k = 0; k < 2 && k < ntiles; ++k) issue_tile(k);
+        }
         for (int s = 0; s <= ntiles; ++s) {
-          if (s < ntiles) wait_ring<1>(ntiles - 1 - s);  // tile s landed
+          if constexpr (SPARSE) {
+            // Tile s and the ids of tile s + 2 landed: loads issued after
+            // them are the rows of tile s + 1 and the ids of tile s + 3.
+            if (s + 3 < ntiles)
+              wait_vmem<kDmaPerThread + 1>();
+            else if (s + 1 < ntiles)
+              wait_vmem<kDmaPerThread>();
+            else if (s < ntiles)
+              wait_vmem<0>();
+          } else {
+            if (s < ntiles) wait_ring<1>(ntiles - 1 - s);  // tile s landed
+          }
           wave_barrier_lds();  // barrier 1: P of tile s - 1 is in pbuf
           u32x4_t pv_p[4];   // bf16 A operands
           i32x8_t pv_pa[4];  // E4M3 A operands
@@ -1417,7 +1511,12 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
             }
           }
           wave_barrier_lds();  // barrier 2: P taken, pbuf may be overwritten
-          if (s + 2 < ntiles) issue_tile(s + 2);
+          if constexpr (SPARSE) {
+            if (s + 2 < ntiles) issue_tile_sparse(s + 2);
+            if (s + 4 < ntiles) issue_ids(s + 4);
+          } else {
+            if (s + 2 < ntiles) issue_tile(s + 2);
+          }
           if (s == 0) continue;
           const int k = s - 1;
           const uint32_t st = ring_lds + uint32_t(k % kStages) * kTileBytesBf16;
@@ -1631,12 +1730,55 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
                             hipStream_t stream) {
   dim3 grid(unsigned(parts_launched) * unsigned(args.head_tiles));
   const dim3 grid_mh(unsigned(parts_launched) * unsigned(args.head_groups));
-  if (kv_fp8)
-    hipLaunchKernelGGL(attn_mh_kernel<1>, grid_mh, dim3(kMhThreads), 0, stream, args);
-  else if (args.head_tiles == 1)
+  if (args.sparse_rows) {
+    if (kv_fp8)
+      hipLaunchKernelGGL((attn_mh_kernel<1, 1>), grid_mh, dim3(kMhThreads), 0, stream, args);
+    else
+      hipLaunchKernelGGL((attn_mh_kernel<0, 1>), grid_mh, dim3(kMhThreads), 0, stream, args);
+  } else if (kv_fp8) {
+    hipLaunchKernelGGL((attn_mh_kernel<1, 0>), grid_mh, dim3(kMhThreads), 0, stream, args);
+  } else if (args.head_tiles == 1) {
     hipLaunchKernelGGL(attn_ws_kernel, grid, dim3(kWsThreads), 0, stream, args);
-  else
-    hipLaunchKernelGGL(attn_mh_kernel<0>, grid_mh, dim3(kMhThreads), 0, stream, args);
+  } else {
+    hipLaunchKernelGGL((attn_mh_kernel<0, 0>), grid_mh, dim3(kMhThreads), 0, stream, args);
+  }
+  return hipGetLastError();
+}
+
+// Sparse decode: physical row id of every listed position (-1 where the
+// entry is outside [0, seq_len) or its block id is outside the cache), the
+// list length as every request's token count, and a zero row.
+__global__ void __launch_bounds__(256) sparse_rows_kernel(
+    const int32_t* indices, int32_t topk, const int32_t* block_table, const int32_t* seq_lens,
+    int32_t batch, int32_t max_blocks, int32_t num_blocks, int32_t bs_log2, int32_t cap_tokens,
+    int32_t stride, int32_t* rows, int32_t* eff_len, uint32_t* zero_row) {
+  const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < kDK * 2 / 4) zero_row[i] = 0u;
+  if (i >= int64_t(batch) * stride) return;
+  const int b = int(i / stride), k = int(i - int64_t(b) * stride);
+  if (k == 0) eff_len[b] = topk;
+  int row = -1;
+  if (k < topk) {
+    const int t = indices[size_t(b) * topk + k];
+    const int n = clamp_len(seq_lens[b], cap_tokens);
+    if (t >= 0 && t < n) {
+      const int blk = block_table[size_t(b) * max_blocks + (t >> bs_log2)];
+      if (blk >= 0 && blk < num_blocks) row = (blk << bs_log2) + (t & ((1 << bs_log2) - 1));
+    }
+  }
+  rows[i] = row;
+}
+
+hipError_t launch_sparse_rows(const int32_t* indices, int32_t topk, const int32_t* block_table,
+                              const int32_t* seq_lens, int32_t batch, int32_t max_blocks,
+                              int32_t num_blocks, int32_t bs_log2, int32_t cap_tokens,
+                              int32_t stride, int32_t* rows, int32_t* eff_len, void* zero_row,
+                              hipStream_t stream) {
+  const int64_t n = int64_t(batch) * stride;
+  const int64_t nb = (n > kDK * 2 / 4 ? n : kDK * 2 / 4) + 255;
+  hipLaunchKernelGGL(sparse_rows_kernel, dim3(unsigned(nb / 256)), dim3(256), 0, stream, indices,
+                     topk, block_table, seq_lens, batch, max_blocks, num_blocks, bs_log2,
+                     cap_tokens, stride, rows, eff_len, static_cast<uint32_t*>(zero_row));
   return hipGetLastError();
 }
 

@@ -56,6 +56,7 @@ def test_constants_match_header():
     assert int(defines["MLA_MAX_HEADS"]) == mla.MAX_HEADS == 128
     assert int(defines["MLA_MAX_FORCED_SPLITS"]) == mla.MAX_FORCED_SPLITS == 16
     assert int(defines["MLA_MAX_QUERY_LEN"]) == mla.MAX_QUERY_LEN == 16
+    assert int(defines["MLA_MAX_TOPK"]) == mla.MAX_TOPK == 65536
     enums = dict((k, int(v)) for k, v in re.findall(r"(MLA_\w+) = (-?\d+)", text))
     for name in ("MLA_OK", "MLA_ERR_INVALID_ARG", "MLA_ERR_UNSUPPORTED",
                  "MLA_ERR_WORKSPACE_TOO_SMALL", "MLA_ERR_NO_DEVICE", "MLA_ERR_HIP",
@@ -216,6 +217,61 @@ def test_combine_rejects():
         mla.MLA_ERR_INVALID_ARG
     if not HAS_GPU:
         assert lib.mla_combine(f, f, f, f, None, 2, 16, None) == mla.MLA_ERR_NO_DEVICE
+
+
+def _layout_sparse(batch, heads, rows, parts, topk):
+    a = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    stride = (topk + 15) // 16 * 16 + 64
+    return _layout(batch, heads, rows, parts) + a(batch * stride * 4) + a(batch * 4) + a(1152)
+
+
+def test_workspace_size_sparse():
+    # The plan sees every request as topk tokens long.
+    assert mla.get_workspace_size_sparse(512, 16, 2048, 0, 0) == \
+        _layout_sparse(512, 16, 512, 256, 2048)
+    assert mla.get_workspace_size_sparse(64, 128, 2048, 0, 0) == \
+        _layout_sparse(64, 128, 256, 128, 2048)
+    assert mla.get_workspace_size_sparse(3, 16, 100, 4, 0) == _layout_sparse(3, 16, 12, 1, 100)
+    for bad in ((1, 16, 0, 0, 0), (1, 16, 65537, 0, 0), (1, 0, 10, 0, 0), (1, 16, 10, 17, 0),
+                (-1, 16, 10, 0, 0)):
+        assert mla.get_workspace_size_sparse(*bad) == 0
+
+
+def _decode_sparse(**over):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, idx=FAKE, topk=64, out=FAKE, lse=None, scale=0.07,
+             heads=16, bs=32, splits=0, batch=2, max_blocks=4, num_blocks=8, kv_dtype=0,
+             kv_scale=1.0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(over)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return mla.library().mla_decode_sparse(
+        vp(a["q"]), vp(a["kv"]), vp(a["bt"]), vp(a["sl"]), vp(a["idx"]), a["topk"], vp(a["out"]),
+        vp(a["lse"]), a["scale"], a["heads"], a["bs"], a["splits"], a["batch"], a["max_blocks"],
+        a["num_blocks"], a["kv_dtype"], a["kv_scale"], vp(a["ws"]), a["ws_bytes"], None)
+
+
+SPARSE_INVALID = [dict(idx=None), dict(idx=FAKE + 2), dict(topk=0), dict(topk=65537),
+                  dict(topk=-1), dict(heads=129), dict(q=None), dict(bs=48),
+                  dict(num_blocks=1 << 26, bs=64)]
+
+
+@pytest.mark.parametrize("over", SPARSE_INVALID, ids=[str(d) for d in SPARSE_INVALID])
+def test_decode_sparse_rejects(over):
+    assert _decode_sparse(**over) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_decode_sparse_workspace_and_device():
+    need = mla.get_workspace_size_sparse(2, 16, 64, 3, 0)
+    assert _decode_sparse(splits=3, ws_bytes=need - 1) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+    if not HAS_GPU:
+        assert _decode_sparse(splits=3, ws_bytes=need) == mla.MLA_ERR_NO_DEVICE
+        assert _decode_sparse() == mla.MLA_ERR_NO_DEVICE
+
+
+def test_decode_sparse_profiled_requires_events():
+    lib = mla.library()
+    f = ctypes.c_void_p(FAKE)
+    args = [f, f, f, f, f, 64, f, None, 0.07, 16, 32, 0, 2, 4, 8, 0, 1.0, f, 1 << 30, None]
+    assert lib.mla_decode_sparse_profiled(*args, None) == mla.MLA_ERR_INVALID_ARG
 
 
 def test_combine_accepts_multi_token_rows():
