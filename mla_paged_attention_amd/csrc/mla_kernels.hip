@@ -1280,6 +1280,10 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
           if (s == ntiles) continue;
           u32x4_t pw[kPWords];
           int e_scale = 127;
+          // The logit wave is the step's critical path: its K reads and
+          // matrix ops take precedence over the P.V wave sharing the SIMD,
+          // whose matrix ops then fill the gaps and the softmax below.
+          __builtin_amdgcn_s_setprio(3);
           if (work) {
             const uint32_t st = ring_lds + uint32_t(s % kStages) * kTileBytesBf16;
             int nv[kUnits];
@@ -1364,6 +1368,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
                 if (id.w < 0) x[u][3] = -INFINITY;
               }
             }
+            __builtin_amdgcn_s_setprio(0);
             float mt = -INFINITY;
 #pragma unroll
             for (int u = 0; u < kUnits; ++u)
@@ -1395,15 +1400,15 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
               const int e = rise > 0.f ? min(int(ceilf(rise)), int(kHeadsSlack)) : 0;
               const float fe = m_use + float(e);
               unsigned ph[4], pl[4];
-              float lt = 0.f;
+              float lt = 0.f;   // sum of the stored weights 2^(x - fe + 8)
+              const float fe8 = fe - 8.f;
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
                 float ps[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                  const float pp = fast_exp2(x[u][r] - fe);
-                  lt += pp;
-                  ps[r] = pp * 256.f;
+                  ps[r] = fast_exp2(x[u][r] - fe8);
+                  lt += ps[r];
                 }
                 ph[u] = pack_e4m3x4_inrange(ps[0], ps[1], ps[2], ps[3]);
                 pl[u] = pack_e4m3x4_inrange(ps[0] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 0),
@@ -1411,7 +1416,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
                                             ps[2] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 2),
                                             ps[3] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 3));
               }
-              l_run += __builtin_amdgcn_ldexpf(lt, e);
+              l_run += __builtin_amdgcn_ldexpf(lt, e - 8);
               pw[0] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
               pw[kPWords - 1] = u32x4_t{pl[0], pl[1], pl[2], pl[3]};
               e_scale = 127 + e;
@@ -1420,6 +1425,9 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
 #pragma unroll
             for (int w = 0; w < kPWords; ++w) pw[w] = u32x4_t{0u, 0u, 0u, 0u};
           }
+          // (Scalar: executes on both sides of the branch above, so the
+          // priority is dropped here rather than in its else side.)
+          __builtin_amdgcn_s_setprio(0);
 #pragma unroll
           for (int w = 0; w < kPWords; ++w) pbuf[wq][lane][w] = pw[w];
           if (KV_FP8 && g == 0) ebuf[wq][c] = e_scale;
