@@ -48,6 +48,7 @@ namespace mla {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
@@ -993,6 +994,27 @@ __device__ __forceinline__ void lds_read_ids9(const uint32_t (&ad)[9], int (&v)[
       : "memory");
 }
 
+// Maximum over lanes c, c + 16, c + 32 and c + 48 (the four lane groups of
+// a 16-column fragment) with gfx950's lane-swap moves, which stay in
+// registers (no round trip through the LDS crossbar). One asm statement:
+// the compiler folds max(swap results) of the builtins to the first result.
+// Each swap reads a VGPR written by the instruction before it, so two wait
+// states (s_nop 1) separate them, as the compiler places them itself.
+__device__ __forceinline__ float max_over_lane_groups(float v) {
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane32_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\t"
+      "s_nop 1\n\t"
+      "v_permlane16_swap_b32 %0, %1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(v), "=&v"(t));
+  return v;
+}
+
 __device__ __forceinline__ f32x4_t mfma_e4m3_128(const i32x8_t& a, const i32x8_t& b,
                                                  const f32x4_t& c, int scale_a) {
   // Format code 0 = E4M3 for both operands; E8M0 scales (127 = 2^0).
@@ -1373,8 +1395,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
 #pragma unroll
             for (int u = 0; u < kUnits; ++u)
               mt = fmaxf(mt, fmaxf(fmaxf(x[u][0], x[u][1]), fmaxf(x[u][2], x[u][3])));
-            mt = fmaxf(mt, __shfl_xor(mt, 16));
-            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            mt = max_over_lane_groups(mt);
             m_seen = fmaxf(m_seen, mt);
             if (m_ref == -INFINITY) m_ref = mt;  // first tile (per head): the frame
             if (__ballot(mt > m_ref + kHeadsSlack) != 0ull) redo = true;  // wave-uniform
@@ -1411,10 +1432,11 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
                   lt += ps[r];
                 }
                 ph[u] = pack_e4m3x4_inrange(ps[0], ps[1], ps[2], ps[3]);
-                pl[u] = pack_e4m3x4_inrange(ps[0] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 0),
-                                            ps[1] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 1),
-                                            ps[2] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 2),
-                                            ps[3] - __builtin_amdgcn_cvt_f32_fp8(int(ph[u]), 3));
+                // Residuals against the rounded bytes 0-1 and 2-3, decoded in pairs.
+                const f32x2_t h01 = __builtin_amdgcn_cvt_pk_f32_fp8(int(ph[u]), false);
+                const f32x2_t h23 = __builtin_amdgcn_cvt_pk_f32_fp8(int(ph[u]), true);
+                pl[u] = pack_e4m3x4_inrange(ps[0] - h01[0], ps[1] - h01[1], ps[2] - h23[0],
+                                            ps[3] - h23[1]);
               }
               l_run += __builtin_amdgcn_ldexpf(lt, e - 8);
               pw[0] = u32x4_t{ph[0], ph[1], ph[2], ph[3]};
