@@ -44,6 +44,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_mla_attend_sparse.argtypes = [vp, vp, i32, ctypes.c_float, vp, vp, i64, i64,
                                              i64, i64, i64, ctypes.c_float, vp, i64, vp, vp]
     lib.oracle_mla_attend_sparse.restype = i32
+    lib.oracle_gemm_fp8_blockscale.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
+    lib.oracle_gemm_fp8_blockscale.restype = i32
     lib.oracle_lse_merge.argtypes = [vp, vp, i64, i64, vp, vp]
     lib.oracle_lse_merge.restype = i32
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
@@ -160,6 +162,45 @@ class Oracle:
         if rc != 0:
             raise ValueError(f"oracle_lse_merge failed with status {rc}")
         return out, lse
+
+    def gemm_fp8_blockscale(self, a, a_scale, b, b_scale):
+        """c [m, n] float64 of the block-scaled E4M3 projection (see the C source):
+        a uint8 [m, k], a_scale float32 [m, k/128], b uint8 [n, k],
+        b_scale float32 [ceil(n/128), k/128]."""
+        a = np.ascontiguousarray(a, dtype=np.uint8)
+        b = np.ascontiguousarray(b, dtype=np.uint8)
+        a_scale = np.ascontiguousarray(a_scale, dtype=np.float32)
+        b_scale = np.ascontiguousarray(b_scale, dtype=np.float32)
+        m, k = a.shape
+        n = b.shape[0]
+        if b.shape[1] != k or k % 128 or a_scale.shape != (m, k // 128) or \
+                b_scale.shape != ((n + 127) // 128, k // 128):
+            raise ValueError("shape mismatch")
+        c = np.empty((m, n), dtype=np.float64)
+        rc = self.lib.oracle_gemm_fp8_blockscale(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale),
+                                                 m, n, k, _ptr(c))
+        if rc != 0:
+            raise ValueError(f"oracle_gemm_fp8_blockscale failed with status {rc}")
+        return c
+
+    @staticmethod
+    def quant_fp8_groups(x):
+        """Per token and 128-wide group: scale = max(amax, 1e-10) / 448 and
+        code = E4M3FN(round to nearest even of clamp(x / scale, +-448)), every
+        step in fp32 (numpy's IEEE division; torch's E4M3FN cast rounds to
+        nearest even). x: bf16 [m, k] as a torch tensor. Returns (codes uint8
+        [m, k], scales float32 [m, k/128])."""
+        import torch
+        m, k = x.shape
+        if k % 128:
+            raise ValueError("k must be a multiple of 128")
+        xf = x.float().numpy().reshape(m, k // 128, 128)
+        amax = np.abs(xf).max(axis=2)
+        scale = np.maximum(amax, np.float32(1e-10)).astype(np.float32) / np.float32(448.0)
+        y = (xf / scale[:, :, None]).astype(np.float32)
+        y = np.clip(y, np.float32(-448.0), np.float32(448.0))
+        codes = torch.from_numpy(y.reshape(m, k)).to(torch.float8_e4m3fn).view(torch.uint8)
+        return codes.numpy(), scale.astype(np.float32)
 
     def e4m3_to_double(self, codes):
         codes = np.asarray(codes, dtype=np.uint8)

@@ -329,4 +329,41 @@ int oracle_lse_merge(const double* part_out, const double* part_lse, int64_t n_p
   return ORACLE_OK;
 }
 
-int oracle_abi_version(void) { return 2; }
+/*
+ * oracle_gemm_fp8_blockscale: the block-scaled E4M3 projection that sits beside
+ * MLA decode (the DeepSeek-R1 fused q/kv down-projection of issue #28427
+ * "DeepSeek-R1 KV Proj is Too Slow for TP": block FP8 weights, small decode M).
+ * The plain definition, dequantising every element:
+ *
+ *   c[i][j] = sum_k (e4m3(a[i][k]) * a_scale[i][k / 128]) *
+ *                   (e4m3(b[j][k]) * b_scale[j / 128][k / 128])
+ *
+ *  a        [m][k] E4M3FN codes (activations); a_scale [m][k / 128] fp32, one
+ *           per token and 128-wide group of k
+ *  b        [n][k] E4M3FN codes (weights, one row per output feature);
+ *           b_scale [ceil(n / 128)][k / 128] fp32, one per 128 x 128 block
+ *  c        [m][n] fp64
+ * k must be a multiple of 128. OpenMP over rows of c.
+ */
+int oracle_gemm_fp8_blockscale(const uint8_t* a, const float* a_scale, const uint8_t* b,
+                               const float* b_scale, int64_t m, int64_t n, int64_t k,
+                               double* c) {
+  if (!a || !a_scale || !b || !b_scale || !c || m < 0 || n < 0 || k < 0 || k % 128)
+    return ORACLE_BAD_ARG;
+  const int64_t kg = k / 128;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < m; ++i) {
+    for (int64_t j = 0; j < n; ++j) {
+      double sum = 0.0;
+      for (int64_t t = 0; t < k; ++t) {
+        double x = oracle_e4m3_to_double(a[i * k + t]) * (double)a_scale[i * kg + t / 128];
+        double w = oracle_e4m3_to_double(b[j * k + t]) * (double)b_scale[(j / 128) * kg + t / 128];
+        sum += x * w;
+      }
+      c[i * n + j] = sum;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_abi_version(void) { return 3; }

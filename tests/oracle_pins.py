@@ -471,12 +471,104 @@ def pin_sparse_split_merge(orc):
         assert _close(mo, full_out[b]) and _close(ml, full_lse[b]), f"sparse split-merge b={b}"
 
 
+def _rand_codes(rng, shape):
+    """Random E4M3FN codes without the two NaN codes."""
+    c = rng.integers(0, 256, size=shape, dtype=np.uint8)
+    c[(c & 0x7F) == 0x7F] = 0x3F
+    return c
+
+
+def _deq(codes):
+    """E4M3FN codes decoded by torch (a library routine, not the oracle)."""
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64)
+
+
+def pin_gemm_matches_torch_matmul(orc):
+    """The block-scaled projection equals torch's float64 matmul of the
+    dequantised operands (decoded by torch's float8_e4m3fn, scales broadcast
+    per 128-group and per 128 x 128 block)."""
+    rng = np.random.default_rng(21)
+    for m, n, k in ((3, 300, 384), (17, 128, 256), (1, 16, 128)):
+        a = _rand_codes(rng, (m, k))
+        b = _rand_codes(rng, (n, k))
+        sa = rng.uniform(0.01, 2.0, size=(m, k // 128)).astype(np.float32)
+        sb = rng.uniform(0.01, 2.0, size=((n + 127) // 128, k // 128)).astype(np.float32)
+        c = orc.gemm_fp8_blockscale(a, sa, b, sb)
+        da = _deq(a) * torch.from_numpy(np.repeat(sa, 128, axis=1)).double()
+        sbe = np.repeat(np.repeat(sb, 128, axis=0)[:n], 128, axis=1)
+        db = _deq(b) * torch.from_numpy(sbe).double()
+        ref = (da @ db.T).numpy()
+        mag = (da.abs() @ db.abs().T).numpy()
+        assert np.all(np.abs(c - ref) <= 1e-12 * (1 + mag)), f"gemm vs matmul (m={m} n={n} k={k})"
+
+
+def pin_gemm_closed_forms(orc):
+    """One-hot activations pick one weight column exactly; scaling one block's
+    weight scale scales exactly that block's contribution (linearity)."""
+    rng = np.random.default_rng(22)
+    n, k, k0 = 200, 384, 257
+    b = _rand_codes(rng, (n, k))
+    sb = rng.uniform(0.5, 2.0, size=(2, 3)).astype(np.float32)
+    a = np.zeros((1, k), np.uint8)
+    a[0, k0] = 0x38                                    # E4M3FN code of 1.0
+    c = orc.gemm_fp8_blockscale(a, np.ones((1, 3), np.float32), b, sb)
+    col = torch.from_numpy(b[:, k0].copy()).view(torch.float8_e4m3fn).double().numpy()
+    want = col * sb[np.arange(n) // 128, k0 // 128].astype(np.float64)
+    assert (c[0] == want).all(), "one-hot row must select the weight column exactly"
+    a = _rand_codes(rng, (4, k))
+    sa = rng.uniform(0.5, 2.0, size=(4, 3)).astype(np.float32)
+    base = orc.gemm_fp8_blockscale(a, sa, b, sb)
+    sb2 = sb.copy()
+    sb2[1, 2] *= 2                                     # rows 128..199, k 256..383
+    only = np.zeros_like(sa)
+    only[:, 2] = sa[:, 2]
+    part = orc.gemm_fp8_blockscale(a, only, b, sb)     # contribution of group 2 alone
+    got = orc.gemm_fp8_blockscale(a, sa, b, sb2)
+    want = base.copy()
+    want[:, 128:] += part[:, 128:]
+    assert np.allclose(got, want, rtol=1e-12, atol=1e-12), "block scale must act on its block"
+
+
+def pin_quant_groups(orc):
+    """Group quantisation: each group's largest magnitude maps to +-448
+    exactly; an all-zero group gives zero codes and scale 1e-10/448; every code is
+    the nearest E4M3FN value to x / scale (ties to the even code), found by
+    brute force over all codes decoded by the oracle's own decoder."""
+    gen = torch.Generator().manual_seed(23)
+    x = (torch.randn((5, 384), generator=gen) * torch.tensor([1e-3, 1.0, 30.0, 1e4, 0.0])[:, None])
+    x = x.to(torch.bfloat16)
+    x[0, 100] = 0.0
+    codes, scale = orc.quant_fp8_groups(x)
+    xf = x.float().numpy().reshape(5, 3, 128)
+    vals = orc.e4m3_to_double(np.arange(256, dtype=np.uint8))
+    finite = ~np.isnan(vals)
+    for i in range(5):
+        for g in range(3):
+            grp = xf[i, g]
+            cg = codes[i, g * 128:(g + 1) * 128]
+            if np.abs(grp).max() == 0:
+                # +0 and -0 keep their sign bit: codes 0x00 and 0x80
+                assert (vals[cg] == 0).all() and scale[i, g] == np.float32(1e-10) / np.float32(448)
+                continue
+            j = int(np.argmax(np.abs(grp)))
+            assert vals[cg[j]] == np.sign(grp[j]) * 448.0, "group maximum must map to +-448"
+            y = np.clip((grp / scale[i, g]).astype(np.float32), -448, 448).astype(np.float64)
+            for t in range(128):
+                d = np.abs(vals - y[t])
+                d[~finite] = np.inf
+                best = np.flatnonzero(d == d.min())
+                if len(best) > 1:                        # tie: the even code
+                    best = best[(best & 1) == 0]
+                assert vals[cg[t]] == vals[best[0]], f"code not nearest (row {i}, group {g})"
+
+
 PINS = [pin_e4m3_decode, pin_bf16_widen, pin_sdpa_identity_table, pin_sdpa_shuffled_pages,
         pin_closed_forms, pin_empty_request, pin_split_merge, pin_merge_closed_form,
         pin_rope_shift, pin_head_padding, pin_block_permutation, pin_batch_independence,
         pin_fp8_dequant, pin_multi_token_causal_sdpa, pin_multi_token_rows_are_single_decodes,
         pin_multi_token_split_merge, pin_sparse_all_positions_is_dense,
-        pin_sparse_sdpa_on_gathered_rows, pin_sparse_closed_forms, pin_sparse_split_merge]
+        pin_sparse_sdpa_on_gathered_rows, pin_sparse_closed_forms, pin_sparse_split_merge,
+        pin_gemm_matches_torch_matmul, pin_gemm_closed_forms, pin_quant_groups]
 
 
 def main(argv=None) -> int:

@@ -44,6 +44,11 @@ MUTANTS = [
     ("sparse_q_row", "qv[d] = bf16_bits_to_double(q[(b * num_heads + h) * ORACLE_D + d]);",
      "qv[d] = bf16_bits_to_double(q[((h % batch) * num_heads + (b % num_heads)) * ORACLE_D + d]);"),
     ("sparse_scale_dropped", "x[j] = s * dot;", "x[j] = dot;"),
+    ("gemm_neighbour_element", "oracle_e4m3_to_double(a[i * k + t])",
+     "oracle_e4m3_to_double(a[i * k + (t ^ 1)])"),
+    ("gemm_weight_scale_group0", "(double)b_scale[(j / 128) * kg + t / 128]",
+     "(double)b_scale[(j / 128) * kg]"),
+    ("gemm_act_scale_group0", "(double)a_scale[i * kg + t / 128]", "(double)a_scale[i * kg]"),
     ("out_row_token_head_transposed", "int64_t row_out = (i * q_len + qi) * num_heads + h;",
      "int64_t row_out = (i * num_heads + h) * q_len + qi;"),
     ("e4m3_bias", "exponent - 7);", "exponent - 8);"),
