@@ -166,6 +166,53 @@ def calib_copy(torch, dev, nbytes: int, reps: int) -> int:
     return 0
 
 
+def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, warmup: int) -> int:
+    """Block-scaled E4M3 projection at decode batch m (DeepSeek-R1 fused q/kv
+    down-projection by default: n = 2112, k = 7168): one JSON line with us per
+    GEMM and its roofline. Weights rotate across copies of >= 1 GB in total so
+    that HBM, not the memory-side cache, is measured."""
+    a, sa, b, sb = workloads.make_gemm(m, n, k, seed=11)
+    copies = max(2, math.ceil(ROTATE_MIN_BYTES / (n * k)))
+    bs = [(b.to(dev), sb.to(dev)) for _ in range(copies)]
+    a, sa = a.to(dev), sa.to(dev)
+    out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
+    avg = statistics.fmean(us)
+    alg_bytes = m * k + n * k + 4 * m * (k // 128) + 4 * ((n + 127) // 128) * (k // 128) + 2 * m * n
+    flops = 2 * m * n * k
+    t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)
+    t_mfma = flops / (PEAK_MFMA_TFLOPS["fp8"] * 1e12)
+    gbps = alg_bytes / (avg * 1e-6) / 1e9
+    tflops = flops / (avg * 1e-6) / 1e12
+    if t_mfma > t_hbm:
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS["fp8"],
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS["fp8"], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    roof.update({"kernel": "mla::gemm_fp8_kernel", "algorithmic_bytes_per_launch": alg_bytes,
+                 "algorithmic_flops_per_launch": flops, "traffic": None})
+    print(json.dumps({
+        "metric": "block-fp8 projection us/call at decode batch", "value": round(avg, 2),
+        "unit": "us/call", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "higher_is_better": False, "dtype": "fp8", "data": "synthetic",
+        "config": {"workload": f"gemm-fp8-m{m}", "m": m, "n": n, "k": k,
+                   "scales": "activation 1x128, weight 128x128"},
+        "us_p10_p90": [round(us[len(us) // 10], 2), round(us[(9 * len(us)) // 10], 2)],
+        "roofline": roof}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +224,10 @@ def main(argv=None) -> int:
                     help="query tokens per request (speculative decoding, causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--gemm", type=int, default=0, metavar="M",
+                    help="instead of decoding, time the block-scaled E4M3 projection at "
+                         "decode batch M (n = 2112, k = 7168 unless --gemm-nk)")
+    ap.add_argument("--gemm-nk", type=int, nargs=2, default=(2112, 7168), metavar=("N", "K"))
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of decoding, run plain device copies and reductions of "
                          "MIB MiB (HBM counter calibration and practical bandwidth)")
@@ -200,6 +251,9 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     if args.calib_copy:
         return calib_copy(torch, dev, args.calib_copy << 20, max(args.steps, 1))
+    if args.gemm:
+        return bench_gemm(torch, mla, workloads, dev, args.gemm, *args.gemm_nk, args.steps,
+                          args.warmup)
     mla.library()  # fail loudly now if the HIP library is missing
 
     label = args.config if args.q_len == 1 else f"{args.config}-q{args.q_len}"

@@ -56,6 +56,10 @@ extern "C" {
 #define MLA_MAX_QUERY_LEN 16   /* query tokens per request (mla_decode_multi_token) */
 #define MLA_MAX_FORCED_SPLITS 16
 #define MLA_MAX_TOPK 65536     /* listed positions per request (mla_decode_sparse) */
+#define MLA_FP8_GROUP 128      /* k per scale group of the block-scaled E4M3 GEMM */
+#define MLA_GEMM_MAX_M 65536   /* tokens per mla_gemm_fp8_blockscale call */
+#define MLA_GEMM_MAX_N 65536
+#define MLA_GEMM_MAX_K 65536
 
 typedef enum {
   MLA_OK = 0,
@@ -266,6 +270,38 @@ mla_status_t mla_decode_sparse_profiled(const void* q, const void* kv_cache,
 mla_status_t mla_combine(const float* partial_out, const float* partial_lse,
                          const int32_t* split_indptr, void* out, float* lse, int32_t batch,
                          int32_t num_heads, void* stream);
+
+/*
+ * The projection beside the decode path: the block-scaled E4M3 GEMM of the
+ * DeepSeek-R1 fused q/kv down-projection (issue #28427, "DeepSeek-R1 KV Proj
+ * is Too Slow for TP": block FP8 weights at a handful of decode tokens,
+ * where a swapped-operand kernel wins). The pages name the format (block
+ * FP8) but not its block shape; this library takes DeepSeek's: one fp32 scale
+ * per token and 128-wide group of k for activations, one per 128 x 128
+ * block for weights.
+ *
+ * mla_quant_fp8_groups: x [m][k] bf16 -> x_fp8 [m][k] E4M3FN codes and
+ * x_scale [m][k / 128] fp32, per token and group:
+ *     scale = max(amax, 1e-10) / 448,  code = E4M3(clamp(x / scale, +-448))
+ * with a correctly rounded fp32 division and round-to-nearest-even codes.
+ *  m 0..65536 (0 is a no-op); k a multiple of 128 up to 65536; x 4-byte,
+ *  x_fp8 2-byte, x_scale 4-byte aligned. Finite inputs.
+ *
+ * mla_gemm_fp8_blockscale: c [m][n] bf16 (fp32 accumulation, round to nearest
+ * even) =
+ *     sum_k e4m3(a[i][k]) a_scale[i][k / 128] * e4m3(b[j][k]) b_scale[j / 128][k / 128]
+ *  a        [m][k] E4M3FN codes, 16-byte aligned; a_scale [m][k / 128] fp32
+ *  b        [n][k] E4M3FN codes (one row per output feature), 16-byte
+ *           aligned; b_scale [ceil(n / 128)][k / 128] fp32
+ *  c        [m][n] bf16, 8-byte aligned, fully overwritten
+ *  m 0..65536, n a multiple of 16 up to 65536, k a multiple of 128 up to 65536.
+ * Ownership, asynchrony and error behaviour as for mla_decode; no workspace.
+ */
+mla_status_t mla_quant_fp8_groups(const void* x, void* x_fp8, float* x_scale, int32_t m,
+                                  int32_t k, void* stream);
+mla_status_t mla_gemm_fp8_blockscale(const void* a, const float* a_scale, const void* b,
+                                     const float* b_scale, void* c, int32_t m, int32_t n,
+                                     int32_t k, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(int32_t status);

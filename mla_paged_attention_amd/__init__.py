@@ -15,6 +15,7 @@ from ._binding import (  # noqa: F401
     MAX_HEADS,
     MAX_QUERY_LEN,
     MAX_TOPK,
+    FP8_GROUP,
     MLA_ERR_HIP,
     MLA_ERR_INVALID_ARG,
     MLA_ERR_NO_DEVICE,
@@ -28,9 +29,11 @@ from ._binding import (  # noqa: F401
     combine,
     decode,
     decode_sparse,
+    gemm_fp8_blockscale,
     get_workspace_size,
     get_workspace_size_sparse,
     library,
+    quant_fp8_groups,
     status_string,
     workspace_for,
 )

@@ -23,6 +23,8 @@ MAX_HEADS = 128
 MAX_QUERY_LEN = 16
 MAX_FORCED_SPLITS = 16
 MAX_TOPK = 65536
+FP8_GROUP = 128
+GEMM_MAX_M = GEMM_MAX_N = GEMM_MAX_K = 65536
 BLOCK_SIZES = (16, 32, 64, 128)
 
 MLA_OK = 0
@@ -38,7 +40,8 @@ MLA_KV_FP8_E4M3 = 1
 EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_get_workspace_size_multi_token",
                     "mla_get_workspace_size_sparse", "mla_decode", "mla_decode_multi_token",
                     "mla_decode_profiled", "mla_decode_sparse", "mla_decode_sparse_profiled",
-                    "mla_combine", "mla_status_string", "mla_abi_version")
+                    "mla_combine", "mla_quant_fp8_groups", "mla_gemm_fp8_blockscale",
+                    "mla_status_string", "mla_abi_version")
 
 _lib = None
 _lock = threading.Lock()
@@ -75,6 +78,10 @@ def _bind(lib: ctypes.CDLL) -> None:
     lib.mla_get_workspace_size_sparse.restype = sz
     lib.mla_combine.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp]
     lib.mla_combine.restype = i32
+    lib.mla_quant_fp8_groups.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.mla_quant_fp8_groups.restype = i32
+    lib.mla_gemm_fp8_blockscale.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
+    lib.mla_gemm_fp8_blockscale.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -279,6 +286,62 @@ def decode_sparse(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
     if st != MLA_OK:
         raise MLAError(st, "mla_decode_sparse")
     return out, lse
+
+
+def _fp8_codes(t: torch.Tensor) -> bool:
+    return t.dtype in (torch.uint8, torch.float8_e4m3fn)
+
+
+def quant_fp8_groups(x: torch.Tensor, *, out: torch.Tensor | None = None,
+                     scale: torch.Tensor | None = None, stream=None):
+    """Per token and 128-wide group E4M3 quantisation of bf16 x [m, k] (see
+    include/mla.h, mla_quant_fp8_groups). Returns (codes uint8 [m, k],
+    scales fp32 [m, k/128])."""
+    if x.dim() != 2 or x.dtype != torch.bfloat16 or not x.is_contiguous():
+        raise ValueError("x must be contiguous [m, k] bf16")
+    m, k = x.shape
+    dev = x.device
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.uint8, device=dev)
+    if scale is None:
+        scale = torch.empty((m, k // FP8_GROUP), dtype=torch.float32, device=dev)
+    if tuple(out.shape) != (m, k) or not _fp8_codes(out) or not out.is_contiguous() or \
+            tuple(scale.shape) != (m, k // FP8_GROUP) or scale.dtype != torch.float32 or \
+            not scale.is_contiguous():
+        raise ValueError("out must be contiguous [m, k] uint8, scale [m, k/128] fp32")
+    st = library().mla_quant_fp8_groups(_ptr(x), _ptr(out), _ptr(scale), m, k,
+                                        _stream_handle(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_quant_fp8_groups")
+    return out, scale
+
+
+def gemm_fp8_blockscale(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor,
+                        b_scale: torch.Tensor, *, out: torch.Tensor | None = None, stream=None):
+    """c [m, n] bf16 = dequant(a) @ dequant(b)^T with per-group activation scales
+    a_scale [m, k/128] and per-128x128-block weight scales b_scale
+    [ceil(n/128), k/128] (see include/mla.h, mla_gemm_fp8_blockscale)."""
+    for name, t in (("a", a), ("b", b)):
+        if t.dim() != 2 or not _fp8_codes(t) or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous 2-D E4M3 codes (uint8/float8_e4m3fn)")
+    m, k = a.shape
+    n = b.shape[0]
+    if b.shape[1] != k:
+        raise ValueError("a and b must share k")
+    if tuple(a_scale.shape) != (m, k // FP8_GROUP) or a_scale.dtype != torch.float32 or \
+            tuple(b_scale.shape) != ((n + FP8_GROUP - 1) // FP8_GROUP, k // FP8_GROUP) or \
+            b_scale.dtype != torch.float32 or not a_scale.is_contiguous() or \
+            not b_scale.is_contiguous():
+        raise ValueError("a_scale must be [m, k/128] and b_scale [ceil(n/128), k/128] fp32")
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.bfloat16, device=a.device)
+    elif tuple(out.shape) != (m, n) or out.dtype != torch.bfloat16 or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous [{m}, {n}] bf16")
+    st = library().mla_gemm_fp8_blockscale(_ptr(a), _ptr(a_scale), _ptr(b), _ptr(b_scale),
+                                           _ptr(out), m, n, k, _stream_handle(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_gemm_fp8_blockscale")
+    return out
 
 
 def combine(partial_out: torch.Tensor, partial_lse: torch.Tensor, split_indptr: torch.Tensor,

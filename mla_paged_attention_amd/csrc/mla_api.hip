@@ -397,6 +397,46 @@ mla_status_t mla_combine(const float* partial_out, const float* partial_lse,
   return MLA_OK;
 }
 
+mla_status_t mla_quant_fp8_groups(const void* x, void* x_fp8, float* x_scale, int32_t m,
+                                  int32_t k, void* stream) {
+  if (m < 0 || m > MLA_GEMM_MAX_M || k < MLA_FP8_GROUP || k % MLA_FP8_GROUP ||
+      k > MLA_GEMM_MAX_K)
+    return MLA_ERR_INVALID_ARG;
+  if (m > 0 && (!x || !x_fp8 || !x_scale || !aligned(x, 4) || !aligned(x_fp8, 2) ||
+                !aligned(x_scale, 4)))
+    return MLA_ERR_INVALID_ARG;
+  DeviceInfo dev;
+  mla_status_t st = query_device(&dev);
+  if (st != MLA_OK) return st;
+  if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
+  if (m == 0) return MLA_OK;
+  if (mla::launch_quant_fp8_groups(static_cast<const uint16_t*>(x), static_cast<uint8_t*>(x_fp8),
+                                   x_scale, m, k, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status_t mla_gemm_fp8_blockscale(const void* a, const float* a_scale, const void* b,
+                                     const float* b_scale, void* c, int32_t m, int32_t n,
+                                     int32_t k, void* stream) {
+  if (m < 0 || m > MLA_GEMM_MAX_M || n < 16 || n % 16 || n > MLA_GEMM_MAX_N ||
+      k < MLA_FP8_GROUP || k % MLA_FP8_GROUP || k > MLA_GEMM_MAX_K)
+    return MLA_ERR_INVALID_ARG;
+  if (m > 0 && (!a || !a_scale || !b || !b_scale || !c || !aligned(a, 16) || !aligned(b, 16) ||
+                !aligned(c, 8) || !aligned(a_scale, 4) || !aligned(b_scale, 4)))
+    return MLA_ERR_INVALID_ARG;
+  DeviceInfo dev;
+  mla_status_t st = query_device(&dev);
+  if (st != MLA_OK) return st;
+  if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
+  if (m == 0) return MLA_OK;
+  if (mla::launch_gemm_fp8(static_cast<const uint8_t*>(a), a_scale,
+                           static_cast<const uint8_t*>(b), b_scale, static_cast<uint16_t*>(c), m,
+                           n, k, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_status_string(int32_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

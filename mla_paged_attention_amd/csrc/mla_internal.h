@@ -162,6 +162,15 @@ hipError_t launch_sparse_rows(const int32_t* indices, int32_t topk, const int32_
                               int32_t stride, int32_t* rows, int32_t* eff_len, void* zero_row,
                               hipStream_t stream);
 
+// Block-scaled E4M3 projection (gemm_fp8.hip): bf16 -> E4M3 codes with one
+// scale per token and 128-wide group, and c[m][n] = A[m][k] B[n][k]^T with
+// per-group activation and per-128x128-block weight scales.
+hipError_t launch_quant_fp8_groups(const uint16_t* x, uint8_t* q, float* scale, int32_t m,
+                                   int32_t k, hipStream_t stream);
+hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* b,
+                           const float* b_scale, uint16_t* c, int32_t m, int32_t n, int32_t k,
+                           hipStream_t stream);
+
 // Combine of the automatic plan: only the requests listed in `split`
 // (header[2] of them, at most `max_split`).
 hipError_t launch_combine_split(const float* part_out, const float* part_lse,

@@ -274,6 +274,61 @@ def test_decode_sparse_profiled_requires_events():
     assert lib.mla_decode_sparse_profiled(*args, None) == mla.MLA_ERR_INVALID_ARG
 
 
+def test_gemm_constants():
+    text = header_text()
+    defines = dict(re.findall(r"#define (MLA_\w+) (\d+)", text))
+    assert int(defines["MLA_FP8_GROUP"]) == mla.FP8_GROUP == 128
+    for name in ("MLA_GEMM_MAX_M", "MLA_GEMM_MAX_N", "MLA_GEMM_MAX_K"):
+        assert int(defines[name]) == 65536
+
+
+GEMM_INVALID = [(-1, 16, 128), (65537, 16, 128), (4, 0, 128), (4, 24, 128), (4, 16, 0),
+                (4, 16, 64), (4, 16, 200), (4, 65552, 128), (4, 16, 65664)]
+
+
+@pytest.mark.parametrize("mnk", GEMM_INVALID, ids=str)
+def test_gemm_rejects_shapes(mnk):
+    f = ctypes.c_void_p(FAKE)
+    assert mla.library().mla_gemm_fp8_blockscale(f, f, f, f, f, *mnk, None) == \
+        mla.MLA_ERR_INVALID_ARG
+
+
+def test_gemm_rejects_pointers():
+    lib = mla.library()
+    f = ctypes.c_void_p(FAKE)
+    bad = [(None, f, f, f, f), (f, None, f, f, f), (f, f, None, f, f), (f, f, f, None, f),
+           (f, f, f, f, None), (ctypes.c_void_p(FAKE + 8), f, f, f, f),
+           (f, f, ctypes.c_void_p(FAKE + 8), f, f), (f, f, f, f, ctypes.c_void_p(FAKE + 4)),
+           (f, ctypes.c_void_p(FAKE + 2), f, f, f)]
+    for ptrs in bad:
+        assert lib.mla_gemm_fp8_blockscale(*ptrs, 4, 32, 256, None) == mla.MLA_ERR_INVALID_ARG
+    if not HAS_GPU:
+        assert lib.mla_gemm_fp8_blockscale(f, f, f, f, f, 4, 32, 256, None) == \
+            mla.MLA_ERR_NO_DEVICE
+        assert lib.mla_gemm_fp8_blockscale(None, None, None, None, None, 0, 32, 256, None) == \
+            mla.MLA_ERR_NO_DEVICE
+
+
+def test_quant_rejects():
+    lib = mla.library()
+    f = ctypes.c_void_p(FAKE)
+    for args in ((f, f, f, -1, 128), (f, f, f, 4, 64), (f, f, f, 4, 0), (None, f, f, 4, 128),
+                 (f, None, f, 4, 128), (f, f, None, 4, 128), (ctypes.c_void_p(FAKE + 2), f, f, 4, 128),
+                 (f, ctypes.c_void_p(FAKE + 1), f, 4, 128)):
+        assert lib.mla_quant_fp8_groups(*args, None) == mla.MLA_ERR_INVALID_ARG
+    if not HAS_GPU:
+        assert lib.mla_quant_fp8_groups(f, f, f, 4, 256, None) == mla.MLA_ERR_NO_DEVICE
+
+
+def test_gemm_binding_rejects():
+    a = torch.zeros((4, 256), dtype=torch.uint8)
+    with pytest.raises(ValueError):
+        mla.gemm_fp8_blockscale(a, torch.zeros((4, 1)), torch.zeros((32, 256), dtype=torch.uint8),
+                                torch.zeros((1, 2)))
+    with pytest.raises(ValueError):
+        mla.gemm_fp8_blockscale(a.float(), torch.zeros((4, 2)), a, torch.zeros((1, 2)))
+
+
 def test_combine_accepts_multi_token_rows():
     lib = mla.library()
     f = ctypes.c_void_p(FAKE)

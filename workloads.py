@@ -199,6 +199,30 @@ def draw_indices(gen: torch.Generator, seq_lens: torch.Tensor, topk: int) -> tor
     return out
 
 
+def make_gemm(m: int, n: int, k: int, seed: int):
+    """Operands of the block-scaled E4M3 projection: codes of N(0,1) * 64 cast to
+    E4M3FN (the two NaN codes cannot occur), and scales log-uniform in
+    [2^-10, 2^-4], drawn in that order (a, a_scale, b, b_scale). Returns uint8
+    codes a [m, k], b [n, k] and fp32 scales a_scale [m, k/128], b_scale
+    [ceil(n/128), k/128]. The default projection shape is DeepSeek-R1's fused
+    q/kv down-projection: n = 1536 + 576 = 2112, k = 7168."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+
+    def codes(rows):
+        x = torch.randn((rows, k), generator=gen, dtype=torch.float32) * 64.0
+        return x.clamp(-E4M3_MAX, E4M3_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+
+    def scales(rows):
+        u = torch.rand((rows, k // 128), generator=gen, dtype=torch.float64)
+        return torch.exp2(-10.0 + 6.0 * u).to(torch.float32)
+
+    a = codes(m)
+    a_scale = scales(m)
+    b = codes(n)
+    b_scale = scales((n + 127) // 128)
+    return a, a_scale, b, b_scale
+
+
 def quantize_e4m3(kv32: torch.Tensor):
     """Per-tensor E4M3 codes (uint8) and fp32 scale: amax maps to 448."""
     amax = float(kv32.abs().max())
