@@ -9,11 +9,13 @@
 //  1. quant_fp8_groups_kernel: bf16 activations -> E4M3 codes with one fp32
 //     scale per token and 128-wide group (scale = max(amax, 1e-10) / 448,
 //     codes rounded to nearest even from clamp(x / scale, +-448)).
-//  2. gemm_fp8_kernel<MT>: one workgroup per 16 weight rows and 16 MT tokens.
-//     The weight tile is the A operand of v_mfma_scale_f32_16x16x128_f8f6f4
-//     (rows = output features), the tokens the B operand (columns), so a
-//     single token wastes only the unused columns. Wave w of eight takes the
-//     128-wide k blocks w, w + 8, ..., loading two blocks ahead; each block's
+//  2. gemm_fp8_kernel<NT, MT, G>: one workgroup per 16 NT weight rows and
+//     16 MT tokens. Weight tiles are the A operand of
+//     v_mfma_scale_f32_16x16x128_f8f6f4 (rows = output features), tokens the B
+//     operand (columns), so a single token wastes only the unused columns.
+//     Wave w of eight takes the 128-wide k blocks w, w + 8, ..., with two
+//     groups of G blocks in flight (all seven of a wave's blocks at k = 7168
+//     and the smallest tiles); each block's
 //     product is scaled in fp32 by its token's group scale times the block's
 //     weight scale (the op's power-of-two scales cannot hold fp32 scales), and
 //     the eight partial tiles are summed through LDS.
@@ -61,99 +63,138 @@ __global__ void __launch_bounds__(256) quant_fp8_groups_kernel(const uint16_t* x
   if (lane == 0) scale[row * groups + grp] = s;
 }
 
-// 32 bytes (k = 32 g .. 32 g + 31 of one 128-wide block) of one row.
+// The 32 k-bytes of lane group g within one 128-wide block of a row: bytes
+// 16 g .. 16 g + 15 and 64 + 16 g .. 64 + 16 g + 15. Both operands use the same
+// assignment (a dot product does not depend on the order of k), and each of
+// the two loads of a wave reads one contiguous 64-byte half of every row.
 __device__ __forceinline__ g_i32x8_t load32(const uint8_t* p) {
   const g_u32x4_t lo = *reinterpret_cast<const g_u32x4_t*>(p);
-  const g_u32x4_t hi = *reinterpret_cast<const g_u32x4_t*>(p + 16);
+  const g_u32x4_t hi = *reinterpret_cast<const g_u32x4_t*>(p + 64);
   return __builtin_bit_cast(g_i32x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-template <int MT>
+// One workgroup per RT NT weight rows x 16 MT tokens (RT = 16, or 8: lanes
+// 8..15 of the op's 16-row side repeat rows 0..7 and their results are
+// dropped, which doubles the workgroups streaming the weights). Wave w takes
+// the k blocks w, w + 8, ..., loading G blocks per group, two groups in flight.
+template <int RT, int NT, int MT, int G>
 __global__ void __launch_bounds__(kGemmThreads) gemm_fp8_kernel(
     const uint8_t* a, const float* a_scale, const uint8_t* b, const float* b_scale, uint16_t* c,
     int32_t m, int32_t n, int32_t k) {
-  __shared__ g_f32x4_t red[kGemmWaves][MT][64];
+  __shared__ g_f32x4_t red[kGemmWaves][NT * MT][64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int cc = lane & 15, g = lane >> 4;
-  const int n0 = blockIdx.x * 16;
+  static_assert(RT == 16 || RT == 8, "rows per tile");
+  const int n0 = blockIdx.x * RT * NT;
   const int m0 = blockIdx.y * 16 * MT;
   const int kb_n = k / kGroup;
 
-  // A operand: weight row n0 + cc; B operand of tile t: token m0 + 16 t + cc
-  // (a token past m reads token 0 and is dropped at the store).
-  const uint8_t* brow = b + size_t(n0 + cc) * k + 32 * g;
-  const float* bs_row = b_scale + size_t(n0 / kGroup) * kb_n;
+  // A operands: weight rows n0 + 16 u + cc (a tile past n reads the last
+  // tile and is dropped at the store). B operands: token m0 + 16 t + cc (a
+  // token past m reads token 0 and is dropped).
+  const uint8_t* brow[NT];
+  const float* bs_row[NT];
+#pragma unroll
+  for (int u = 0; u < NT; ++u) {
+    const int tile = min(n0 + RT * u, n - RT);
+    brow[u] = b + size_t(tile + (cc & (RT - 1))) * k + 16 * g;
+    bs_row[u] = b_scale + size_t(tile / kGroup) * kb_n;
+  }
   const uint8_t* arow[MT];
   const float* as_row[MT];
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
     const int tok = m0 + 16 * t + cc;
     const int tk = tok < m ? tok : 0;
-    arow[t] = a + size_t(tk) * k + 32 * g;
+    arow[t] = a + size_t(tk) * k + 16 * g;
     as_row[t] = a_scale + size_t(tk) * kb_n;
   }
 
-  g_f32x4_t acc[MT];
+  g_f32x4_t acc[NT][MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) acc[t] = g_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int u = 0; u < NT; ++u)
+#pragma unroll
+    for (int t = 0; t < MT; ++t) acc[u][t] = g_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   struct Stage {
-    g_i32x8_t w;
+    g_i32x8_t w[NT];
     g_i32x8_t x[MT];
-    float s[MT];
+    float sb[NT];
+    float sa[MT];
   };
-  auto load = [&](int kb, Stage& st) {
-    st.w = load32(brow + size_t(kb) * kGroup);
-    const float bs = bs_row[kb];
+  auto load_stage = [&](int kb, Stage& st) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      st.w[u] = load32(brow[u] + size_t(kb) * kGroup);
+      st.sb[u] = bs_row[u][kb];
+    }
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       st.x[t] = load32(arow[t] + size_t(kb) * kGroup);
-      st.s[t] = as_row[t][kb] * bs;
+      st.sa[t] = as_row[t][kb];
     }
   };
-  auto compute = [&](const Stage& st) {
+  auto compute_stage = [&](const Stage& st) {
 #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      // Format 0 = E4M3 for both operands; E8M0 scales 127 = 2^0.
-      const g_f32x4_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-          st.w, st.x[t], g_f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
-      acc[t] += d * st.s[t];
-    }
+    for (int u = 0; u < NT; ++u)
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        // Format 0 = E4M3 for both operands; E8M0 scales 127 = 2^0.
+        const g_f32x4_t d = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            st.w[u], st.x[t], g_f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, 127, 0, 127);
+        acc[u][t] += d * (st.sa[t] * st.sb[u]);
+      }
   };
 
-  // k blocks of this wave: wave, wave + 8, ...; two stages in flight.
-  Stage s0, s1;
-  int kb = wave;
-  if (kb < kb_n) load(kb, s0);
-  if (kb + kGemmWaves < kb_n) load(kb + kGemmWaves, s1);
-  for (; kb < kb_n; kb += 2 * kGemmWaves) {
-    compute(s0);
-    if (kb + 2 * kGemmWaves < kb_n) load(kb + 2 * kGemmWaves, s0);
-    if (kb + kGemmWaves < kb_n) {
-      compute(s1);
-      if (kb + 3 * kGemmWaves < kb_n) load(kb + 3 * kGemmWaves, s1);
+  // This wave's k blocks: wave + 8 i, i < cnt, in groups of G.
+  const int cnt = kb_n > wave ? (kb_n - wave + kGemmWaves - 1) / kGemmWaves : 0;
+  const int ng = (cnt + G - 1) / G;
+  Stage s0[G], s1[G];
+  auto load_group = [&](int gi, Stage (&st)[G]) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (gi * G + j < cnt) load_stage(wave + kGemmWaves * (gi * G + j), st[j]);
+  };
+  auto compute_group = [&](int gi, const Stage (&st)[G]) {
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+      if (gi * G + j < cnt) compute_stage(st[j]);
+  };
+  load_group(0, s0);
+  load_group(1, s1);
+  for (int gi = 0; gi < ng; gi += 2) {
+    compute_group(gi, s0);
+    if (gi + 2 < ng) load_group(gi + 2, s0);
+    if (gi + 1 < ng) {
+      compute_group(gi + 1, s1);
+      if (gi + 3 < ng) load_group(gi + 3, s1);
     }
   }
 
 #pragma unroll
-  for (int t = 0; t < MT; ++t) red[wave][t][lane] = acc[t];
-  __syncthreads();
-  // Thread (t, lane) sums the eight partial tiles: rows n0 + 4 g + r of
-  // token m0 + 16 t + cc.
-  if (threadIdx.x < MT * 64) {
-    const int t = threadIdx.x >> 6;
-    g_f32x4_t sum = red[0][t][lane];
+  for (int u = 0; u < NT; ++u)
 #pragma unroll
-    for (int w = 1; w < kGemmWaves; ++w) sum += red[w][t][lane];
-    const int tok = m0 + 16 * t + cc;
-    if (tok < m) {
+    for (int t = 0; t < MT; ++t) red[wave][u * MT + t][lane] = acc[u][t];
+  __syncthreads();
+  // (tile, lane) pairs: rows n0 + RT u + 4 (lane / 16) + r of token
+  // m0 + 16 t + lane % 16, summed over the eight waves.
+  for (int idx = threadIdx.x; idx < NT * MT * 64; idx += kGemmThreads) {
+    const int tile = idx >> 6, ln = idx & 63;
+    if (4 * (ln >> 4) >= RT) continue;  // repeated rows of an 8-row tile
+    const int u = tile / MT, t = tile - (tile / MT) * MT;
+    g_f32x4_t sum = red[0][tile][ln];
+#pragma unroll
+    for (int w = 1; w < kGemmWaves; ++w) sum += red[w][tile][ln];
+    const int tok = m0 + 16 * t + (ln & 15);
+    const int row = n0 + RT * u + 4 * (ln >> 4);
+    if (tok < m && n0 + RT * u < n) {
       unsigned short h[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         h[r] = __builtin_bit_cast(unsigned short, (__bf16)sum[r]);  // nearest even
       const unsigned lo = unsigned(h[0]) | (unsigned(h[1]) << 16);
       const unsigned hi = unsigned(h[2]) | (unsigned(h[3]) << 16);
-      *reinterpret_cast<unsigned long long*>(c + size_t(tok) * n + n0 + 4 * g) =
+      *reinterpret_cast<unsigned long long*>(c + size_t(tok) * n + row) =
           (unsigned long long)lo | ((unsigned long long)hi << 32);
     }
   }
@@ -172,17 +213,23 @@ hipError_t launch_quant_fp8_groups(const uint16_t* x, uint8_t* q, float* scale, 
 hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t* b,
                            const float* b_scale, uint16_t* c, int32_t m, int32_t n, int32_t k,
                            hipStream_t stream) {
-  const int mt = m <= 16 ? 1 : (m <= 32 ? 2 : 4);
-  const dim3 grid(unsigned(n / 16), unsigned((m + 16 * mt - 1) / (16 * mt)));
-  if (mt == 1)
-    hipLaunchKernelGGL(gemm_fp8_kernel<1>, grid, dim3(kGemmThreads), 0, stream, a, a_scale, b,
-                       b_scale, c, m, n, k);
-  else if (mt == 2)
-    hipLaunchKernelGGL(gemm_fp8_kernel<2>, grid, dim3(kGemmThreads), 0, stream, a, a_scale, b,
-                       b_scale, c, m, n, k);
+  // Tile shape by token count: 16-row weight tiles (132 workgroups at
+  // n = 2112) up to 128 tokens; above, 32-row tiles cut the activations'
+  // re-reads (a 64-row tile would spill). Measured: 8-row tiles, whose
+  // upper lanes repeat rows, are slower at every m.
+  auto go = [&](auto kern, int rows, int mt) {
+    const dim3 grid(unsigned((n + rows - 1) / rows), unsigned((m + 16 * mt - 1) / (16 * mt)));
+    hipLaunchKernelGGL(kern, grid, dim3(kGemmThreads), 0, stream, a, a_scale, b, b_scale, c, m, n,
+                       k);
+  };
+  if (m <= 16)
+    go(gemm_fp8_kernel<16, 1, 1, 4>, 16, 1);
+  else if (m <= 32)
+    go(gemm_fp8_kernel<16, 1, 2, 3>, 16, 2);
+  else if (m <= 128)
+    go(gemm_fp8_kernel<16, 1, 4, 2>, 16, 4);
   else
-    hipLaunchKernelGGL(gemm_fp8_kernel<4>, grid, dim3(kGemmThreads), 0, stream, a, a_scale, b,
-                       b_scale, c, m, n, k);
+    go(gemm_fp8_kernel<16, 2, 4, 1>, 32, 4);
   return hipGetLastError();
 }
 
