@@ -46,6 +46,8 @@ def _bind(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_mla_attend_sparse.restype = i32
     lib.oracle_gemm_fp8_blockscale.argtypes = [vp, vp, vp, vp, i64, i64, i64, vp]
     lib.oracle_gemm_fp8_blockscale.restype = i32
+    lib.oracle_absorb.argtypes = [vp, vp, i64, i64, i64, i64, vp]
+    lib.oracle_absorb.restype = i32
     lib.oracle_lse_merge.argtypes = [vp, vp, i64, i64, vp, vp]
     lib.oracle_lse_merge.restype = i32
     lib.oracle_e4m3_to_double.argtypes = [ctypes.c_uint8]
@@ -181,6 +183,21 @@ class Oracle:
                                                  m, n, k, _ptr(c))
         if rc != 0:
             raise ValueError(f"oracle_gemm_fp8_blockscale failed with status {rc}")
+        return c
+
+    def absorb(self, x_bits, w_bits):
+        """Per-head product c [B, H, n] float64 of x bf16 bits [B, H, k] and
+        w bf16 bits [H, k, n] (see the C source)."""
+        x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+        w_bits = np.ascontiguousarray(w_bits, dtype=np.uint16)
+        batch, heads, k = x_bits.shape
+        if w_bits.shape[:2] != (heads, k):
+            raise ValueError("shape mismatch")
+        n = w_bits.shape[2]
+        c = np.empty((batch, heads, n), dtype=np.float64)
+        rc = self.lib.oracle_absorb(_ptr(x_bits), _ptr(w_bits), batch, heads, k, n, _ptr(c))
+        if rc != 0:
+            raise ValueError(f"oracle_absorb failed with status {rc}")
         return c
 
     @staticmethod

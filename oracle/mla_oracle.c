@@ -366,4 +366,36 @@ int oracle_gemm_fp8_blockscale(const uint8_t* a, const float* a_scale, const uin
   return ORACLE_OK;
 }
 
-int oracle_abi_version(void) { return 3; }
+/*
+ * oracle_absorb: the per-head products on either side of absorbed MLA decode
+ * (the decode path takes a 576-wide q whose first 512 columns are the no-rope
+ * query absorbed into the latent space, and returns a 512-wide latent output
+ * that the value up-projection maps back to the head dimension; DeepSeek's
+ * shapes: 128 no-rope dims, 64 rope dims, 512 latent dims, 128 value dims).
+ * Written out per element in fp64:
+ *
+ *   c[b][h][j] = sum_i x[b][h][i] * w[h][i][j]       j < n_out
+ *
+ *  x  [batch][heads][k_in] bf16 bits;  w [heads][k_in][n_out] bf16 bits
+ *  c  [batch][heads][n_out] fp64
+ * q absorption: k_in = 128, n_out = 512 (w = W_UK per head); output
+ * absorption: k_in = 512, n_out = 128 (w = W_UV per head).
+ */
+int oracle_absorb(const uint16_t* x, const uint16_t* w, int64_t batch, int64_t heads,
+                  int64_t k_in, int64_t n_out, double* c) {
+  if (!x || !w || !c || batch < 0 || heads < 1 || k_in < 1 || n_out < 1) return ORACLE_BAD_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t bh = 0; bh < batch * heads; ++bh) {
+    int64_t h = bh % heads;
+    for (int64_t j = 0; j < n_out; ++j) {
+      double sum = 0.0;
+      for (int64_t i = 0; i < k_in; ++i)
+        sum += bf16_bits_to_double(x[bh * k_in + i]) *
+               bf16_bits_to_double(w[(h * k_in + i) * n_out + j]);
+      c[bh * n_out + j] = sum;
+    }
+  }
+  return ORACLE_OK;
+}
+
+int oracle_abi_version(void) { return 4; }

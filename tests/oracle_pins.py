@@ -562,13 +562,32 @@ def pin_quant_groups(orc):
                 assert vals[cg[t]] == vals[best[0]], f"code not nearest (row {i}, group {g})"
 
 
+def pin_absorb(orc):
+    """The per-head absorption products equal torch's float64 batched matmul;
+    an identity block in W passes x through exactly."""
+    gen = torch.Generator().manual_seed(24)
+    for b, h, k, n in ((3, 2, 128, 512), (5, 3, 512, 128)):
+        x = _bf16(torch.randn((b, h, k), generator=gen))
+        w = _bf16(torch.randn((h, k, n), generator=gen) * 0.05)
+        c = orc.absorb(_bits(x), _bits(w))
+        ref = torch.matmul(x.double().permute(1, 0, 2), w.double()).permute(1, 0, 2).numpy()
+        mag = torch.matmul(x.double().abs().permute(1, 0, 2), w.double().abs()).permute(1, 0, 2)
+        assert np.all(np.abs(c - ref) <= 1e-12 * (1 + mag.numpy())), f"absorb vs matmul k={k}"
+    x = _bf16(torch.randn((2, 2, 128), generator=gen))
+    w = torch.zeros((2, 128, 512), dtype=torch.bfloat16)
+    w[:, :, :128] = torch.eye(128, dtype=torch.bfloat16)
+    c = orc.absorb(_bits(x), _bits(w))
+    assert (c[:, :, :128] == x.double().numpy()).all() and (c[:, :, 128:] == 0).all(), \
+        "identity block must pass x through"
+
+
 PINS = [pin_e4m3_decode, pin_bf16_widen, pin_sdpa_identity_table, pin_sdpa_shuffled_pages,
         pin_closed_forms, pin_empty_request, pin_split_merge, pin_merge_closed_form,
         pin_rope_shift, pin_head_padding, pin_block_permutation, pin_batch_independence,
         pin_fp8_dequant, pin_multi_token_causal_sdpa, pin_multi_token_rows_are_single_decodes,
         pin_multi_token_split_merge, pin_sparse_all_positions_is_dense,
         pin_sparse_sdpa_on_gathered_rows, pin_sparse_closed_forms, pin_sparse_split_merge,
-        pin_gemm_matches_torch_matmul, pin_gemm_closed_forms, pin_quant_groups]
+        pin_gemm_matches_torch_matmul, pin_gemm_closed_forms, pin_quant_groups, pin_absorb]
 
 
 def main(argv=None) -> int:

@@ -49,6 +49,9 @@ MUTANTS = [
     ("gemm_weight_scale_group0", "(double)b_scale[(j / 128) * kg + t / 128]",
      "(double)b_scale[(j / 128) * kg]"),
     ("gemm_act_scale_group0", "(double)a_scale[i * kg + t / 128]", "(double)a_scale[i * kg]"),
+    ("absorb_weight_transposed", "bf16_bits_to_double(w[(h * k_in + i) * n_out + j])",
+     "bf16_bits_to_double(w[(h * k_in + (i + j) % k_in) * n_out + j])"),
+    ("absorb_head_zero", "int64_t h = bh % heads;", "int64_t h = 0;"),
     ("out_row_token_head_transposed", "int64_t row_out = (i * q_len + qi) * num_heads + h;",
      "int64_t row_out = (i * num_heads + h) * q_len + qi;"),
     ("e4m3_bias", "exponent - 7);", "exponent - 8);"),
