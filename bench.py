@@ -166,6 +166,25 @@ def calib_copy(torch, dev, nbytes: int, reps: int) -> int:
     return 0
 
 
+def time_queued(torch, fn, steps: int, warmup: int):
+    """Per-call GPU time of fn(i) in us, sorted, for calls that are shorter
+    than their own host-side launch cost. The stream is held by a bounded spin
+    kernel while the host queues all the calls and their events, so the calls
+    run back to back and each event pair sees the kernel, not the host."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        fn(i)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda.synchronize()
+    torch.cuda._sleep(100_000 * steps)  # clock ticks; covers the host's queueing
+    for i in range(steps):
+        ev[2 * i].record(stream)
+        fn(i)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    return sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
+
+
 def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, warmup: int) -> int:
     """Block-scaled E4M3 projection at decode batch m (DeepSeek-R1 fused q/kv
     down-projection by default: n = 2112, k = 7168): one JSON line with us per
@@ -176,17 +195,8 @@ def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, w
     bs = [(b.to(dev), sb.to(dev)) for _ in range(copies)]
     a, sa = a.to(dev), sa.to(dev)
     out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    stream = torch.cuda.current_stream()
-    for i in range(warmup):
-        mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        ev[2 * i].record(stream)
-        mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out)
-        ev[2 * i + 1].record(stream)
-    torch.cuda.synchronize()
-    us = sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
+    us = time_queued(torch, lambda i: mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out),
+                     steps, warmup)
     avg = statistics.fmean(us)
     alg_bytes = m * k + n * k + 4 * m * (k // 128) + 4 * ((n + 127) // 128) * (k // 128) + 2 * m * n
     flops = 2 * m * n * k
@@ -213,6 +223,52 @@ def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, w
     return 0
 
 
+def bench_absorb(torch, mla, workloads, dev, batch: int, heads: int, steps: int,
+                 warmup: int) -> int:
+    """Per-head absorption products at decode batch `batch` and `heads` heads:
+    one JSON line with us per call of mla_absorb_q and mla_absorb_out and the
+    roofline of the first. Weights rotate across copies of >= 1 GB in total
+    so that their reads come from HBM."""
+    q_nope, q_rope, w_uk, o_lat, w_uv = workloads.make_absorb(batch, heads, seed=12)
+    copies = max(2, math.ceil(ROTATE_MIN_BYTES / (2 * w_uk.numel())))
+    wk = [w_uk.to(dev) for _ in range(copies)]
+    wv = [w_uv.to(dev) for _ in range(copies)]
+    q_nope, q_rope, o_lat = q_nope.to(dev), q_rope.to(dev), o_lat.to(dev)
+    q = torch.empty((batch, heads, 576), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((batch, heads, 128), dtype=torch.bfloat16, device=dev)
+    us_q = time_queued(torch, lambda i: mla.absorb_q(q_nope, wk[i % copies], q_rope, out=q),
+                       steps, warmup)
+    us_o = time_queued(torch, lambda i: mla.absorb_out(o_lat, wv[i % copies], out=o),
+                       steps, warmup)
+    avg_q, avg_o = statistics.fmean(us_q), statistics.fmean(us_o)
+    # Algorithmic bytes of mla_absorb_q: q_nope + W_UK + q_rope read, q written.
+    bytes_q = 2 * (batch * heads * 128 + heads * 128 * 512 + batch * heads * 64
+                   + batch * heads * 576)
+    bytes_o = 2 * (batch * heads * 512 + heads * 512 * 128 + batch * heads * 128)
+    flops = 2 * batch * heads * 128 * 512
+    gbps = bytes_q / (avg_q * 1e-6) / 1e9
+    tflops = flops / (avg_q * 1e-6) / 1e12
+    if flops / (PEAK_MFMA_TFLOPS["bf16"] * 1e12) > bytes_q / (PEAK_HBM_GBPS * 1e9):
+        roof = {"bound": "mfma", "achieved": round(tflops, 1), "peak": PEAK_MFMA_TFLOPS["bf16"],
+                "unit": "TFLOP/s", "frac": round(tflops / PEAK_MFMA_TFLOPS["bf16"], 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
+                "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
+    roof.update({"kernel": "mla::absorb_q_kernel",
+                 "algorithmic_bytes_per_launch": bytes_q, "algorithmic_flops_per_launch": flops,
+                 "traffic": None})
+    print(json.dumps({
+        "metric": "absorbed query projection us/call at decode batch", "value": round(avg_q, 2),
+        "unit": "us/call", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"absorb-b{batch}-h{heads}", "batch": batch, "heads": heads},
+        "us_p10_p90": [round(us_q[len(us_q) // 10], 2), round(us_q[(9 * len(us_q)) // 10], 2)],
+        "absorb_out": {"us": round(avg_o, 2), "algorithmic_bytes_per_launch": bytes_o,
+                       "GB/s": round(bytes_o / (avg_o * 1e-6) / 1e9, 1)},
+        "roofline": roof}), flush=True)
+    return 0
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -228,6 +284,10 @@ def main(argv=None) -> int:
                     help="instead of decoding, time the block-scaled E4M3 projection at "
                          "decode batch M (n = 2112, k = 7168 unless --gemm-nk)")
     ap.add_argument("--gemm-nk", type=int, nargs=2, default=(2112, 7168), metavar=("N", "K"))
+    ap.add_argument("--absorb", type=int, default=0, metavar="B",
+                    help="instead of decoding, time the per-head absorption products at "
+                         "decode batch B (heads from --absorb-heads)")
+    ap.add_argument("--absorb-heads", type=int, default=16)
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of decoding, run plain device copies and reductions of "
                          "MIB MiB (HBM counter calibration and practical bandwidth)")
@@ -251,6 +311,9 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     if args.calib_copy:
         return calib_copy(torch, dev, args.calib_copy << 20, max(args.steps, 1))
+    if args.absorb:
+        return bench_absorb(torch, mla, workloads, dev, args.absorb, args.absorb_heads,
+                            args.steps, args.warmup)
     if args.gemm:
         return bench_gemm(torch, mla, workloads, dev, args.gemm, *args.gemm_nk, args.steps,
                           args.warmup)

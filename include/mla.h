@@ -303,6 +303,32 @@ mla_status_t mla_gemm_fp8_blockscale(const void* a, const float* a_scale, const 
                                      const float* b_scale, void* c, int32_t m, int32_t n,
                                      int32_t k, void* stream);
 
+/*
+ * The per-head products on either side of absorbed decode (the pages show
+ * only the absorbed, 576-wide query; DeepSeek's shapes are taken: 128
+ * no-rope and 64 rope query dims per head, 512 latent dims, 128 value dims).
+ *
+ * mla_absorb_q: q [batch][num_heads][576] bf16 =
+ *     [ q_nope[b][h][0:128] . w_uk[h] (128 x 512), q_rope[b][h][0:64] ]
+ * the query mla_decode takes.
+ *  q_nope [batch][num_heads][128], w_uk [num_heads][128][512],
+ *  q_rope [batch][num_heads][64]: bf16, 16-byte aligned.
+ *
+ * mla_absorb_out: o [batch][num_heads][128] bf16,
+ *     o[b][h][v] = sum over c < 512 of o_latent[b][h][c] * w_uv[h][v][c]
+ * mapping mla_decode's output back to the value dimension. w_uv holds one
+ * 512-wide row per value dim (the value up-projection's own layout).
+ *  o_latent [batch][num_heads][512], w_uv [num_heads][128][512]: bf16,
+ *  16-byte aligned.
+ *
+ * fp32 accumulation, bf16 rounding to nearest even. batch 0..65536 (0 is a
+ * no-op), num_heads 1..128. Ownership and errors as for mla_decode.
+ */
+mla_status_t mla_absorb_q(const void* q_nope, const void* w_uk, const void* q_rope, void* q,
+                          int32_t batch, int32_t num_heads, void* stream);
+mla_status_t mla_absorb_out(const void* o_latent, const void* w_uv, void* o, int32_t batch,
+                            int32_t num_heads, void* stream);
+
 /* Static, human-readable name of a status code. */
 const char* mla_status_string(int32_t status);
 

@@ -26,6 +26,8 @@ from ._binding import (  # noqa: F401
     MLA_OK,
     MLAError,
     abi_version,
+    absorb_out,
+    absorb_q,
     combine,
     decode,
     decode_sparse,

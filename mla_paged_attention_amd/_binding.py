@@ -41,6 +41,7 @@ EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_get_workspace_size_multi_toke
                     "mla_get_workspace_size_sparse", "mla_decode", "mla_decode_multi_token",
                     "mla_decode_profiled", "mla_decode_sparse", "mla_decode_sparse_profiled",
                     "mla_combine", "mla_quant_fp8_groups", "mla_gemm_fp8_blockscale",
+                    "mla_absorb_q", "mla_absorb_out",
                     "mla_status_string", "mla_abi_version")
 
 _lib = None
@@ -82,6 +83,10 @@ def _bind(lib: ctypes.CDLL) -> None:
     lib.mla_quant_fp8_groups.restype = i32
     lib.mla_gemm_fp8_blockscale.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, vp]
     lib.mla_gemm_fp8_blockscale.restype = i32
+    lib.mla_absorb_q.argtypes = [vp, vp, vp, vp, i32, i32, vp]
+    lib.mla_absorb_q.restype = i32
+    lib.mla_absorb_out.argtypes = [vp, vp, vp, i32, i32, vp]
+    lib.mla_absorb_out.restype = i32
     lib.mla_status_string.argtypes = [i32]
     lib.mla_status_string.restype = ctypes.c_char_p
     lib.mla_abi_version.argtypes = []
@@ -341,6 +346,46 @@ def gemm_fp8_blockscale(a: torch.Tensor, a_scale: torch.Tensor, b: torch.Tensor,
                                            _ptr(out), m, n, k, _stream_handle(stream))
     if st != MLA_OK:
         raise MLAError(st, "mla_gemm_fp8_blockscale")
+    return out
+
+
+def _check_bf16(name, t, shape):
+    if tuple(t.shape) != tuple(shape) or t.dtype != torch.bfloat16 or not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous {tuple(shape)} bf16")
+
+
+def absorb_q(q_nope: torch.Tensor, w_uk: torch.Tensor, q_rope: torch.Tensor, *,
+             out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q [B, H, 576] = [q_nope [B, H, 128] . w_uk [H, 128, 512], q_rope [B, H, 64]]
+    (see include/mla.h, mla_absorb_q)."""
+    batch, heads = q_nope.shape[0], q_nope.shape[1]
+    _check_bf16("q_nope", q_nope, (batch, heads, 128))
+    _check_bf16("w_uk", w_uk, (heads, 128, 512))
+    _check_bf16("q_rope", q_rope, (batch, heads, 64))
+    if out is None:
+        out = torch.empty((batch, heads, HEAD_DIM_K), dtype=torch.bfloat16, device=q_nope.device)
+    _check_bf16("out", out, (batch, heads, HEAD_DIM_K))
+    st = library().mla_absorb_q(_ptr(q_nope), _ptr(w_uk), _ptr(q_rope), _ptr(out), batch, heads,
+                                _stream_handle(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_q")
+    return out
+
+
+def absorb_out(o_latent: torch.Tensor, w_uv: torch.Tensor, *, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+    """o [B, H, 128], o[b, h, v] = sum_c o_latent[b, h, c] w_uv[h, v, c], with
+    o_latent [B, H, 512] and w_uv [H, 128, 512] (see include/mla.h, mla_absorb_out)."""
+    batch, heads = o_latent.shape[0], o_latent.shape[1]
+    _check_bf16("o_latent", o_latent, (batch, heads, HEAD_DIM_V))
+    _check_bf16("w_uv", w_uv, (heads, 128, HEAD_DIM_V))
+    if out is None:
+        out = torch.empty((batch, heads, 128), dtype=torch.bfloat16, device=o_latent.device)
+    _check_bf16("out", out, (batch, heads, 128))
+    st = library().mla_absorb_out(_ptr(o_latent), _ptr(w_uv), _ptr(out), batch, heads,
+                                  _stream_handle(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_absorb_out")
     return out
 
 

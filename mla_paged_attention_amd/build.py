@@ -12,7 +12,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
-SOURCES = [os.path.join(CSRC, f) for f in ("mla_kernels.hip", "gemm_fp8.hip", "mla_api.hip")]
+SOURCES = [os.path.join(CSRC, f)
+           for f in ("mla_kernels.hip", "gemm_fp8.hip", "absorb.hip", "mla_api.hip")]
 LIBRARY = os.path.join(HERE, "libmla_mi355x.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

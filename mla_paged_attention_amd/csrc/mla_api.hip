@@ -437,6 +437,43 @@ mla_status_t mla_gemm_fp8_blockscale(const void* a, const float* a_scale, const 
   return MLA_OK;
 }
 
+namespace {
+mla_status_t absorb_checks(const void* x, const void* w, const void* out, int32_t batch,
+                           int32_t heads) {
+  if (batch < 0 || batch > MLA_GEMM_MAX_M || heads < 1 || heads > MLA_MAX_HEADS)
+    return MLA_ERR_INVALID_ARG;
+  if (batch > 0 && (!x || !w || !out || !aligned(x, 16) || !aligned(w, 16) || !aligned(out, 16)))
+    return MLA_ERR_INVALID_ARG;
+  DeviceInfo dev;
+  mla_status_t st = query_device(&dev);
+  if (st != MLA_OK) return st;
+  return dev.gfx950 ? MLA_OK : MLA_ERR_UNSUPPORTED;
+}
+}  // namespace
+
+mla_status_t mla_absorb_q(const void* q_nope, const void* w_uk, const void* q_rope, void* q,
+                          int32_t batch, int32_t num_heads, void* stream) {
+  if (batch > 0 && (!q_rope || !aligned(q_rope, 16))) return MLA_ERR_INVALID_ARG;
+  mla_status_t st = absorb_checks(q_nope, w_uk, q, batch, num_heads);
+  if (st != MLA_OK || batch == 0) return st;
+  if (mla::launch_absorb_q(static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(w_uk),
+                           static_cast<const uint16_t*>(q_rope), static_cast<uint16_t*>(q), batch,
+                           num_heads, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
+mla_status_t mla_absorb_out(const void* o_latent, const void* w_uv, void* o, int32_t batch,
+                            int32_t num_heads, void* stream) {
+  mla_status_t st = absorb_checks(o_latent, w_uv, o, batch, num_heads);
+  if (st != MLA_OK || batch == 0) return st;
+  if (mla::launch_absorb_out(static_cast<const uint16_t*>(o_latent),
+                             static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(o), batch,
+                             num_heads, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return MLA_ERR_HIP;
+  return MLA_OK;
+}
+
 const char* mla_status_string(int32_t status) {
   switch (status) {
     case MLA_OK: return "MLA_OK";

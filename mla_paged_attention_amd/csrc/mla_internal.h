@@ -171,6 +171,13 @@ hipError_t launch_gemm_fp8(const uint8_t* a, const float* a_scale, const uint8_t
                            const float* b_scale, uint16_t* c, int32_t m, int32_t n, int32_t k,
                            hipStream_t stream);
 
+// Per-head absorption products (absorb.hip): q = [q_nope . W_UK[h], q_rope]
+// and o[v] = sum_c o_latent[c] W_UV[h][v][c], bf16 with fp32 accumulation.
+hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, const uint16_t* q_rope,
+                           uint16_t* q, int32_t batch, int32_t heads, hipStream_t stream);
+hipError_t launch_absorb_out(const uint16_t* o_latent, const uint16_t* w_uv, uint16_t* o,
+                             int32_t batch, int32_t heads, hipStream_t stream);
+
 // Combine of the automatic plan: only the requests listed in `split`
 // (header[2] of them, at most `max_split`).
 hipError_t launch_combine_split(const float* part_out, const float* part_lse,

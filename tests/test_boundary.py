@@ -329,6 +329,21 @@ def test_gemm_binding_rejects():
         mla.gemm_fp8_blockscale(a.float(), torch.zeros((4, 2)), a, torch.zeros((1, 2)))
 
 
+def test_absorb_rejects():
+    lib = mla.library()
+    f = ctypes.c_void_p(FAKE)
+    m = ctypes.c_void_p(FAKE + 8)
+    for args in ((f, f, f, f, -1, 16), (f, f, f, f, 4, 0), (f, f, f, f, 4, 129),
+                 (None, f, f, f, 4, 16), (f, None, f, f, 4, 16), (f, f, None, f, 4, 16),
+                 (f, f, f, None, 4, 16), (m, f, f, f, 4, 16), (f, f, m, f, 4, 16)):
+        assert lib.mla_absorb_q(*args, None) == mla.MLA_ERR_INVALID_ARG
+    for args in ((f, f, f, -1, 16), (f, f, f, 4, 0), (None, f, f, 4, 16), (f, m, f, 4, 16)):
+        assert lib.mla_absorb_out(*args, None) == mla.MLA_ERR_INVALID_ARG
+    if not HAS_GPU:
+        assert lib.mla_absorb_q(f, f, f, f, 4, 16, None) == mla.MLA_ERR_NO_DEVICE
+        assert lib.mla_absorb_out(f, f, f, 4, 16, None) == mla.MLA_ERR_NO_DEVICE
+
+
 def test_combine_accepts_multi_token_rows():
     lib = mla.library()
     f = ctypes.c_void_p(FAKE)

@@ -223,6 +223,25 @@ def make_gemm(m: int, n: int, k: int, seed: int):
     return a, a_scale, b, b_scale
 
 
+def make_absorb(batch: int, heads: int, seed: int):
+    """Operands of the per-head absorption products, all bf16 from fp32 normals
+    rounded to nearest even, drawn in order: q_nope [B, H, 128], q_rope
+    [B, H, 64], W_UK [H, 128, 512] * 0.05, o_latent [B, H, 512], W_UV
+    [H, 128, 512] * 0.05 (one 512-wide row per value dim; weights scaled so
+    that outputs stay near N(0, 1))."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+
+    def draw(shape, s=1.0):
+        return (torch.randn(shape, generator=gen, dtype=torch.float32) * s).to(torch.bfloat16)
+
+    q_nope = draw((batch, heads, 128))
+    q_rope = draw((batch, heads, 64))
+    w_uk = draw((heads, 128, 512), 0.05)
+    o_latent = draw((batch, heads, 512))
+    w_uv = draw((heads, 128, 512), 0.05)
+    return q_nope, q_rope, w_uk, o_latent, w_uv
+
+
 def quantize_e4m3(kv32: torch.Tensor):
     """Per-tensor E4M3 codes (uint8) and fp32 scale: amax maps to 448."""
     amax = float(kv32.abs().max())
