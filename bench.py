@@ -167,22 +167,32 @@ def calib_copy(torch, dev, nbytes: int, reps: int) -> int:
 
 
 def time_queued(torch, fn, steps: int, warmup: int):
-    """Per-call GPU time of fn(i) in us, sorted, for calls that are shorter
-    than their own host-side launch cost. The stream is held by a bounded spin
-    kernel while the host queues all the calls and their events, so the calls
-    run back to back and each event pair sees the kernel, not the host."""
+    """GPU time of calls fn(i) that are shorter than their own host-side
+    launch cost. The stream is held by a bounded spin kernel while the host
+    queues the calls, so they run back to back on the GPU. Returns (mean us
+    per call over `steps` calls between one event pair, sorted per-call us
+    from a second pass with an event pair around each call; those include the
+    events' own cost, about 2 us)."""
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         fn(i)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     torch.cuda._sleep(100_000 * steps)  # clock ticks; covers the host's queueing
+    e0.record(stream)
+    for i in range(steps):
+        fn(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    mean = e0.elapsed_time(e1) * 1e3 / steps
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda._sleep(100_000 * steps)
     for i in range(steps):
         ev[2 * i].record(stream)
         fn(i)
         ev[2 * i + 1].record(stream)
     torch.cuda.synchronize()
-    return sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
+    return mean, sorted(ev[2 * i].elapsed_time(ev[2 * i + 1]) * 1e3 for i in range(steps))
 
 
 def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, warmup: int) -> int:
@@ -195,9 +205,9 @@ def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, w
     bs = [(b.to(dev), sb.to(dev)) for _ in range(copies)]
     a, sa = a.to(dev), sa.to(dev)
     out = torch.empty((m, n), dtype=torch.bfloat16, device=dev)
-    us = time_queued(torch, lambda i: mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out),
-                     steps, warmup)
-    avg = statistics.fmean(us)
+    avg, us = time_queued(torch,
+                          lambda i: mla.gemm_fp8_blockscale(a, sa, *bs[i % copies], out=out),
+                          steps, warmup)
     alg_bytes = m * k + n * k + 4 * m * (k // 128) + 4 * ((n + 127) // 128) * (k // 128) + 2 * m * n
     flops = 2 * m * n * k
     t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)
@@ -218,7 +228,8 @@ def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, w
         "higher_is_better": False, "dtype": "fp8", "data": "synthetic",
         "config": {"workload": f"gemm-fp8-m{m}", "m": m, "n": n, "k": k,
                    "scales": "activation 1x128, weight 128x128"},
-        "us_p10_p90": [round(us[len(us) // 10], 2), round(us[(9 * len(us)) // 10], 2)],
+        "us_p10_p90_with_events": [round(us[len(us) // 10], 2),
+                                   round(us[(9 * len(us)) // 10], 2)],
         "roofline": roof}), flush=True)
     return 0
 
@@ -236,11 +247,10 @@ def bench_absorb(torch, mla, workloads, dev, batch: int, heads: int, steps: int,
     q_nope, q_rope, o_lat = q_nope.to(dev), q_rope.to(dev), o_lat.to(dev)
     q = torch.empty((batch, heads, 576), dtype=torch.bfloat16, device=dev)
     o = torch.empty((batch, heads, 128), dtype=torch.bfloat16, device=dev)
-    us_q = time_queued(torch, lambda i: mla.absorb_q(q_nope, wk[i % copies], q_rope, out=q),
-                       steps, warmup)
-    us_o = time_queued(torch, lambda i: mla.absorb_out(o_lat, wv[i % copies], out=o),
-                       steps, warmup)
-    avg_q, avg_o = statistics.fmean(us_q), statistics.fmean(us_o)
+    avg_q, us_q = time_queued(
+        torch, lambda i: mla.absorb_q(q_nope, wk[i % copies], q_rope, out=q), steps, warmup)
+    avg_o, _ = time_queued(
+        torch, lambda i: mla.absorb_out(o_lat, wv[i % copies], out=o), steps, warmup)
     # Algorithmic bytes of mla_absorb_q: q_nope + W_UK + q_rope read, q written.
     bytes_q = 2 * (batch * heads * 128 + heads * 128 * 512 + batch * heads * 64
                    + batch * heads * 576)
@@ -262,7 +272,8 @@ def bench_absorb(torch, mla, workloads, dev, batch: int, heads: int, steps: int,
         "unit": "us/call", "n_gpus": 1, "steps": steps, "warmup": warmup,
         "higher_is_better": False, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"absorb-b{batch}-h{heads}", "batch": batch, "heads": heads},
-        "us_p10_p90": [round(us_q[len(us_q) // 10], 2), round(us_q[(9 * len(us_q)) // 10], 2)],
+        "us_p10_p90_with_events": [round(us_q[len(us_q) // 10], 2),
+                                   round(us_q[(9 * len(us_q)) // 10], 2)],
         "absorb_out": {"us": round(avg_o, 2), "algorithmic_bytes_per_launch": bytes_o,
                        "GB/s": round(bytes_o / (avg_o * 1e-6) / 1e9, 1)},
         "roofline": roof}), flush=True)

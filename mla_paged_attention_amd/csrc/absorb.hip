@@ -77,49 +77,52 @@ __device__ __forceinline__ void stage(const uint16_t* src, size_t stride, uint16
 }
 
 // q[b][h] = [q_nope[b][h] . W_UK[h], q_rope[b][h]]; blockIdx.x = h * (512 /
-// NS) + slice, blockIdx.y = 64-row batch group. Slice 0 also copies the rope
-// part of its rows.
-template <int NS>
+// NS) + slice, blockIdx.y = group of 64 TW batch rows, TW 16-row tiles per
+// wave. Slice 0 also copies the rope part of its rows.
+template <int NS, int TW>
 __global__ void __launch_bounds__(kAbsorbThreads) absorb_q_kernel(const uint16_t* x,
                                                                   const uint16_t* w,
                                                                   const uint16_t* rope,
                                                                   uint16_t* c, int32_t batch,
                                                                   int32_t heads) {
   constexpr int K = kNope, kOut = kLatent + kRope, kJ = NS / 16, kSplit = kLatent / NS;
-  constexpr int kPitch = NS + 8;
+  constexpr int kPitch = NS + 8, kRows = kAbsorbRows * TW;
   __shared__ __attribute__((aligned(16))) uint16_t sw[K * kPitch];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cc = lane & 15, g = lane >> 4;
   const int h = blockIdx.x / kSplit, n0 = (blockIdx.x % kSplit) * NS;
-  const int bt = blockIdx.y * kAbsorbRows + 16 * wave;  // this wave's batch tile
+  const int b0 = blockIdx.y * kRows;
+  const int bt = b0 + 16 * TW * wave;  // this wave's first batch row
 
-  // B operand: batch row bt + cc, k = 32 s + 8 g .. + 7 (a row past the
-  // batch reads the last row and is dropped at the store).
-  a_u32x4_t xf[K / 32];
-  {
-    const int b = min(bt + cc, batch - 1);
+  // B operand: batch row bt + 16 t + cc, k = 32 s + 8 g .. + 7 (a row past
+  // the batch reads the last row and is dropped at the store).
+  a_u32x4_t xf[TW][K / 32];
+#pragma unroll
+  for (int t = 0; t < TW; ++t) {
+    const int b = min(bt + 16 * t + cc, batch - 1);
     const uint16_t* p = x + (size_t(b) * heads + h) * K + 8 * g;
 #pragma unroll
-    for (int s = 0; s < K / 32; ++s) xf[s] = *reinterpret_cast<const a_u32x4_t*>(p + 32 * s);
+    for (int s = 0; s < K / 32; ++s) xf[t][s] = *reinterpret_cast<const a_u32x4_t*>(p + 32 * s);
   }
   stage<K, NS>(w + size_t(h) * K * kLatent + n0, kLatent, sw, tid);
   __syncthreads();
 
   if (n0 == 0) {
-    const int b0 = blockIdx.y * kAbsorbRows;
-    for (int i = tid; i < kAbsorbRows * kRope / 8; i += kAbsorbThreads) {
+    for (int i = tid; i < kRows * kRope / 8; i += kAbsorbThreads) {
       const int b = b0 + i / (kRope / 8), q = i % (kRope / 8);
       if (b < batch)
         *reinterpret_cast<a_u32x4_t*>(c + (size_t(b) * heads + h) * kOut + kLatent + 8 * q) =
             *reinterpret_cast<const a_u32x4_t*>(rope + (size_t(b) * heads + h) * kRope + 8 * q);
     }
   }
-  if (bt >= batch) return;  // no rows in this wave's tile
+  if (bt >= batch) return;  // no rows in this wave's tiles
 
-  a_f32x4_t acc[kJ];
+  a_f32x4_t acc[kJ][TW];
 #pragma unroll
-  for (int j = 0; j < kJ; ++j) acc[j] = a_f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < kJ; ++j)
+#pragma unroll
+    for (int t = 0; t < TW; ++t) acc[j][t] = a_f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // A operand by transposing reads: lane 4a + e of a 16-lane group gets
   // element e of the 8-byte words of lanes a, a + 4, a + 8, a + 12; lane l
@@ -138,17 +141,23 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_q_kernel(const uint16_t
           (__attribute__((address_space(3))) a_s16x4_t*)(p0 + 4 * kPitch));
       const a_bf16x8_t av = __builtin_bit_cast(
           a_bf16x8_t, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-          av, __builtin_bit_cast(a_bf16x8_t, xf[s]), acc[j], 0, 0, 0);
+#pragma unroll
+      for (int t = 0; t < TW; ++t)
+        acc[j][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            av, __builtin_bit_cast(a_bf16x8_t, xf[t][s]), acc[j][t], 0, 0, 0);
     }
   }
 
-  // D[4 g + r][cc] of block j = q[bt + cc][h][n0 + 16 j + 4 g + r].
-  const int b = bt + cc;
-  if (b < batch) {
-    uint16_t* dst = c + (size_t(b) * heads + h) * kOut + n0 + 4 * g;
+  // D[4 g + r][cc] of (j, t) = q[bt + 16 t + cc][h][n0 + 16 j + 4 g + r].
 #pragma unroll
-    for (int j = 0; j < kJ; ++j) *reinterpret_cast<a_u32x2_t*>(dst + 16 * j) = pack4(acc[j]);
+  for (int t = 0; t < TW; ++t) {
+    const int b = bt + 16 * t + cc;
+    if (b < batch) {
+      uint16_t* dst = c + (size_t(b) * heads + h) * kOut + n0 + 4 * g;
+#pragma unroll
+      for (int j = 0; j < kJ; ++j)
+        *reinterpret_cast<a_u32x2_t*>(dst + 16 * j) = pack4(acc[j][t]);
+    }
   }
 }
 
@@ -204,32 +213,64 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_out_kernel(const uint16
   }
 }
 
-// Workgroups of a launch with slices of width NS.
-inline long absorb_groups(int32_t batch, int32_t heads, int split) {
-  return long(heads) * split * ((batch + kAbsorbRows - 1) / kAbsorbRows);
+// Bytes one CU moves for an absorb_q launch with slices of NS columns and
+// `rows` batch rows per workgroup: the launch's workgroup bytes (activations,
+// weight slice, output, rope share) spread over min(workgroups, 256) CUs.
+// Re-reads of a slice or a row by another workgroup are L2 hits, but they
+// still pass through a CU, and a CU's own stream rate is what bounds these
+// small products.
+inline double absorb_q_cu_bytes(int32_t batch, int32_t heads, int ns, int rows) {
+  const long groups = long(heads) * (kLatent / ns) * ((batch + rows - 1) / rows);
+  const double r = double(batch < rows ? batch : rows);
+  const double per = r * kNope * 2 + double(kNope) * ns * 2 + r * ns * 2 +
+                     r * kRope * 2 * ns / kLatent;
+  return per * groups / double(groups < 256 ? groups : 256);
 }
 
 }  // namespace
 
-// Slice widths: the widest that still gives at least 256 workgroups (one per
-// CU), down to 32 latent columns for the query and 16 value columns for the
-// output.
+// absorb_q: the slice width and rows per workgroup that move the fewest
+// bytes per CU (absorb_q_cu_bytes) among four shapes.
 hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, const uint16_t* q_rope,
                            uint16_t* q, int32_t batch, int32_t heads, hipStream_t stream) {
-  const unsigned groups = unsigned((batch + kAbsorbRows - 1) / kAbsorbRows);
-  if (absorb_groups(batch, heads, kLatent / 128) >= 256)
-    hipLaunchKernelGGL(absorb_q_kernel<128>, dim3(unsigned(heads) * (kLatent / 128), groups),
-                       dim3(kAbsorbThreads), 0, stream, q_nope, w_uk, q_rope, q, batch, heads);
-  else
-    hipLaunchKernelGGL(absorb_q_kernel<32>, dim3(unsigned(heads) * (kLatent / 32), groups),
-                       dim3(kAbsorbThreads), 0, stream, q_nope, w_uk, q_rope, q, batch, heads);
+  struct Shape { int ns, tw; };
+  constexpr Shape kShapes[] = {{32, 1}, {128, 1}, {128, 2}, {256, 2}};
+  int best = 0;
+  double best_bytes = 0;
+  for (int i = 0; i < 4; ++i) {
+    const double v = absorb_q_cu_bytes(batch, heads, kShapes[i].ns, kAbsorbRows * kShapes[i].tw);
+    if (i == 0 || v < best_bytes) best = i, best_bytes = v;
+  }
+  const int ns = kShapes[best].ns, rows = kAbsorbRows * kShapes[best].tw;
+  const dim3 grid(unsigned(heads) * unsigned(kLatent / ns), unsigned((batch + rows - 1) / rows));
+  const dim3 block(kAbsorbThreads);
+  switch (best) {
+    case 0:
+      hipLaunchKernelGGL((absorb_q_kernel<32, 1>), grid, block, 0, stream, q_nope, w_uk, q_rope,
+                         q, batch, heads);
+      break;
+    case 1:
+      hipLaunchKernelGGL((absorb_q_kernel<128, 1>), grid, block, 0, stream, q_nope, w_uk, q_rope,
+                         q, batch, heads);
+      break;
+    case 2:
+      hipLaunchKernelGGL((absorb_q_kernel<128, 2>), grid, block, 0, stream, q_nope, w_uk, q_rope,
+                         q, batch, heads);
+      break;
+    default:
+      hipLaunchKernelGGL((absorb_q_kernel<256, 2>), grid, block, 0, stream, q_nope, w_uk, q_rope,
+                         q, batch, heads);
+      break;
+  }
   return hipGetLastError();
 }
 
+// absorb_out: 32 value columns per workgroup, or 16 where that leaves fewer
+// than 256 workgroups.
 hipError_t launch_absorb_out(const uint16_t* o_latent, const uint16_t* w_uv, uint16_t* o,
                              int32_t batch, int32_t heads, hipStream_t stream) {
   const unsigned groups = unsigned((batch + kAbsorbRows - 1) / kAbsorbRows);
-  if (absorb_groups(batch, heads, kNope / 32) >= 256)
+  if (long(heads) * (kNope / 32) * groups >= 256)
     hipLaunchKernelGGL(absorb_out_kernel<32>, dim3(unsigned(heads) * (kNope / 32), groups),
                        dim3(kAbsorbThreads), 0, stream, o_latent, w_uv, o, batch, heads);
   else

@@ -38,7 +38,12 @@ def magnitude(x, w):
     return torch.matmul(x.double().abs().permute(1, 0, 2), w.double().abs()).permute(1, 0, 2).numpy()
 
 
-@pytest.mark.parametrize("batch,heads", [(1, 16), (17, 16), (64, 1), (100, 20), (512, 16), (3, 128)])
+# Shapes chosen so that each launch shape of mla_absorb_q runs, with ragged
+# last row groups: 32-column slices (1, 17, 64 rows), 128-column slices with
+# one tile per wave (100 x 20) or two (512 x 16, 250 x 32), 256-column slices
+# (3 x 128, 130 x 128).
+@pytest.mark.parametrize("batch,heads", [(1, 16), (17, 16), (64, 1), (100, 20), (512, 16),
+                                         (250, 32), (3, 128), (130, 128)])
 def test_absorb_q(orc, batch, heads):
     q_nope, q_rope, w_uk, _, _ = workloads.make_absorb(batch, heads, seed=batch + heads)
     q = mla.absorb_q(q_nope.to(DEV), w_uk.to(DEV), q_rope.to(DEV))
