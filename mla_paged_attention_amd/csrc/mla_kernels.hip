@@ -65,50 +65,55 @@ __device__ __forceinline__ unsigned short bf16_bits(float x) {
 }
 
 // ----------------------------------------------------------------------------
-// Block-wide exclusive scan over NT threads.
+// Wave-level scan and maximum on DPP row shifts (rows of 16 lanes: shifts 1,
+// 2, 4, 8 with zero fill), then the row totals through v_readlane. All 64
+// lanes must be active.
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+  const int r0 = __builtin_amdgcn_readlane(v, 15), r1 = __builtin_amdgcn_readlane(v, 31),
+            r2 = __builtin_amdgcn_readlane(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  return v + (row > 0 ? r0 : 0) + (row > 1 ? r1 : 0) + (row > 2 ? r2 : 0);
+}
+
+__device__ __forceinline__ int wave_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(v, v, 0x118, 0xf, 0xf, false));
+  return max(max(__builtin_amdgcn_readlane(v, 15), __builtin_amdgcn_readlane(v, 31)),
+             max(__builtin_amdgcn_readlane(v, 47), __builtin_amdgcn_readlane(v, 63)));
+}
+
+// Block-wide exclusive scan over NT threads: wave scans, then every thread
+// adds the totals of the waves before its own.
 template <int NT = kPlanThreads>
 __device__ int block_exclusive_scan(int v, int* s_wave, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    int t = __shfl_up(inc, d);
-    if (lane >= d) inc += t;
-  }
+  const int inc = wave_inclusive_scan(v);
   if (lane == 63) s_wave[wave] = inc;
   __syncthreads();
-  if (wave == 0) {
-    int w = lane < NT / 64 ? s_wave[lane] : 0;
-    int winc = w;
+  int base = 0, tot = 0;
 #pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      int t = __shfl_up(winc, d);
-      if (lane >= d) winc += t;
-    }
-    if (lane < NT / 64) s_wave[16 + lane] = winc - w;
-    if (lane == NT / 64 - 1) s_wave[32] = winc;
+  for (int w = 0; w < NT / 64; ++w) {
+    const int t = s_wave[w];
+    base += w < wave ? t : 0;
+    tot += t;
   }
+  *total = tot;
   __syncthreads();
-  int res = s_wave[16 + wave] + inc - v;
-  *total = s_wave[32];
-  __syncthreads();
-  return res;
+  return base + inc - v;
 }
 
 // Block-wide exclusive scans of three values at once (same barriers).
 template <int NT>
 __device__ int3 block_exclusive_scan3(int3 v, int* s_wave, int3* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int3 inc = v;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int tx = __shfl_up(inc.x, d), ty = __shfl_up(inc.y, d), tz = __shfl_up(inc.z, d);
-    if (lane >= d) {
-      inc.x += tx;
-      inc.y += ty;
-      inc.z += tz;
-    }
-  }
+  const int3 inc = make_int3(wave_inclusive_scan(v.x), wave_inclusive_scan(v.y),
+                             wave_inclusive_scan(v.z));
   if (lane == 63) {
     s_wave[wave] = inc.x;
     s_wave[16 + wave] = inc.y;
@@ -154,8 +159,7 @@ constexpr int kSnakeMaxBatch = 4096;   // largest batch the snake plan sorts
 
 template <int NT>
 __device__ __forceinline__ int block_max(int v, int* s_wave) {
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) v = max(v, __shfl_xor(v, d));
+  v = wave_max(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   __syncthreads();
   if (lane == 0) s_wave[wave] = v;
@@ -1672,13 +1676,20 @@ __device__ __forceinline__ void combine_rows(const float* part_out, const float*
   f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   for (int s0 = 0; s0 < nr; s0 += kCombineUnroll) {
+    // Rows past the request's last are not loaded (the count is uniform
+    // across the workgroup, so the skipped loads are branched over).
+    const int cnt = min(nr - s0, kCombineUnroll);
     f32x4_t v[kCombineUnroll];
     float ls[kCombineUnroll];
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) {
-      const int s = min(s0 + k, nr - 1);
-      ls[k] = s0 + k < nr ? part_lse[size_t(r0 + s) * H + h] : -INFINITY;
-      v[k] = *reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s) * H + h) * kDV + d);
+      if (k < cnt) {
+        ls[k] = part_lse[size_t(r0 + s0 + k) * H + h];
+        v[k] = *reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s0 + k) * H + h) * kDV + d);
+      } else {
+        ls[k] = -INFINITY;
+        v[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
     }
     float mb = ls[0];
 #pragma unroll
