@@ -1653,42 +1653,50 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
 }
 
 // ----------------------------------------------------------------------------
-// LSE combine: one workgroup per (request, 16-head tile, 64-feature chunk);
-// thread (head hh, sub) merges features 4 sub .. 4 sub + 3 of the chunk,
-// with kCombineUnroll partial rows in flight.
-constexpr int kCombineChunk = 64;
-constexpr int kCombineChunks = kDV / kCombineChunk;  // 8
-constexpr int kCombineUnroll = 16;
+// LSE combine: one workgroup per (request, 16-head tile, feature chunk);
+// thread (head hh, sub) merges kCombineF features of the chunk from
+// kCombineUnroll partial rows in flight.
+constexpr int kCombineF = 8;                          // features per thread
+constexpr int kCombineChunk = 16 * kCombineF;         // features per workgroup
+constexpr int kCombineChunks = kDV / kCombineChunk;
+constexpr int kCombineUnroll = 64 / kCombineF;        // rows per batch of loads
 constexpr int kCombineGrid = 1 << 30;  // no cap: one workgroup per (request, tile, chunk)
 
-// Merge rows r0 .. r0 + nr - 1 of request b for head tile ht and 64-feature
-// chunk `chunk`: thread (head tid / 16, features 4 (tid % 16) ..) of 256.
+// Merge rows r0 .. r0 + nr - 1 of request b for head tile ht and feature
+// chunk `chunk`: thread (head tid / 16, features kCombineF (tid % 16) ..) of 256.
 __device__ __forceinline__ void combine_rows(const float* part_out, const float* part_lse, int r0,
                                              int nr, uint16_t* out, float* lse, int b, int H,
                                              int ht, int chunk) {
+  constexpr int V = kCombineF / 4;
   const int tid = threadIdx.x;
   const int h = ht * kHeadTile + (tid >> 4);
   if (h >= H) return;
-  const int d = chunk * kCombineChunk + 4 * (tid & 15);
+  const int d = chunk * kCombineChunk + kCombineF * (tid & 15);
   // One pass with a running maximum, kCombineUnroll rows in flight:
   // acc and W are kept relative to M and rescaled when M rises.
   float M = -INFINITY;
-  f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   float W = 0.f;
   for (int s0 = 0; s0 < nr; s0 += kCombineUnroll) {
     // Rows past the request's last are not loaded (the count is uniform
     // across the workgroup, so the skipped loads are branched over).
     const int cnt = min(nr - s0, kCombineUnroll);
-    f32x4_t v[kCombineUnroll];
+    f32x4_t v[kCombineUnroll][V];
     float ls[kCombineUnroll];
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) {
       if (k < cnt) {
         ls[k] = part_lse[size_t(r0 + s0 + k) * H + h];
-        v[k] = *reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s0 + k) * H + h) * kDV + d);
+        const f32x4_t* src =
+            reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s0 + k) * H + h) * kDV + d);
+#pragma unroll
+        for (int i = 0; i < V; ++i) v[k][i] = src[i];
       } else {
         ls[k] = -INFINITY;
-        v[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < V; ++i) v[k][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       }
     }
     float mb = ls[0];
@@ -1697,22 +1705,35 @@ __device__ __forceinline__ void combine_rows(const float* part_out, const float*
     if (mb == -INFINITY) continue;  // only empty rows in this batch
     const float Mn = fmaxf(M, mb);
     const float a = M == -INFINITY ? 0.f : fast_exp2((M - Mn) * kLog2e);
-    acc *= a;
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] *= a;
     W *= a;
     M = Mn;
 #pragma unroll
     for (int k = 0; k < kCombineUnroll; ++k) {
       const float w = ls[k] != -INFINITY ? fast_exp2((ls[k] - M) * kLog2e) : 0.f;
-      if (w != 0.f) acc += w * v[k];  // an empty row's values are never used
+      if (w != 0.f) {  // an empty row's values are never used
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] += w * v[k][i];
+      }
       W += w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  const f32x4_t o = acc * inv;
-  u32x2_t pk;
-  pk[0] = unsigned(bf16_bits(o[0])) | (unsigned(bf16_bits(o[1])) << 16);
-  pk[1] = unsigned(bf16_bits(o[2])) | (unsigned(bf16_bits(o[3])) << 16);
-  *reinterpret_cast<u32x2_t*>(out + (size_t(b) * H + h) * kDV + d) = pk;
+  u32x2_t pk[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    const f32x4_t o = acc[i] * inv;
+    pk[i][0] = unsigned(bf16_bits(o[0])) | (unsigned(bf16_bits(o[1])) << 16);
+    pk[i][1] = unsigned(bf16_bits(o[2])) | (unsigned(bf16_bits(o[3])) << 16);
+  }
+  uint16_t* dst = out + (size_t(b) * H + h) * kDV + d;
+  if constexpr (V == 2) {
+    *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < V; ++i) *reinterpret_cast<u32x2_t*>(dst + 4 * i) = pk[i];
+  }
   if (chunk == 0 && (tid & 15) == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
