@@ -201,8 +201,12 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
       return MLA_ERR_HIP;
     lens = sp_len;
   }
-  if (mla::launch_plan(lens, a.batch, int32_t(cap), a.num_splits, int32_t(max_parts), w,
-                       a.workspace, s) != hipSuccess)
+  // Small batches on the contiguous plan work it out inside the attention
+  // kernel: one launch fewer.
+  const bool inline_plan = a.num_splits == 0 && a.batch <= mla::kInlinePlanBatch &&
+                           a.batch < 2 * max_parts;
+  if (!inline_plan && mla::launch_plan(lens, a.batch, int32_t(cap), a.num_splits,
+                                       int32_t(max_parts), w, a.workspace, s) != hipSuccess)
     return MLA_ERR_HIP;
   if (!rec(1)) return MLA_ERR_HIP;
 
@@ -238,6 +242,10 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   args.sparse_rows = sparse ? reinterpret_cast<const int32_t*>(ws + w.sp_rows) : nullptr;
   args.sparse_stride = sparse ? int32_t(mla::sparse_stride(a.topk)) : 0;
   args.zero_row = sparse ? ws + w.zero_row : nullptr;
+  args.inline_plan = inline_plan ? 1 : 0;
+  args.wr_row_ptr = row_ptr;
+  args.wr_split = split;
+  args.wr_header = header;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
   int64_t parts_launched = (parts + 7) / 8 * 8;
   if (parts_launched * args.head_tiles > INT32_MAX) return MLA_ERR_INVALID_ARG;

@@ -138,7 +138,17 @@ struct AttnArgs {
   const int32_t* sparse_rows;
   int32_t sparse_stride;
   const uint8_t* zero_row;
+  // Automatic plan worked out inside the attention kernel (batches of at
+  // most kInlinePlanBatch requests with a contiguous plan): no plan launch;
+  // the partition-0 workgroups write row_ptr, split and header for the
+  // combine.
+  int32_t inline_plan;
+  int32_t* wr_row_ptr;
+  int32_t* wr_split;
+  int32_t* wr_header;
 };
+
+constexpr int kInlinePlanBatch = 64;  // one request per lane of a wave
 
 // Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
 // only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.

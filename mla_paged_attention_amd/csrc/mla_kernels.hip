@@ -423,25 +423,86 @@ __global__ void __launch_bounds__(NT) plan_kernel(
 // when row < 0, else as partial row `row`. Uniform across the workgroup.
 template <typename Fn>
 __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, Fn&& fn) {
+  // The item list of the three modes, then one loop with the only call of
+  // fn (the whole attention body is inlined there).
+  __shared__ int4 s_items[kInlinePlanBatch];
+  __shared__ int s_nitems;
+  int n = 0, i0 = 0;
   if (a.num_splits > 0) {
     // Forced split k of request b; an empty split still writes its
     // (zero, -inf) partial because the combine reads every row.
-    const int S = a.num_splits;
-    if (part >= a.batch * S) return;
-    const int b = part / S, k = part - b * S;
-    const int nu = (clamp_len(a.seq_lens[b], a.cap_tokens) + kUnit - 1) / kUnit;
-    fn(b, int((long long)k * nu / S), int((long long)(k + 1) * nu / S), S > 1 ? part : -1);
-    return;
+    n = part < a.batch * a.num_splits ? 1 : 0;
+  } else if (a.inline_plan) {
+    // The contiguous plan of plan_kernel, worked out by the first wave from
+    // seq_lens (request = lane): costs, their prefix, the per-partition
+    // target P, the pieces k of each request and the partial rows of split
+    // requests. This partition's pieces go to LDS in request order.
+    if (threadIdx.x < 64) {
+      const int lane = threadIdx.x;
+      const bool live = lane < a.batch;
+      const int units = live ? units_of(clamp_len(a.seq_lens[lane], a.cap_tokens)) : 0;
+      const int cost = live ? kOverheadUnits + units : 0;
+      const int cinc = wave_inclusive_scan(cost);
+      const int total = __builtin_amdgcn_readlane(cinc, 63);
+      int P = (total + a.parts_cap - 1) / a.parts_cap;
+      if (P < kMinPartUnits) P = kMinPartUnits;
+      const int ub = cinc - cost + kOverheadUnits, ue = cinc;
+      const int first = ub / P;
+      const int k = live ? (ue - 1) / P - first + 1 : 0;
+      const int nrows = k > 1 ? k : 0;
+      const int rinc = wave_inclusive_scan(nrows);
+      const int sinc = wave_inclusive_scan(k > 1 ? 1 : 0);
+      if (part == 0) {
+        // Same values from every partition-0 workgroup (one per head tile).
+        if (live) {
+          a.wr_row_ptr[lane] = rinc - nrows;
+          if (k > 1) a.wr_split[sinc - 1] = lane;
+        }
+        if (lane == 0) {
+          a.wr_row_ptr[a.batch] = __builtin_amdgcn_readlane(rinc, 63);
+          a.wr_header[0] = (total + P - 1) / P;
+          a.wr_header[1] = P;
+          a.wr_header[2] = __builtin_amdgcn_readlane(sinc, 63);
+          a.wr_header[3] = kPlanContiguous;
+        }
+      }
+      const bool mine = part < a.parts_cap && live && first <= part && part < first + k;
+      const uint64_t m = __ballot(mine);
+      if (mine) {
+        const int idx = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
+        const int p0 = max(ub, part * P), p1 = min(ue, (part + 1) * P);
+        s_items[idx] = make_int4(lane, p0 - ub, p1 - ub, k > 1 ? rinc - nrows + part - first : -1);
+      }
+      if (lane == 0) s_nitems = __popcll(m);
+    }
+    __syncthreads();
+    n = __builtin_amdgcn_readfirstlane(s_nitems);
+  } else if (part < a.parts_cap) {
+    i0 = max(a.part_ptr[part], 0);
+    n = min(a.part_ptr[part + 1], a.items_cap) - i0;
   }
-  if (part >= a.parts_cap) return;
-  const int i0 = max(a.part_ptr[part], 0), i1 = min(a.part_ptr[part + 1], a.items_cap);
-  for (int i = i0; i < i1; ++i) {
-    const int4 it = a.work[i];
+  for (int i = 0; i < n; ++i) {
+    int b, u0, u1, row;
+    if (a.num_splits > 0) {
+      const int S = a.num_splits;
+      b = part / S;
+      const int k = part - b * S;
+      const int nu = (clamp_len(a.seq_lens[b], a.cap_tokens) + kUnit - 1) / kUnit;
+      u0 = int((long long)k * nu / S);
+      u1 = int((long long)(k + 1) * nu / S);
+      row = S > 1 ? part : -1;
+    } else {
+      const int4 it = a.inline_plan ? s_items[i] : a.work[i0 + i];
+      b = __builtin_amdgcn_readfirstlane(it.x);
+      u0 = __builtin_amdgcn_readfirstlane(it.y);
+      u1 = __builtin_amdgcn_readfirstlane(it.z);
+      row = __builtin_amdgcn_readfirstlane(it.w);
+    }
     // Items that would address outside the buffers are skipped (never
-    // produced by the plan; a guard against a corrupted workspace).
-    if (unsigned(it.x) >= unsigned(a.batch) || it.y < 0 || it.z < it.y || it.w >= a.rows_cap)
-      continue;
-    fn(it.x, it.y, it.z, it.w);
+    // produced by a plan; a guard against a corrupted workspace).
+    if (unsigned(b) >= unsigned(a.batch) || u0 < 0 || u1 < u0 || row >= a.rows_cap) continue;
+    fn(b, u0, u1, row);
   }
 }
 
