@@ -290,6 +290,8 @@ def main(argv=None) -> int:
     ap.add_argument("--q-len", type=int, default=1,
                     help="query tokens per request (speculative decoding, causal)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the call replayed from a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--gemm", type=int, default=0, metavar="M",
                     help="instead of decoding, time the block-scaled E4M3 projection at "
@@ -354,14 +356,14 @@ def main(argv=None) -> int:
     log(f"tokens={wl.total_tokens} pool={pool_bytes / 2**20:.0f} MiB copies={copies} "
         f"workspace={nbytes / 2**20:.1f} MiB")
 
-    def call(i, events=None):
+    def call(i, events=None, on=stream):
         if wl.indices is not None:
             mla.decode_sparse(q, kvs[i % copies], bt, sl, idx, scale=wl.scale,
                               num_splits=args.num_splits, kv_scale=wl.kv_scale, out=out, lse=lse,
-                              workspace=ws, stream=stream, events=events)
+                              workspace=ws, stream=on, events=events)
             return
         mla.decode(q, kvs[i % copies], bt, sl, scale=wl.scale, num_splits=args.num_splits,
-                   kv_scale=wl.kv_scale, out=out, lse=lse, workspace=ws, stream=stream,
+                   kv_scale=wl.kv_scale, out=out, lse=lse, workspace=ws, stream=on,
                    events=events)
 
     for i in range(args.warmup):
@@ -398,6 +400,27 @@ def main(argv=None) -> int:
     attn_avg = statistics.fmean(attn_ms)
     log(f"attention kernel {attn_avg * 1e3:.1f} us avg, plan {statistics.fmean(plan_ms) * 1e3:.1f},"
         f" combine {statistics.fmean(comb_ms) * 1e3:.1f}")
+
+    graph_us = None
+    if args.graph:
+        # Timed region 3 (optional): one HIP graph holding `copies` calls
+        # (one per cache copy), replayed back to back.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(copies):
+                call(i, on=None)  # the capture stream
+        torch.cuda.synchronize()
+        reps = max(1, args.steps // copies)
+        graph.replay()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        g0.record(stream)
+        for _ in range(reps):
+            graph.replay()
+        g1.record(stream)
+        torch.cuda.synchronize()
+        graph_us = round(g0.elapsed_time(g1) * 1e3 / (reps * copies), 2)
+        log(f"graph replays: {graph_us} us/call")
 
     alg_bytes = algorithmic_bytes(wl)
     alg_flops = algorithmic_flops(wl)
@@ -463,6 +486,8 @@ def main(argv=None) -> int:
         "roofline": roofline,
         "cpu_baseline": None,
     }
+    if graph_us is not None:
+        result["graph_us_per_call"] = graph_us
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample")
         result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)

@@ -217,6 +217,26 @@ def test_small_workspace_auto_mode(orc):
         compare(out, lse, ref_out, ref_lse, what=f"auto with {nbytes} B workspace")
 
 
+def test_plan_modes_agree(orc):
+    # 64 requests: the attention kernel works the contiguous plan out itself;
+    # 65: plan_kernel's contiguous plan; 64 with a workspace too small for
+    # partial rows: plan_kernel's snake plan. Lengths include empty, single
+    # token and long requests cut into many pieces.
+    gen = np.random.default_rng(61)
+    lens = [0, 1, 15, 16, 17, 20000, 9000] + gen.integers(0, 3000, size=58).tolist()
+    for batch in (64, 65):
+        wl = workloads.make_workload(batch=batch, num_heads=16, seq=("fixed", lens[:batch]),
+                                     block_size=32, seed=62, poison=True)
+        ref_out, ref_lse = run_oracle(orc, wl)
+        out, lse = to_np(*run_gpu(wl, 0))
+        compare(out, lse, ref_out, ref_lse, what=f"automatic plan, batch {batch}")
+        if batch == 64:
+            meta = mla.get_workspace_size(wl.batch, wl.num_heads, 0, 1, 0)
+            ws = torch.empty(meta, dtype=torch.uint8, device="cuda:0")
+            out, lse = to_np(*run_gpu(wl, 0, workspace=ws))
+            compare(out, lse, ref_out, ref_lse, what="batch 64, no partial rows (snake plan)")
+
+
 def test_forced_workspace_too_small():
     wl = workloads.make_config("tiny")
     ws = torch.empty(mla.get_workspace_size(wl.batch, wl.num_heads, 0, 1, 0), dtype=torch.uint8,
