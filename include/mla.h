@@ -128,7 +128,10 @@ size_t mla_get_workspace_size_multi_token(int64_t batch, int64_t num_heads, int6
  *               ranges is merged by the LSE combine. 1..16 = every request is
  *               cut into exactly that many near-equal token ranges (some may
  *               be empty), merged the same way.
- *  batch        number of requests (0 is a no-op)
+ *  batch        number of requests (0 is a no-op); batch * (1 + ceil(
+ *               max_blocks_per_seq * block_size / 16)) must not exceed
+ *               2^30 - 1 (the split plan sums per-request costs in int32;
+ *               with sparse decode topk stands for the product)
  *  max_blocks_per_seq  row length of block_table (>= 1)
  *  num_blocks   number of physical blocks in kv_cache (>= 1)
  *  kv_dtype     mla_kv_dtype_t

@@ -119,6 +119,13 @@ mla_status_t validate_decode(const DecodeArgs& a) {
     if (int64_t(a.batch) * mla::sparse_stride(a.topk) > INT32_MAX) return MLA_ERR_INVALID_ARG;
   }
   if (a.batch == 0) return MLA_OK;
+  {
+    // The split plan sums per-request costs (1 + 16-token units, at most the
+    // cap) in int32: the largest total, plus a partition of slack, must fit.
+    const int64_t cap_tokens = a.topk > 0 ? a.topk : int64_t(a.max_blocks) * a.block_size;
+    const int64_t max_cost = mla::kOverheadUnits + (cap_tokens + mla::kUnit - 1) / mla::kUnit;
+    if (int64_t(a.batch) * max_cost > INT32_MAX / 2) return MLA_ERR_INVALID_ARG;
+  }
   if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out || !a.workspace)
     return MLA_ERR_INVALID_ARG;
   if (a.topk > 0 && (!a.indices || !aligned(a.indices, 4))) return MLA_ERR_INVALID_ARG;

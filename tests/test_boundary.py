@@ -329,6 +329,16 @@ def test_gemm_binding_rejects():
         mla.gemm_fp8_blockscale(a.float(), torch.zeros((4, 2)), a, torch.zeros((1, 2)))
 
 
+def test_plan_cost_total_bound():
+    # batch * (1 + ceil(max_blocks * block_size / 16)) must stay within
+    # 2^30 - 1: at block 64 and 2^20 blocks per row (2^22 + 1 units), 255
+    # requests fit and 256 do not. A too-small workspace stops the accepted
+    # case before any HIP call.
+    big = dict(max_blocks=1 << 20, bs=64, num_blocks=1 << 20, ws_bytes=128)
+    assert _decode(batch=256, **big) == mla.MLA_ERR_INVALID_ARG
+    assert _decode(batch=255, **big) == mla.MLA_ERR_WORKSPACE_TOO_SMALL
+
+
 def test_absorb_rejects():
     lib = mla.library()
     f = ctypes.c_void_p(FAKE)
