@@ -212,7 +212,6 @@ __global__ void __launch_bounds__(NT) plan_kernel(
   __shared__ int s_wave[48];
   __shared__ int s_cnt[kMaxPlanParts + 1];
   __shared__ int s_bucket[4 * NT];
-  __shared__ int s_pb[kSnakeMaxBatch + 1];
   __shared__ short s_pq[kSnakeMaxBatch + kMaxPlanParts];
   const int tid = threadIdx.x;
   if (num_splits > 0) {
@@ -532,6 +531,13 @@ constexpr int kTileBytesBf16 = kTile * kRowBytes;     // 36864
 constexpr int kDmaPerThread = kTile * kRowChunks / kThreads;  // 9
 static_assert(kTile * kRowChunks == kDmaPerThread * kThreads, "tile must split evenly");
 
+// Cache policy of the ring's loads: the non-temporal (nt) bit. A cache row is
+// read once per call (one head group) or twice within microseconds (two head
+// groups on the same XCD), so it is streamed rather than kept. Measured at
+// batch 512 x 16 heads: 219.6 -> 197.3 us per attention launch (6.2 TB/s of
+// algorithmic bytes); 128 heads gain 1-3 %.
+constexpr int kRingLoadPolicy = 2;
+
 template <int N>
 __device__ __forceinline__ void wait_vmem() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -710,7 +716,8 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
       for (int i = 0; i < kDmaPerThread; ++i) {
         const uint8_t* src = ((dma_hi >> i) & 1 ? r1 : r0) + dma_off[i];
         __builtin_amdgcn_global_load_lds(
-            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0, 0);
+            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0,
+            kRingLoadPolicy);
       }
     };
 
@@ -1243,7 +1250,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
         const uint8_t* base = (us & 2) ? ((us & 1) ? r[3] : r[2]) : ((us & 1) ? r[1] : r[0]);
         __builtin_amdgcn_global_load_lds(
             base + dma_off[i], (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16),
-            16, 0, 0);
+            16, 0, kRingLoadPolicy);
       }
     };
     // Sparse: ids of tile k (a quarter per P.V wave) into slot k % 8.
@@ -1270,7 +1277,8 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
         const uint32_t ch16 = dma_off[i] & 0xffffu;
         const uint8_t* src = rid[i] >= 0 ? a.kv + size_t(rid[i]) * kRowB + ch16 : a.zero_row + ch16;
         __builtin_amdgcn_global_load_lds(
-            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0, 0);
+            src, (void __attribute__((address_space(3)))*)(dst + i * kThreads * 16), 16, 0,
+            kRingLoadPolicy);
       }
     };
 
@@ -1372,7 +1380,6 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
           // whose matrix ops then fill the gaps and the softmax below.
           __builtin_amdgcn_s_setprio(3);
           if (work) {
-            const uint32_t st = ring_lds + uint32_t(s % kStages) * kTileBytesBf16;
             int nv[kUnits];
             tile_nv(s, nv);
             // Row c's visible tokens per unit (none once past its query token).
