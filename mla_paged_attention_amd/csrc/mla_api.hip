@@ -209,11 +209,13 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
     lens = sp_len;
   }
   // Small batches on the contiguous plan work it out inside the attention
-  // kernel: one launch fewer.
+  // kernel, and forced splits need no plan (piece k of request b is
+  // partition b * S + k, its partial row too): one launch fewer.
   const bool inline_plan = a.num_splits == 0 && a.batch <= mla::kInlinePlanBatch &&
                            a.batch < 2 * max_parts;
-  if (!inline_plan && mla::launch_plan(lens, a.batch, int32_t(cap), a.num_splits,
-                                       int32_t(max_parts), w, a.workspace, s) != hipSuccess)
+  if (!inline_plan && a.num_splits == 0 &&
+      mla::launch_plan(lens, a.batch, int32_t(cap), int32_t(max_parts), w, a.workspace, s) !=
+          hipSuccess)
     return MLA_ERR_HIP;
   if (!rec(1)) return MLA_ERR_HIP;
 
@@ -263,7 +265,7 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
 
   if (a.num_splits > 1) {
     if (mla::launch_combine(part_out, part_lse, row_ptr, static_cast<uint16_t*>(a.out), a.lse,
-                            a.batch, rows, 0, s) != hipSuccess)
+                            a.batch, rows, 0, a.num_splits, s) != hipSuccess)
       return MLA_ERR_HIP;
   } else if (a.num_splits == 0 && max_parts > 1 && w.rows > 0) {
     // Split requests are fewer than the partitions (each is costlier than
@@ -406,7 +408,7 @@ mla_status_t mla_combine(const float* partial_out, const float* partial_lse,
   if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
   if (batch == 0) return MLA_OK;
   if (mla::launch_combine(partial_out, partial_lse, split_indptr, static_cast<uint16_t*>(out),
-                          lse, batch, num_heads, 1, static_cast<hipStream_t>(stream)) !=
+                          lse, batch, num_heads, 1, 0, static_cast<hipStream_t>(stream)) !=
       hipSuccess)
     return MLA_ERR_HIP;
   return MLA_OK;

@@ -153,8 +153,8 @@ constexpr int kInlinePlanBatch = 64;  // one request per lane of a wave
 // Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
 // only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
-                       int32_t num_splits, int32_t max_parts, const WorkspaceLayout& w,
-                       void* workspace, hipStream_t stream);
+                       int32_t max_parts, const WorkspaceLayout& w, void* workspace,
+                       hipStream_t stream);
 
 // kv_fp8: 0 = bf16 cache, 1 = E4M3 cache. `parts_launched` is a multiple of 8.
 hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_launched,
@@ -162,7 +162,8 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
 
 hipError_t launch_combine(const float* part_out, const float* part_lse,
                           const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
-                          int32_t num_heads, int zero_empty, hipStream_t stream);
+                          int32_t num_heads, int zero_empty, int32_t uniform,
+                          hipStream_t stream);
 
 // Sparse decode prepass: rows[b * stride + k] = physical row of listed
 // position k of request b, or -1; eff_len[b] = topk; zero_row = 1152 zero bytes.

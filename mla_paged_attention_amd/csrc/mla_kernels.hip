@@ -193,8 +193,8 @@ __device__ int block_scan_lds(int* s, int n, int* s_wave) {
   return tot;
 }
 
-// One workgroup. Forced mode (num_splits > 0): request b's partial rows
-// start at b * num_splits. Automatic mode: a list of work items
+// One workgroup, automatic splits only (forced splits need no plan: piece k
+// of request b is partition and partial row b * S + k). A list of work items
 // (request, unit begin, unit end, partial row or -1 when the item is the
 // whole request) per partition, at most max_parts partitions, with costs
 // balanced in units of 16 tokens plus a fixed per-request overhead:
@@ -206,24 +206,14 @@ __device__ int block_scan_lds(int* s, int n, int* s_wave) {
 //    equal partitions; a request straddling a cut becomes several pieces.
 template <int NT>
 __global__ void __launch_bounds__(NT) plan_kernel(
-    const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t num_splits,
-    int32_t max_parts, int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr,
-    int4* work, int32_t* split) {
+    const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t max_parts,
+    int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr, int4* work,
+    int32_t* split) {
   __shared__ int s_wave[48];
   __shared__ int s_cnt[kMaxPlanParts + 1];
   __shared__ int s_bucket[4 * NT];
   __shared__ short s_pq[kSnakeMaxBatch + kMaxPlanParts];
   const int tid = threadIdx.x;
-  if (num_splits > 0) {
-    for (int b = tid; b <= batch; b += NT) row_ptr[b] = num_splits > 1 ? b * num_splits : 0;
-    if (tid == 0) {
-      header[0] = batch * num_splits;
-      header[1] = 0;
-      header[2] = 0;
-      header[3] = -1;
-    }
-    return;
-  }
   if (batch <= 4 * NT) {
     // Fast path: thread t owns requests 4 t .. 4 t + 3, kept in registers.
     int units[4], cost[4], c0[4];
@@ -1805,15 +1795,19 @@ __device__ __forceinline__ void combine_rows(const float* part_out, const float*
   if (chunk == 0 && (tid & 15) == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
+// Rows of request b: row_ptr[b] .. row_ptr[b + 1] - 1, or with uniform > 0
+// (forced splits, no plan launched) b * uniform .. b * uniform + uniform - 1.
 __global__ void __launch_bounds__(256) combine_kernel(const float* part_out, const float* part_lse,
                                                       const int32_t* row_ptr, uint16_t* out,
                                                       float* lse, int32_t batch, int32_t H,
-                                                      int32_t tiles, int zero_empty) {
+                                                      int32_t tiles, int zero_empty,
+                                                      int32_t uniform) {
   const int blk = blockIdx.x;
   const int chunk = blk % kCombineChunks;
   const int bt = blk / kCombineChunks;
   const int b = bt / tiles, ht = bt - (bt / tiles) * tiles;
-  const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
+  const int r0 = uniform > 0 ? b * uniform : row_ptr[b];
+  const int nr = uniform > 0 ? uniform : row_ptr[b + 1] - r0;
   if (nr <= 0 && !zero_empty) return;
   combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
 }
@@ -1841,14 +1835,14 @@ __global__ void __launch_bounds__(256) combine_split_kernel(
 // Host-side launchers.
 
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
-                       int32_t num_splits, int32_t max_parts, const WorkspaceLayout& w,
-                       void* workspace, hipStream_t stream) {
+                       int32_t max_parts, const WorkspaceLayout& w, void* workspace,
+                       hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   // Small batches and partition counts: a quarter of the threads (cheaper barriers).
   const bool small = batch <= 4 * kPlanThreadsSmall && max_parts < 4 * kPlanThreadsSmall;
   auto kern = small ? plan_kernel<kPlanThreadsSmall> : plan_kernel<kPlanThreads>;
   hipLaunchKernelGGL(kern, dim3(1), dim3(small ? kPlanThreadsSmall : kPlanThreads), 0, stream,
-                     seq_lens, batch, cap_tokens, num_splits, max_parts,
+                     seq_lens, batch, cap_tokens, max_parts,
                      reinterpret_cast<int32_t*>(ws + w.header), reinterpret_cast<int32_t*>(ws + w.cum),
                      reinterpret_cast<int32_t*>(ws + w.row_ptr),
                      reinterpret_cast<int32_t*>(ws + w.part_ptr),
@@ -1914,11 +1908,12 @@ hipError_t launch_sparse_rows(const int32_t* indices, int32_t topk, const int32_
 
 hipError_t launch_combine(const float* part_out, const float* part_lse,
                           const int32_t* row_ptr, uint16_t* out, float* lse, int32_t batch,
-                          int32_t num_heads, int zero_empty, hipStream_t stream) {
+                          int32_t num_heads, int zero_empty, int32_t uniform,
+                          hipStream_t stream) {
   const int tiles = head_tiles(num_heads);
   hipLaunchKernelGGL(combine_kernel, dim3(unsigned(batch) * unsigned(tiles) * kCombineChunks),
-                     dim3(256), 0, stream,
-                     part_out, part_lse, row_ptr, out, lse, batch, num_heads, tiles, zero_empty);
+                     dim3(256), 0, stream, part_out, part_lse, row_ptr, out, lse, batch,
+                     num_heads, tiles, zero_empty, uniform);
   return hipGetLastError();
 }
 
