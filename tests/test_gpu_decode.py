@@ -237,6 +237,34 @@ def test_plan_modes_agree(orc):
             compare(out, lse, ref_out, ref_lse, what="batch 64, no partial rows (snake plan)")
 
 
+def test_dirty_workspace(orc):
+    # The workspace needs no initialisation: one buffer, filled with 0xFF bytes
+    # (int32 -1, fp32 NaN) and then reused dirty, serves every mode in turn:
+    # forced splits (no plan launch), the in-kernel plan (5 requests),
+    # plan_kernel's contiguous plan (65, 300) and its snake plan (600 requests
+    # of 16 heads), for both cache types and both attention kernels.
+    gen = np.random.default_rng(63)
+    cases = []
+    for kv_dtype, heads, batches in (("bf16", 16, (5, 65, 600)), ("fp8", 32, (5, 65, 300)),
+                                     ("bf16", 40, (5, 65, 300))):
+        for batch in batches:
+            lens = gen.integers(0, 1200, size=batch).tolist()
+            lens[0] = 7000
+            wl = workloads.make_workload(batch=batch, num_heads=heads, seq=("fixed", lens),
+                                         block_size=64, seed=64 + batch, kv_dtype=kv_dtype,
+                                         poison=True)
+            cases.append(wl)
+    nbytes = max(mla.get_workspace_size(wl.batch, wl.num_heads, wl.max_blocks * wl.block_size,
+                                        s, 0) for wl in cases for s in (0, 1, 3))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda:0")
+    for wl in cases:
+        ref_out, ref_lse = run_oracle(orc, wl)
+        for s in (3, 0, 1):
+            out, lse = to_np(*run_gpu(wl, s, workspace=ws))
+            compare(out, lse, ref_out, ref_lse, wl.kv_dtype,
+                    what=f"dirty workspace {wl.kv_dtype} H={wl.num_heads} B={wl.batch} splits={s}")
+
+
 def test_forced_workspace_too_small():
     wl = workloads.make_config("tiny")
     ws = torch.empty(mla.get_workspace_size(wl.batch, wl.num_heads, 0, 1, 0), dtype=torch.uint8,
