@@ -110,6 +110,22 @@ def test_large_batch_with_long_requests(orc):
     _check(orc, wl, 0, what="large batch with long requests")
 
 
+@pytest.mark.parametrize("num_heads,kv_dtype,splits",
+                         [(16, "bf16", (0, 1)), (128, "bf16", (0, 1)), (32, "fp8", (0, 1))])
+def test_long_context(orc, num_heads, kv_dtype, splits):
+    # A 128K-token context beside a 1-token and a 64K + 1-token request:
+    # unit, tile and piece counts far beyond the benchmark lengths. With one
+    # forced split a single workgroup streams the whole 128K context.
+    lens = [131072, 1, 65537]
+    wl = workloads.make_workload(batch=len(lens), num_heads=num_heads, seq=("fixed", lens),
+                                 block_size=64, seed=47, kv_dtype=kv_dtype)
+    ref_out, ref_lse = run_oracle(orc, wl)
+    for s in splits:
+        out, lse = to_np(*run_gpu(wl, s))
+        compare(out, lse, ref_out, ref_lse, kv_dtype,
+                f"long context, {num_heads} heads, {kv_dtype}, splits={s}")
+
+
 def test_very_large_batch(orc):
     # Beyond the register-resident plan's batch limit.
     gen = np.random.default_rng(42)
