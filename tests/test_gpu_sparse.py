@@ -5,7 +5,8 @@ attend_sparse on the same seeded inputs, element by element, at the
 tolerances of dense decode. Lists cover: sorted and shuffled positions,
 repeats, entries outside [0, seq_len) (skipped), -1 padding, lists with no
 valid entry, lengths that are not multiples of the 16/32/64-token tiles,
-forced and automatic splits, both cache types and 1 to 128 heads; rising
+forced and automatic splits, both cache types and 1 to 128 heads, the
+longest list the ABI accepts; rising
 logits (second passes over gathered rows); a list of every position
 against dense decode; and sampled requests of the full-size sparse
 workloads.
@@ -106,6 +107,24 @@ def test_sparse_rising_logits(orc, kv_dtype):
     for s in (0, 1):
         out, lse = run_sparse(wl, idx, s)
         compare(out, lse, *oracle_sparse(orc, wl, idx), kv_dtype, f"sparse rising {kv_dtype} s={s}")
+
+
+@pytest.mark.parametrize("kv_dtype,num_heads", [("bf16", 16), ("fp8", 32)])
+def test_sparse_max_topk(orc, kv_dtype, num_heads):
+    # The longest list the ABI accepts, drawn from a 128K-token context,
+    # beside a short request whose list is mostly -1 padding.
+    topk = mla.MAX_TOPK
+    wl = workloads.make_workload(batch=2, num_heads=num_heads, seq=("fixed", [131072, 300]),
+                                 block_size=64, seed=76, kv_dtype=kv_dtype)
+    rng = np.random.default_rng(76)
+    idx = np.full((2, topk), -1, np.int32)
+    idx[0] = np.sort(rng.choice(131072, size=topk, replace=False))
+    idx[1, :300] = rng.permutation(300)
+    idx = torch.from_numpy(idx)
+    ref = oracle_sparse(orc, wl, idx)
+    for s in (0, 1):
+        out, lse = run_sparse(wl, idx, s)
+        compare(out, lse, *ref, kv_dtype, f"sparse max topk {kv_dtype} H={num_heads} splits={s}")
 
 
 def test_sparse_empty_lists():
