@@ -97,8 +97,20 @@ def algorithmic_flops(wl) -> int:
     return 2 * (D_K + D_V) * wl.num_heads * visible
 
 
-def cpu_baseline(wl, target_s: float) -> dict:
-    """Time the fp64 oracle on a bounded prefix of the requests."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(wl, target_s: float):
+    """Time the fp64 oracle on a bounded prefix of the requests. Returns the
+    baseline record and the oracle's (out, lse) for that prefix."""
     import numpy as np
 
     import oracle
@@ -110,9 +122,9 @@ def cpu_baseline(wl, target_s: float) -> dict:
         total = int(lens.sum())
 
         def run(n):
-            orc.attend_sparse(wl.q_bits()[:n], wl.kv_bits(), wl.block_table.numpy()[:n],
-                              wl.seq_lens.numpy()[:n], wl.block_size, wl.scale,
-                              np.ascontiguousarray(idx[:n]), **kw)
+            return orc.attend_sparse(wl.q_bits()[:n], wl.kv_bits(), wl.block_table.numpy()[:n],
+                                     wl.seq_lens.numpy()[:n], wl.block_size, wl.scale,
+                                     np.ascontiguousarray(idx[:n]), **kw)
     else:
         lens = wl.seq_lens.numpy().astype(np.int64)
         total = wl.total_tokens
@@ -120,7 +132,7 @@ def cpu_baseline(wl, target_s: float) -> dict:
                 wl.block_size, wl.scale)
 
         def run(n):
-            orc.attend(*args, req=np.arange(n, dtype=np.int32), **kw)
+            return orc.attend(*args, req=np.arange(n, dtype=np.int32), **kw)
     n_probe = min(wl.batch, 4)
     t0 = time.perf_counter()
     run(n_probe)
@@ -136,7 +148,7 @@ def cpu_baseline(wl, target_s: float) -> dict:
     spent = 0.0
     while True:
         t0 = time.perf_counter()
-        run(n_req)
+        ref = run(n_req)
         times.append(time.perf_counter() - t0)
         spent += times[-1]
         if spent + times[-1] > target_s or len(times) == 20:
@@ -147,11 +159,41 @@ def cpu_baseline(wl, target_s: float) -> dict:
     threads = int(os.environ.get("OMP_NUM_THREADS", len(os.sched_getaffinity(0))))
     what = "all" if n_req == wl.batch else f"first {n_req} of {wl.batch}"
     return {"value": round(full_s * 1e6, 1), "unit": "us/call", "cores": threads,
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": (f"{what} requests ({tok} of {total} tokens, all heads), median of "
                        f"{len(times)} runs ({dt:.2f} s each, {spent:.1f} s in all)"
                        + ("" if n_req == wl.batch else ", scaled to the whole batch")),
-            "tokens_per_s": round(tok / dt, 1)}
+            "tokens_per_s": round(tok / dt, 1)}, (n_req, ref)
+
+
+def parity_figures(wl, out, lse, n_req: int, ref) -> dict:
+    """Element-wise error of the benchmarked call's output against the oracle
+    on the first n_req requests, at the stated tolerances (bf16 cache: out
+    1e-2 + 1e-2|ref|, lse 1e-3; E4M3 cache: 2e-2 + 2e-2|ref| for both)."""
+    import numpy as np
+
+    ref_out, ref_lse = ref
+    got_out = out[:n_req].float().cpu().double().numpy()
+    got_lse = lse[:n_req].cpu().double().numpy()
+    if wl.kv_dtype == "fp8":
+        o_atol, o_rtol, l_atol, l_rtol = 2e-2, 2e-2, 2e-2, 2e-2
+    else:
+        o_atol, o_rtol, l_atol, l_rtol = 1e-2, 1e-2, 1e-3, 0.0
+    err = np.abs(got_out - ref_out)
+    ratio = err / (o_atol + o_rtol * np.abs(ref_out))
+    fin = np.isfinite(ref_lse)
+    lerr = np.where(fin, np.abs(got_lse - np.where(fin, ref_lse, 0.0)), 0.0)
+    lratio = lerr / (l_atol + l_rtol * np.abs(np.where(fin, ref_lse, 0.0)))
+    worst = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    lse_pattern_ok = bool((np.isneginf(got_lse) == ~fin).all())
+    return {"requests_compared": int(n_req), "elements_compared": int(err.size),
+            "max_abs_err_out": float(err.max()), "max_abs_err_lse": float(lerr.max()),
+            "max_err_over_bound": round(float(max(ratio.max(), lratio.max())), 4),
+            "worst_out_element": {"index": [int(i) for i in worst],
+                                  "gpu": float(got_out[worst]), "ref": float(ref_out[worst])},
+            "tolerance": {"out": [o_atol, o_rtol], "lse": [l_atol, l_rtol]},
+            "pass": bool(ratio.max() <= 1.0 and lratio.max() <= 1.0 and lse_pattern_ok
+                         and np.isfinite(got_out).all())}
 
 
 def calib_copy(torch, dev, nbytes: int, reps: int) -> int:
@@ -383,25 +425,49 @@ def main(argv=None) -> int:
     torch.cuda.synchronize()
     log(f"warmup done ({args.warmup} calls)")
 
-    # Timed region 1: K plain calls.
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    def timed_run():
+        """K plain calls back to back between one event pair: us per call."""
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(args.steps):
+            call(i)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(stop) / args.steps
+
+    # Timed region: K plain calls (the headline value).
     t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        call(i)
-    stop.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed_run()
     wall = time.perf_counter() - t0
-    ms_per_step = start.elapsed_time(stop) / args.steps
     log(f"timed {args.steps} calls: {ms_per_step * 1e3:.1f} us/call (wall {wall * 1e3 / args.steps:.1f})")
 
-    # Timed region 2: K calls with HIP events around each kernel (same stream).
+    def hold(n_calls):
+        # A bounded spin kernel holds the stream while the host queues the
+        # calls, so that they run back to back on the GPU (no idle gaps in
+        # which the clock could recover between calls).
+        torch.cuda._sleep(int(200_000 * n_calls))
+
+    # Per-call spread: an event pair around each call, calls back to back.
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    hold(args.steps)
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        call(i)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    call_us = sorted(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+
+    # Kernel durations: HIP events around each kernel (same stream), the
+    # calls again queued back to back.
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for row in evs:
         for e in row:
             e.record(stream)  # create the underlying HIP events
     torch.cuda.synchronize()
+    hold(args.steps)
     for i in range(args.steps):
         call(i, events=evs[i])
     torch.cuda.synchronize()
@@ -413,10 +479,14 @@ def main(argv=None) -> int:
     log(f"attention kernel {attn_avg * 1e3:.1f} us avg, plan {statistics.fmean(plan_ms) * 1e3:.1f},"
         f" combine {statistics.fmean(comb_ms) * 1e3:.1f}")
 
+    # Second timed run of the same K plain calls, after the other regions.
+    ms_second = timed_run()
+    log(f"second timed run: {ms_second * 1e3:.1f} us/call")
+
     graph_us = None
     if args.graph:
-        # Timed region 3 (optional): one HIP graph holding `copies` calls
-        # (one per cache copy), replayed back to back.
+        # Optional: one HIP graph holding `copies` calls (one per cache copy),
+        # replayed back to back.
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
             for i in range(copies):
@@ -433,6 +503,9 @@ def main(argv=None) -> int:
         torch.cuda.synchronize()
         graph_us = round(g0.elapsed_time(g1) * 1e3 / (reps * copies), 2)
         log(f"graph replays: {graph_us} us/call")
+
+    def pct(v, f):
+        return round(v[min(len(v) - 1, int(f * len(v)))], 2)
 
     alg_bytes = algorithmic_bytes(wl)
     alg_flops = algorithmic_flops(wl)
@@ -451,6 +524,7 @@ def main(argv=None) -> int:
     t_hbm = alg_bytes / (PEAK_HBM_GBPS * 1e9)
     t_mfma = alg_flops / (mfma_peak * 1e12)
     achieved_tflops = alg_flops / (attn_avg * 1e-3) / 1e12
+    t_floor = max(t_hbm, t_mfma)
     if t_mfma > t_hbm:
         roofline = {"bound": "mfma", "achieved": round(achieved_tflops, 1), "peak": mfma_peak,
                     "unit": "TFLOP/s", "frac": round(achieved_tflops / mfma_peak, 4)}
@@ -459,12 +533,16 @@ def main(argv=None) -> int:
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
     roofline.update({
         "traffic": traffic, "kernel": kernel_name,
+        "kernel_us_avg": round(attn_avg * 1e3, 2),
+        "timing": "attention kernel between HIP events, calls queued back to back",
         "hbm_time_us_at_peak": round(t_hbm * 1e6, 2),
         "mfma_time_us_at_peak": round(t_mfma * 1e6, 2),
         "algorithmic_bytes_per_launch": alg_bytes,
         "algorithmic_flops_per_launch": alg_flops,
         "hbm_frac": round(achieved / PEAK_HBM_GBPS, 4),
-        "mfma_frac": round(achieved_tflops / mfma_peak, 4)})
+        "mfma_frac": round(achieved_tflops / mfma_peak, 4),
+        # The whole call (plan, attention and combine) against the same floor.
+        "call_frac": round(t_floor / (ms_per_step * 1e-3), 4)})
     result = {
         "metric": "MLA decode us/call + achieved HBM GB/s & MFMA % at bs=512, 16 heads",
         "value": round(ms_per_step * 1e3, 2),
@@ -484,25 +562,35 @@ def main(argv=None) -> int:
                    "seq_lens": list(cfg["seq"]) if cfg["seq"][0] != "fixed" else
                    sorted(set(cfg["seq"][1])), "total_tokens": wl.total_tokens,
                    "block_size": wl.block_size, "kv_dtype": wl.kv_dtype,
-                   "num_splits": args.num_splits or "auto", "parallelism": "single-gpu"},
+                   "num_splits": args.num_splits or "auto", "parallelism": "single-gpu",
+                   "kv_pool_copies": copies},
         "tokens_per_s": round((wl.total_tokens if wl.indices is None else listed_tokens(wl))
                               / (ms_per_step * 1e-3), 1),
         "hbm_GBps_algorithmic": round(alg_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "mfma_pct": round(100 * alg_flops / (ms_per_step * 1e-3) / 1e12 / mfma_peak, 2),
+        "call_us": {"first_run": round(ms_per_step * 1e3, 2),
+                    "second_run": round(ms_second * 1e3, 2),
+                    "median_with_events": pct(call_us, 0.5),
+                    "p10_p90_with_events": [pct(call_us, 0.1), pct(call_us, 0.9)]},
         "kernels_us": {"plan": round(statistics.fmean(plan_ms) * 1e3, 2),
                        "attention": round(attn_avg * 1e3, 2),
                        "combine": round(statistics.fmean(comb_ms) * 1e3, 2),
                        "call_with_events": round(statistics.fmean(tot_ms) * 1e3, 2),
-                       "attention_p10_p90": [round(sorted(attn_ms)[len(attn_ms) // 10] * 1e3, 2),
-                                             round(sorted(attn_ms)[(9 * len(attn_ms)) // 10] * 1e3, 2)]},
+                       "attention_median": pct(sorted(x * 1e3 for x in attn_ms), 0.5),
+                       "attention_p10_p90": [pct(sorted(x * 1e3 for x in attn_ms), 0.1),
+                                             pct(sorted(x * 1e3 for x in attn_ms), 0.9)]},
         "roofline": roofline,
         "cpu_baseline": None,
+        "parity": None,
     }
     if graph_us is not None:
         result["graph_us_per_call"] = graph_us
     if not args.no_cpu_baseline:
         log("timing the fp64 oracle on a sample")
-        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
+        base, (n_req, ref) = cpu_baseline(wl, args.cpu_seconds)
+        result["cpu_baseline"] = base
+        result["parity"] = parity_figures(wl, out, lse, n_req, ref)
+        log(f"parity on {n_req} requests: max err/bound {result['parity']['max_err_over_bound']}")
     print(json.dumps(result), flush=True)
     return 0
 

@@ -26,9 +26,12 @@
  *
  * Conventions shared by every entry point:
  *  - All data pointers are caller-owned DEVICE memory on the current HIP
- *    device. The library never allocates, frees, or retains pointers, and
- *    keeps no mutable global state (PR #20769 review: a module-global
- *    workspace is not thread-safe; the workspace is per caller).
+ *    device. The library never allocates, frees, or retains pointers. Every
+ *    call's plan, partial rows and counters live in the caller's workspace
+ *    (PR #20769 review: a module-global workspace is not thread-safe; the
+ *    workspace is per caller). The only global state is a mutex-guarded
+ *    cache of immutable device properties (architecture, CU count), filled
+ *    on a device's first call.
  *  - Every call enqueues on `stream` (a hipStream_t; NULL = the null stream)
  *    and returns without synchronising. A returned MLA_OK covers argument
  *    validation and launch only.

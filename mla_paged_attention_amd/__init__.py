@@ -37,5 +37,6 @@ from ._binding import (  # noqa: F401
     library,
     quant_fp8_groups,
     status_string,
+    release_workspaces,
     workspace_for,
 )

@@ -144,16 +144,43 @@ def _stream_handle(stream) -> ctypes.c_void_p:
 _workspaces: dict = {}
 
 
+def _launch_stream(device: torch.device, stream):
+    return stream if stream is not None else torch.cuda.current_stream(device)
+
+
 def workspace_for(device: torch.device, stream, nbytes: int) -> torch.Tensor:
-    """Per (device, stream) uninitialised workspace, grown on demand. Calls on
-    one stream are ordered, so reusing the buffer between them is safe."""
-    key = (device.index, stream.cuda_stream if stream is not None else
-           torch.cuda.current_stream(device).cuda_stream)
+    """Per (device, stream) uninitialised workspace, grown on demand.
+
+    Calls on one stream are ordered, so reusing the buffer between them is
+    safe. The buffer is allocated on the launch stream itself, so when a
+    larger call replaces it, torch's allocator hands the old block out again
+    only to later work on that same stream. A graph capture must bring its
+    own workspace: a replayed graph keeps using the buffer it captured, which
+    this cache may free or replace in the meantime."""
+    if torch.cuda.is_current_stream_capturing():
+        raise RuntimeError("pass workspace= when capturing a graph: the binding's cached "
+                           "workspace may be replaced while the graph still uses it")
+    s = _launch_stream(device, stream)
+    key = (device.index, s.cuda_stream)
     buf = _workspaces.get(key)
     if buf is None or buf.numel() < nbytes:
-        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        with torch.cuda.stream(s):
+            buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _workspaces[key] = buf
     return buf
+
+
+def release_workspaces() -> None:
+    """Drop the cached per-stream workspaces (their memory returns to torch's
+    allocator once the work queued on their streams has run)."""
+    _workspaces.clear()
+
+
+def _empty_on(stream, shape, dtype, device):
+    """An output buffer allocated on the launch stream (so that torch's
+    allocator orders its reuse after the kernels that write it)."""
+    with torch.cuda.stream(_launch_stream(device, stream)):
+        return torch.empty(shape, dtype=dtype, device=device)
 
 
 def _kv_dtype(kv: torch.Tensor) -> int:
@@ -198,12 +225,12 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
             raise ValueError(f"{name} must be contiguous on {dev}")
     lead = tuple(q.shape[:-1])                     # (B, H) or (B, q_len, H)
     if out is None:
-        out = torch.empty(lead + (HEAD_DIM_V,), dtype=torch.bfloat16, device=dev)
+        out = _empty_on(stream, lead + (HEAD_DIM_V,), torch.bfloat16, dev)
     elif tuple(out.shape) != lead + (HEAD_DIM_V,) or out.dtype != torch.bfloat16 or \
             out.device != dev or not out.is_contiguous():
         raise ValueError(f"out must be contiguous {lead + (HEAD_DIM_V,)} bf16 on {dev}")
     if lse is True:
-        lse = torch.empty(lead, dtype=torch.float32, device=dev)
+        lse = _empty_on(stream, lead, torch.float32, dev)
     elif lse is False:
         lse = None
     elif lse is not None and (tuple(lse.shape) != lead or lse.dtype != torch.float32 or
@@ -263,12 +290,12 @@ def decode_sparse(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Te
         if t.device != dev or not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous on {dev}")
     if out is None:
-        out = torch.empty((batch, num_heads, HEAD_DIM_V), dtype=torch.bfloat16, device=dev)
+        out = _empty_on(stream, (batch, num_heads, HEAD_DIM_V), torch.bfloat16, dev)
     elif tuple(out.shape) != (batch, num_heads, HEAD_DIM_V) or out.dtype != torch.bfloat16 or \
             out.device != dev or not out.is_contiguous():
         raise ValueError(f"out must be contiguous [{batch}, {num_heads}, 512] bf16 on {dev}")
     if lse is True:
-        lse = torch.empty((batch, num_heads), dtype=torch.float32, device=dev)
+        lse = _empty_on(stream, (batch, num_heads), torch.float32, dev)
     elif lse is False:
         lse = None
     elif lse is not None and (tuple(lse.shape) != (batch, num_heads) or

@@ -309,6 +309,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        if (k[i] == 0) continue;  // slot past the batch
         const int q = units[i] / k[i], r = units[i] - q * k[i];
         for (int j = 0; j < k[i]; ++j) {
           const int len = q + (j < r ? 1 : 0);
@@ -1311,7 +1312,11 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
               }
           amax = fmaxf(amax, __shfl_xor(amax, 16));
           amax = fmaxf(amax, __shfl_xor(amax, 32));
-          const float inv = amax > 0.f ? 448.f / amax : 0.f;
+          // The floor keeps 448 / amax finite for rows of tiny magnitude (bf16
+          // reaches 1e-38, where 448 / amax would overflow fp32); such rows'
+          // logits are far below any resolution of the softmax anyway.
+          amax = fmaxf(amax, 0x1p-100f);
+          const float inv = 448.f / amax;
           xscale = (amax / 448.f) * a.kv_scale * a.scale_log2;
 #pragma unroll
           for (int m = 0; m < kKChunksFp8; ++m) {

@@ -86,12 +86,20 @@ double oracle_e4m3_to_double(uint8_t code) {
 
 double oracle_bf16_to_double(uint16_t bits) { return bf16_bits_to_double(bits); }
 
+/* The value of every E4M3 code, from oracle_e4m3_to_double (filled before any
+ * parallel region; a lookup gives exactly the decoded value, only faster). */
+static double e4m3[256];
+
+static void fill_e4m3_table(void) {
+  for (int c = 0; c < 256; ++c) e4m3[c] = oracle_e4m3_to_double((uint8_t)c);
+}
+
 /* Key/value row of one cached token, widened to fp64. */
 static void load_token(const void* kv_cache, int kv_fp8, double kv_scale, int64_t row,
                        double* k) {
   if (kv_fp8) {
     const uint8_t* p = (const uint8_t*)kv_cache + row * ORACLE_D;
-    for (int d = 0; d < ORACLE_D; ++d) k[d] = oracle_e4m3_to_double(p[d]) * kv_scale;
+    for (int d = 0; d < ORACLE_D; ++d) k[d] = e4m3[p[d]] * kv_scale;
   } else {
     const uint16_t* p = (const uint16_t*)kv_cache + row * ORACLE_D;
     for (int d = 0; d < ORACLE_D; ++d) k[d] = bf16_bits_to_double(p[d]);
@@ -149,6 +157,7 @@ int oracle_mla_attend(const uint16_t* q, const void* kv_cache, int kv_fp8, float
   const double s = (double)scale;
   const double kvs = (double)kv_scale;
   int64_t n_work = n_items * q_len * num_heads;
+  fill_e4m3_table();
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t w = 0; w < n_work; ++w) {
@@ -239,6 +248,7 @@ int oracle_mla_attend_sparse(const uint16_t* q, const void* kv_cache, int kv_fp8
   }
   const double s = (double)scale;
   const double kvs = (double)kv_scale;
+  fill_e4m3_table();
 
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t w = 0; w < batch * num_heads; ++w) {
@@ -351,13 +361,14 @@ int oracle_gemm_fp8_blockscale(const uint8_t* a, const float* a_scale, const uin
   if (!a || !a_scale || !b || !b_scale || !c || m < 0 || n < 0 || k < 0 || k % 128)
     return ORACLE_BAD_ARG;
   const int64_t kg = k / 128;
+  fill_e4m3_table();
 #pragma omp parallel for schedule(dynamic, 1)
   for (int64_t i = 0; i < m; ++i) {
     for (int64_t j = 0; j < n; ++j) {
       double sum = 0.0;
       for (int64_t t = 0; t < k; ++t) {
-        double x = oracle_e4m3_to_double(a[i * k + t]) * (double)a_scale[i * kg + t / 128];
-        double w = oracle_e4m3_to_double(b[j * k + t]) * (double)b_scale[(j / 128) * kg + t / 128];
+        double x = e4m3[a[i * k + t]] * (double)a_scale[i * kg + t / 128];
+        double w = e4m3[b[j * k + t]] * (double)b_scale[(j / 128) * kg + t / 128];
         sum += x * w;
       }
       c[i * n + j] = sum;

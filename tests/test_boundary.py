@@ -375,3 +375,15 @@ def test_binding_rejects_bad_tensors():
     with pytest.raises(ValueError):
         mla.decode(torch.zeros((2, 16, 576), dtype=torch.bfloat16), kv, bt.long(), sl,
                    scale=0.1)
+
+
+def test_cached_workspace_refused_under_graph_capture(monkeypatch):
+    # A graph keeps using the buffer it captured, so the binding's cached
+    # workspace is refused while a capture is under way (checked before any
+    # allocation or HIP call).
+    import torch
+
+    import mla_paged_attention_amd as mla
+    monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
+    with pytest.raises(RuntimeError, match="capturing"):
+        mla.workspace_for(torch.device("cuda", 0), None, 1024)

@@ -65,3 +65,30 @@ def test_two_term_q_and_p_fit_the_bound():
     # One E4M3 term for P is not enough on short rows, nor one for q on long ones.
     assert worst_ratio(short, True, False) > 1.0
     assert worst_ratio(long_rows, False, True) > 1.0
+
+
+def test_tiny_q_rows_need_a_scale_floor():
+    # A bf16 q row can be as small as 1e-38. Its E4M3 scale 448 / amax then
+    # overflows fp32 (codes inf or NaN), so the kernel floors amax at 2^-100:
+    # codes stay finite and such a row's logits (about 1e-37) still give the
+    # uniform softmax the oracle computes.
+    wl = workloads.make_workload(batch=2, num_heads=16, seq=("fixed", [40, 300]), block_size=64,
+                                 seed=62, kv_dtype="fp8")
+    q = wl.q.to(torch.float32) * 1e-37
+    amax = q.abs().amax(-1, keepdim=True)
+    assert not torch.isfinite(torch.tensor(448.0, dtype=torch.float32) / amax).all()
+    floored = amax.clamp(min=2.0 ** -100)
+    inv = torch.tensor(448.0, dtype=torch.float32) / floored
+    codes = (q * inv).clamp(-448, 448).to(torch.float8_e4m3fn).to(torch.float64)
+    assert torch.isfinite(codes).all() and codes.abs().max() <= 448
+    deq = wl.kv.view(torch.float8_e4m3fn).to(torch.float64) * wl.kv_scale
+    for b in range(wl.batch):
+        n = int(wl.seq_lens[b])
+        rows = torch.stack([deq[int(wl.block_table[b, t // wl.block_size]), t % wl.block_size]
+                            for t in range(n)])
+        x_ref = wl.scale * q[b].to(torch.float64) @ rows.T
+        x_emu = wl.scale * (codes[b] * (floored[b].to(torch.float64) / 448)) @ rows.T
+        assert float((x_ref - x_emu).abs().max()) < 1e-30
+        ref = torch.softmax(x_ref, 1) @ rows[:, :512]
+        emu = torch.softmax(x_emu, 1) @ rows[:, :512]
+        assert float(((emu - ref).abs() / (BOUND_ATOL + BOUND_RTOL * ref.abs())).max()) < 0.01

@@ -53,11 +53,9 @@ def test_gemm_matches_oracle(orc, m, n, k):
 
 
 @pytest.mark.parametrize("m", [64, 256])
-def test_gemm_full_shape_sampled_rows(orc, m):
-    # DeepSeek-R1's fused q/kv down-projection at decode batch m; rows sampled.
-    rng = np.random.default_rng(m)
-    rows = np.unique(np.concatenate([rng.choice(m, 6, replace=False), [0, m - 1]]))
-    check_gemm(orc, m, 2112, 7168, seed=900 + m, rows=rows)
+def test_gemm_full_shape(orc, m):
+    # DeepSeek-R1's fused q/kv down-projection at decode batch m; every row.
+    check_gemm(orc, m, 2112, 7168, seed=900 + m)
 
 
 @pytest.mark.parametrize("m,k", [(1, 128), (5, 7168), (64, 1024), (300, 256)])

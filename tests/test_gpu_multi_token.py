@@ -7,7 +7,7 @@ several, rows of different query tokens inside one tile (heads not a
 multiple of 16), requests shorter than q_len (query tokens that see
 nothing), lengths around the 16/32/64-token boundaries, forced and
 automatic splits, both cache types, rising logits (second passes with
-partly masked rows), and sampled requests of a full-size batch.
+partly masked rows), and every request of a full-size batch.
 """
 import numpy as np
 import pytest
@@ -103,16 +103,11 @@ def test_query_tokens_equal_cut_one_token_decodes():
 
 
 @pytest.mark.parametrize("q_len", [2, 4])
-def test_r1tp8_multi_token_sampled(orc, q_len):
+def test_r1tp8_multi_token_full(orc, q_len):
     # The full 512-request batch at 16 heads, q_len query tokens per request,
-    # in the automatic plan the benchmark times; a sample of requests against
-    # the oracle and every output finite.
+    # in the automatic plan the benchmark times; every request against the
+    # oracle.
     wl = workloads.make_config("r1tp8", q_len=q_len)
     out, lse = to_np(*run_gpu(wl, 0))
-    assert np.isfinite(out).all() and np.isfinite(lse).all()
-    rng = np.random.default_rng(q_len)
-    req = np.unique(np.concatenate([rng.choice(wl.batch, 10, replace=False),
-                                    [0, wl.batch - 1, int(np.argmax(wl.seq_lens.numpy()))]]))
-    req = req.astype(np.int32)
-    ref_out, ref_lse = run_oracle(orc, wl, req)
-    compare(out[req], lse[req], ref_out, ref_lse, "bf16", f"r1tp8 q_len={q_len} (sampled)")
+    ref_out, ref_lse = run_oracle(orc, wl)
+    compare(out, lse, ref_out, ref_lse, "bf16", f"r1tp8 q_len={q_len} (whole batch)")

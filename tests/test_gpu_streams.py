@@ -42,3 +42,27 @@ def test_concurrent_streams_with_own_workspaces():
         torch.cuda.synchronize()
         assert torch.equal(out_a, ref_a[0]) and torch.equal(lse_a, ref_a[1]), f"stream a, rep {rep}"
         assert torch.equal(out_b, ref_b[0]) and torch.equal(lse_b, ref_b[1]), f"stream b, rep {rep}"
+
+
+def test_cached_workspace_on_a_side_stream_grows(orc):
+    # No workspace passed: the binding's cached buffer for the side stream is
+    # replaced by a larger one at each call, and the outputs are allocated on
+    # that stream too. Every result must still match the oracle after the
+    # stream has drained (nothing freed and reused while a kernel used it).
+    from gpu_helpers import compare, run_oracle, to_np
+
+    mla.release_workspaces()
+    side = torch.cuda.Stream()  # default priority
+    runs = []
+    for i, (batch, hi) in enumerate(((2, 300), (9, 4000), (40, 20000), (300, 3000))):
+        wl = workloads.make_workload(batch=batch, num_heads=16, seq=("uniform", 1, hi),
+                                     block_size=32, seed=90 + i)
+        dev = to_device(wl)
+        side.wait_stream(torch.cuda.current_stream())
+        out, lse = mla.decode(*dev, scale=wl.scale, stream=side)
+        runs.append((wl, dev, out, lse))
+    torch.cuda.synchronize()
+    for wl, _, out, lse in runs:
+        o, l = to_np(out, lse)
+        compare(o, l, *run_oracle(orc, wl), what=f"side stream, batch {wl.batch}")
+    mla.release_workspaces()

@@ -44,8 +44,7 @@ MUTANTS = [
     ("sparse_q_row", "qv[d] = bf16_bits_to_double(q[(b * num_heads + h) * ORACLE_D + d]);",
      "qv[d] = bf16_bits_to_double(q[((h % batch) * num_heads + (b % num_heads)) * ORACLE_D + d]);"),
     ("sparse_scale_dropped", "x[j] = s * dot;", "x[j] = dot;"),
-    ("gemm_neighbour_element", "oracle_e4m3_to_double(a[i * k + t])",
-     "oracle_e4m3_to_double(a[i * k + (t ^ 1)])"),
+    ("gemm_neighbour_element", "e4m3[a[i * k + t]]", "e4m3[a[i * k + (t ^ 1)]]"),
     ("gemm_weight_scale_group0", "(double)b_scale[(j / 128) * kg + t / 128]",
      "(double)b_scale[(j / 128) * kg]"),
     ("gemm_act_scale_group0", "(double)a_scale[i * kg + t / 128]", "(double)a_scale[i * kg]"),
@@ -56,7 +55,7 @@ MUTANTS = [
      "int64_t row_out = (i * num_heads + h) * q_len + qi;"),
     ("e4m3_bias", "exponent - 7);", "exponent - 8);"),
     ("e4m3_subnormal", "ldexp((double)mantissa / 8.0, -6)", "ldexp((double)mantissa / 8.0, -7)"),
-    ("kv_scale_dropped", "oracle_e4m3_to_double(p[d]) * kv_scale;", "oracle_e4m3_to_double(p[d]);"),
+    ("kv_scale_dropped", "k[d] = e4m3[p[d]] * kv_scale;", "k[d] = e4m3[p[d]];"),
     ("merge_weight_sign", "double w = exp(ls - M);", "double w = exp(M - ls);"),
     ("merge_unnormalised", "for (int d = 0; d < ORACLE_DV; ++d) o[d] /= wsum;", ""),
     ("tail_overread", "if (t1 > visible) t1 = visible;\n    int64_t row_out",
