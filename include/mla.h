@@ -63,6 +63,8 @@ extern "C" {
 #define MLA_GEMM_MAX_M 65536   /* tokens per mla_gemm_fp8_blockscale call */
 #define MLA_GEMM_MAX_N 65536
 #define MLA_GEMM_MAX_K 65536
+/* Bytes of the device scratch array behind mla_decode_noalloc (one per GPU). */
+#define MLA_NOALLOC_SCRATCH_BYTES (96ull << 20)
 
 typedef enum {
   MLA_OK = 0,
@@ -192,6 +194,37 @@ mla_status_t mla_decode_multi_token(const void* q, const void* kv_cache,
                                     int32_t batch, int32_t max_blocks_per_seq,
                                     int32_t num_blocks, int32_t kv_dtype, float kv_scale,
                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * mla_decode_noalloc: mla_decode_multi_token for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). It takes no workspace: the plan, partial rows and
+ * counters live in a static device array of MLA_NOALLOC_SCRATCH_BYTES
+ * (96 MiB) that every GPU the library runs on holds until the process ends;
+ * the call itself allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine). The caller still passes inputs and outputs, with the
+ * layouts, limits and error behaviour of mla_decode_multi_token.
+ *
+ *  - A call whose workspace need, mla_get_workspace_size_multi_token(batch,
+ *    num_heads, q_len, max_blocks_per_seq * block_size, num_splits, <CUs>),
+ *    exceeds the array is rejected with MLA_ERR_WORKSPACE_TOO_SMALL before
+ *    anything is enqueued. Automatic mode fits any head count and query
+ *    length at batches up to tens of thousands of requests; forced splits
+ *    need batch * num_splits * num_heads * q_len * 2052 bytes and more.
+ *  - Nothing in the array needs to start at zero: each call writes what it
+ *    reads, and the array keeps the last call's contents.
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (concurrent streams, or several host threads) race and may corrupt
+ *    each other's results. Serialise them, e.g. on one stream.
+ *  - The array's device address is looked up once per device, on that
+ *    device's first call (hipGetSymbolAddress), with the device current.
+ */
+mla_status_t mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, void* out, float* lse, float scale,
+                                int32_t num_heads, int32_t q_len, int32_t block_size,
+                                int32_t num_splits, int32_t batch, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, int32_t kv_dtype, float kv_scale,
+                                void* stream);
 
 /*
  * mla_decode_profiled: exactly mla_decode_multi_token, and additionally

@@ -24,12 +24,14 @@ from ._binding import (  # noqa: F401
     MLA_KV_BF16,
     MLA_KV_FP8_E4M3,
     MLA_OK,
+    NOALLOC_SCRATCH_BYTES,
     MLAError,
     abi_version,
     absorb_out,
     absorb_q,
     combine,
     decode,
+    decode_noalloc,
     decode_sparse,
     gemm_fp8_blockscale,
     get_workspace_size,

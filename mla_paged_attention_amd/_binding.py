@@ -41,8 +41,9 @@ EXPORTED_SYMBOLS = ("mla_get_workspace_size", "mla_get_workspace_size_multi_toke
                     "mla_get_workspace_size_sparse", "mla_decode", "mla_decode_multi_token",
                     "mla_decode_profiled", "mla_decode_sparse", "mla_decode_sparse_profiled",
                     "mla_combine", "mla_quant_fp8_groups", "mla_gemm_fp8_blockscale",
-                    "mla_absorb_q", "mla_absorb_out",
+                    "mla_absorb_q", "mla_absorb_out", "mla_decode_noalloc",
                     "mla_status_string", "mla_abi_version")
+NOALLOC_SCRATCH_BYTES = 96 << 20
 
 _lib = None
 _lock = threading.Lock()
@@ -70,6 +71,8 @@ def _bind(lib: ctypes.CDLL) -> None:
     lib.mla_decode_multi_token.restype = i32
     lib.mla_decode_profiled.argtypes = multi_args + [ctypes.POINTER(vp)]
     lib.mla_decode_profiled.restype = i32
+    lib.mla_decode_noalloc.argtypes = multi_args[:16] + [vp]  # no workspace arguments
+    lib.mla_decode_noalloc.restype = i32
     sparse_args = decode_args[:4] + [vp, i32] + decode_args[4:]  # indices, topk after seq_lens
     lib.mla_decode_sparse.argtypes = sparse_args
     lib.mla_decode_sparse.restype = i32
@@ -258,6 +261,47 @@ def decode(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
         what = "mla_decode_multi_token"
     if st != MLA_OK:
         raise MLAError(st, what)
+    return out, lse
+
+
+def decode_noalloc(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                   seq_lens: torch.Tensor, *, scale: float, out: torch.Tensor,
+                   lse: torch.Tensor | None, num_splits: int = 0, kv_scale: float = 1.0,
+                   stream=None):
+    """decode() through mla_decode_noalloc: no workspace, and the library
+    allocates nothing (see include/mla.h). The caller passes out (and lse, or
+    None); calls that overlap on one GPU race on its scratch array."""
+    if q.dim() not in (3, 4) or q.shape[-1] != HEAD_DIM_K or q.dtype != torch.bfloat16:
+        raise ValueError("q must be [batch, num_heads, 576] or [batch, q_len, num_heads, 576] "
+                         "bf16")
+    if kv_cache.dim() != 3 or kv_cache.shape[2] != HEAD_DIM_K:
+        raise ValueError("kv_cache must be [num_blocks, block_size, 576]")
+    kv_dtype = _kv_dtype(kv_cache)
+    batch, num_heads = q.shape[0], q.shape[-2]
+    q_len = q.shape[1] if q.dim() == 4 else 1
+    num_blocks, block_size, _ = kv_cache.shape
+    if block_table.dim() != 2 or block_table.shape[0] != batch or block_table.dtype != torch.int32:
+        raise ValueError("block_table must be [batch, max_blocks] int32")
+    if seq_lens.shape != (batch,) or seq_lens.dtype != torch.int32:
+        raise ValueError("seq_lens must be [batch] int32")
+    lead = tuple(q.shape[:-1])
+    dev = q.device
+    for name, t in (("q", q), ("kv_cache", kv_cache), ("block_table", block_table),
+                    ("seq_lens", seq_lens)):
+        if t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous on {dev}")
+    if tuple(out.shape) != lead + (HEAD_DIM_V,) or out.dtype != torch.bfloat16 or \
+            out.device != dev or not out.is_contiguous():
+        raise ValueError(f"out must be contiguous {lead + (HEAD_DIM_V,)} bf16 on {dev}")
+    if lse is not None and (tuple(lse.shape) != lead or lse.dtype != torch.float32 or
+                            lse.device != dev or not lse.is_contiguous()):
+        raise ValueError(f"lse must be contiguous {lead} fp32 on {dev}")
+    st = library().mla_decode_noalloc(
+        _ptr(q), _ptr(kv_cache), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+        float(scale), num_heads, q_len, block_size, num_splits, batch, block_table.shape[1],
+        num_blocks, kv_dtype, float(kv_scale), _stream_handle(stream))
+    if st != MLA_OK:
+        raise MLAError(st, "mla_decode_noalloc")
     return out, lse
 
 

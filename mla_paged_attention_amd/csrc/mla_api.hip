@@ -56,9 +56,10 @@ struct DeviceInfo {
 std::mutex g_dev_mutex;
 DeviceInfo g_dev[kMaxDevices];  // immutable device properties, filled once per device
 
-mla_status_t query_device(DeviceInfo* info) {
+mla_status_t query_device(DeviceInfo* info, int* dev_index = nullptr) {
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MLA_ERR_NO_DEVICE;
+  if (dev_index) *dev_index = dev;
   if (dev >= kMaxDevices) return MLA_ERR_UNSUPPORTED;
   std::lock_guard<std::mutex> lock(g_dev_mutex);
   if (!g_dev[dev].valid) {
@@ -71,6 +72,35 @@ mla_status_t query_device(DeviceInfo* info) {
     g_dev[dev] = d;
   }
   *info = g_dev[dev];
+  return MLA_OK;
+}
+
+// Workspace bytes of a dense decode call (one or several query tokens).
+size_t dense_workspace_need(int64_t batch, int64_t rows, int64_t max_seq_len,
+                            int64_t num_splits, int64_t num_cus);
+
+}  // namespace
+
+// Device scratch of mla_decode_noalloc: the workspace of calls that cannot
+// allocate. Every GPU the library runs on holds its own copy of this array
+// (set up by the code object's loader) until the process ends. In host code
+// the name is only a stand-in: its device address comes from
+// hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[MLA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+void* g_scratch[kMaxDevices];  // device address of `scratch` per device (g_dev_mutex)
+
+// Address of `scratch` on device `dev`, which must be the current device.
+mla_status_t scratch_address(int dev, void** ptr) {
+  std::lock_guard<std::mutex> lock(g_dev_mutex);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ptr = g_scratch[dev];
   return MLA_OK;
 }
 
@@ -89,6 +119,7 @@ struct DecodeArgs {
   hipStream_t stream;
   const int32_t* indices = nullptr;  // sparse decode: [batch][topk] token positions
   int32_t topk = 0;                  // > 0: sparse decode
+  bool scratch = false;              // workspace = the library's device scratch array
 
   int32_t rows() const { return num_heads * q_len; }  // query rows per request
 };
@@ -126,13 +157,26 @@ mla_status_t validate_decode(const DecodeArgs& a) {
     const int64_t max_cost = mla::kOverheadUnits + (cap_tokens + mla::kUnit - 1) / mla::kUnit;
     if (int64_t(a.batch) * max_cost > INT32_MAX / 2) return MLA_ERR_INVALID_ARG;
   }
-  if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out || !a.workspace)
+  if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out)
     return MLA_ERR_INVALID_ARG;
+  if (!a.scratch && !a.workspace) return MLA_ERR_INVALID_ARG;
   if (a.topk > 0 && (!a.indices || !aligned(a.indices, 4))) return MLA_ERR_INVALID_ARG;
   if (!aligned(a.q, 16) || !aligned(a.kv_cache, 16) || !aligned(a.out, 16) ||
-      !aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) || !aligned(a.workspace, 256))
+      !aligned(a.block_table, 4) || !aligned(a.seq_lens, 4) ||
+      (!a.scratch && !aligned(a.workspace, 256)))
     return MLA_ERR_INVALID_ARG;
   if (a.lse && !aligned(a.lse, 4)) return MLA_ERR_INVALID_ARG;
+  // The scratch array's size is checked against the whole need once the
+  // device (its CU count) is known.
+  if (a.scratch) {
+    if (a.num_splits > 0) {
+      const int64_t tiles = mla::head_tiles(a.rows());
+      if (int64_t(a.batch) * a.num_splits * tiles > INT32_MAX ||
+          int64_t(a.batch) * tiles * (MLA_HEAD_DIM_V / 64) > INT32_MAX)
+        return MLA_ERR_INVALID_ARG;
+    }
+    return MLA_OK;
+  }
   // Metadata alone must fit whatever the mode.
   if (a.workspace_bytes < mla::workspace_layout(a.batch, a.rows(), 0, 1, a.topk).total)
     return MLA_ERR_WORKSPACE_TOO_SMALL;
@@ -150,15 +194,29 @@ mla_status_t validate_decode(const DecodeArgs& a) {
   return MLA_OK;
 }
 
-mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
-  mla_status_t st = validate_decode(a);
+mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
+  mla_status_t st = validate_decode(call);
   if (st != MLA_OK) return st;
   if (events && (!events[0] || !events[1] || !events[2] || !events[3]))
     return MLA_ERR_INVALID_ARG;
   DeviceInfo dev;
-  st = query_device(&dev);
+  int dev_index = -1;
+  st = query_device(&dev, &dev_index);
   if (st != MLA_OK) return st;
   if (!dev.gfx950) return MLA_ERR_UNSUPPORTED;
+  DecodeArgs a = call;
+  if (a.scratch) {
+    // The whole workspace this call needs must fit the fixed array; nothing
+    // is shrunk to fit, so the call computes exactly what mla_decode would
+    // with a workspace of mla_get_workspace_size bytes.
+    const size_t need = dense_workspace_need(a.batch, a.rows(),
+                                             int64_t(a.max_blocks) * a.block_size, a.num_splits,
+                                             dev.cus);
+    if (need == 0 || need > MLA_NOALLOC_SCRATCH_BYTES) return MLA_ERR_WORKSPACE_TOO_SMALL;
+    st = scratch_address(dev_index, &a.workspace);
+    if (st != MLA_OK) return st;
+    a.workspace_bytes = MLA_NOALLOC_SCRATCH_BYTES;
+  }
   if (a.batch == 0) return MLA_OK;
 
   // Tokens per request the kernels walk: the cache (dense) or the list (sparse).
@@ -280,6 +338,15 @@ mla_status_t run_decode(const DecodeArgs& a, void* const* events) {
   return MLA_OK;
 }
 
+size_t dense_workspace_need(int64_t batch, int64_t rows, int64_t max_seq_len,
+                            int64_t num_splits, int64_t num_cus) {
+  if (num_cus <= 0) num_cus = kDefaultCus;
+  if (num_splits > 0)
+    return mla::workspace_layout(batch, rows, forced_rows(batch, num_splits), 1).total;
+  const int64_t parts = mla::max_partitions(num_cus, rows, 0);
+  return mla::workspace_layout(batch, rows, auto_rows(batch, parts, max_seq_len), parts).total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -292,12 +359,7 @@ size_t mla_get_workspace_size_multi_token(int64_t batch, int64_t num_heads, int6
   if (q_len < 1 || q_len > MLA_MAX_QUERY_LEN) return 0;
   if (max_seq_len < 0 || max_seq_len > INT32_MAX / 2) return 0;
   if (num_splits < 0 || num_splits > MLA_MAX_FORCED_SPLITS) return 0;
-  if (num_cus <= 0) num_cus = kDefaultCus;
-  const int64_t rows = num_heads * q_len;
-  if (num_splits > 0)
-    return mla::workspace_layout(batch, rows, forced_rows(batch, num_splits), 1).total;
-  const int64_t parts = mla::max_partitions(num_cus, rows, 0);
-  return mla::workspace_layout(batch, rows, auto_rows(batch, parts, max_seq_len), parts).total;
+  return dense_workspace_need(batch, num_heads * q_len, max_seq_len, num_splits, num_cus);
 }
 
 size_t mla_get_workspace_size(int64_t batch, int64_t num_heads, int64_t max_seq_len,
@@ -329,6 +391,19 @@ mla_status_t mla_decode(const void* q, const void* kv_cache, const int32_t* bloc
                                 1, block_size, num_splits, batch, max_blocks_per_seq,
                                 num_blocks, kv_dtype, kv_scale, workspace, workspace_bytes,
                                 stream);
+}
+
+mla_status_t mla_decode_noalloc(const void* q, const void* kv_cache, const int32_t* block_table,
+                                const int32_t* seq_lens, void* out, float* lse, float scale,
+                                int32_t num_heads, int32_t q_len, int32_t block_size,
+                                int32_t num_splits, int32_t batch, int32_t max_blocks_per_seq,
+                                int32_t num_blocks, int32_t kv_dtype, float kv_scale,
+                                void* stream) {
+  DecodeArgs a{q, kv_cache, block_table, seq_lens, out, lse, scale, num_heads, q_len,
+               block_size, num_splits, batch, max_blocks_per_seq, num_blocks, kv_dtype,
+               kv_scale, nullptr, 0, static_cast<hipStream_t>(stream)};
+  a.scratch = true;
+  return run_decode(a, nullptr);
 }
 
 mla_status_t mla_decode_profiled(const void* q, const void* kv_cache,

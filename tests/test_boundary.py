@@ -387,3 +387,32 @@ def test_cached_workspace_refused_under_graph_capture(monkeypatch):
     monkeypatch.setattr(torch.cuda, "is_current_stream_capturing", lambda: True)
     with pytest.raises(RuntimeError, match="capturing"):
         mla.workspace_for(torch.device("cuda", 0), None, 1024)
+
+
+def _decode_noalloc(q_len=1, **over):
+    a = dict(q=FAKE, kv=FAKE, bt=FAKE, sl=FAKE, out=FAKE, lse=None, scale=0.07, heads=16,
+             bs=32, splits=0, batch=2, max_blocks=4, num_blocks=8, kv_dtype=0, kv_scale=1.0)
+    a.update(over)
+    vp = lambda x: ctypes.c_void_p(x) if x is not None else None  # noqa: E731
+    return mla.library().mla_decode_noalloc(
+        vp(a["q"]), vp(a["kv"]), vp(a["bt"]), vp(a["sl"]), vp(a["out"]), vp(a["lse"]),
+        a["scale"], a["heads"], q_len, a["bs"], a["splits"], a["batch"], a["max_blocks"],
+        a["num_blocks"], a["kv_dtype"], a["kv_scale"], None)
+
+
+@pytest.mark.parametrize("over", [d for d in INVALID if "ws" not in d],
+                         ids=lambda d: str(d))
+def test_decode_noalloc_rejects_like_decode(over):
+    assert _decode_noalloc(**over) == mla.MLA_ERR_INVALID_ARG
+
+
+def test_decode_noalloc_scratch_size_in_header():
+    text = open(HEADER).read()
+    assert "#define MLA_NOALLOC_SCRATCH_BYTES (96ull << 20)" in text
+    assert mla.NOALLOC_SCRATCH_BYTES == 96 << 20
+
+
+@pytest.mark.skipif(HAS_GPU, reason="would reach the device")
+def test_decode_noalloc_without_device():
+    assert _decode_noalloc() == mla.MLA_ERR_NO_DEVICE
+    assert _decode_noalloc(q_len=3, splits=16, batch=300, heads=128) == mla.MLA_ERR_NO_DEVICE
