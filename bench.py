@@ -220,6 +220,98 @@ def calib_copy(torch, dev, nbytes: int, reps: int) -> int:
     return 0
 
 
+def _peaks_lib():
+    import ctypes
+
+    from mla_paged_attention_amd import build as hip_build
+    if not os.path.exists(hip_build.PEAKS_LIBRARY):
+        raise RuntimeError(f"{hip_build.PEAKS_LIBRARY} is not built")
+    lib = ctypes.CDLL(hip_build.PEAKS_LIBRARY)
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.peaks_stream_lds.argtypes = [vp, i64, i32, i32, i32, vp]
+    lib.peaks_read.argtypes = [vp, i64, i32, vp, vp]
+    lib.peaks_mfma.argtypes = [i32, i32, i32, vp, vp]
+    for f in (lib.peaks_stream_lds, lib.peaks_read, lib.peaks_mfma):
+        f.restype = i32
+    return lib
+
+
+def _median_launch_us(torch, launch, reps: int) -> float:
+    """Median duration of `reps` back-to-back launches, each between events."""
+    stream = torch.cuda.current_stream()
+    launch()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for e0, e1 in ev:
+        e0.record(stream)
+        launch()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) * 1e3 for e0, e1 in ev)
+
+
+TILE_BYTES = 36864          # one ring stage of the attention kernels
+
+
+def measure_peaks(torch, dev, which=("hbm", "bf16", "fp8"), full: bool = False,
+                  reps: int = 10) -> dict:
+    """What this GPU delivers, measured by libmla_peaks.so's calibration
+    kernels (HBM: 2 GiB streamed through LDS as 36 KB direct-to-LDS tiles
+    with the non-temporal bit, one workgroup per CU and two tiles in flight
+    as in the attention ring; matrix cores: dense loops of the bf16 16x16x32
+    and scaled E4M3 16x16x128 ops on every SIMD)."""
+    import ctypes
+    lib = _peaks_lib()
+    h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    if "hbm" in which:
+        nbytes = 2 << 30
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        ntiles = nbytes // TILE_BYTES
+        moved = ntiles * TILE_BYTES
+        shapes = [(256, 2, 1)]
+        if full:
+            shapes += [(256, 1, 1), (256, 3, 1), (1024, 2, 1), (2048, 2, 1), (256, 2, 0),
+                       (1024, 2, 0)]
+        for grid, inflight, nt in shapes:
+            def launch(g=grid, k=inflight, n=nt):
+                assert lib.peaks_stream_lds(ctypes.c_void_p(buf.data_ptr()), ntiles, g, k, n,
+                                            h) == 0
+            us = _median_launch_us(torch, launch, reps)
+            key = f"stream_lds_grid{grid}_inflight{inflight}_{'nt' if nt else 'plain'}"
+            res[key] = round(moved / (us * 1e-6) / 1e9, 1)
+        sink = torch.zeros(1, dtype=torch.int32, device=dev)
+        for grid in ((1024, 4096) if full else (4096,)):
+            def launch_read(g=grid):
+                assert lib.peaks_read(ctypes.c_void_p(buf.data_ptr()), nbytes // 16, g,
+                                      ctypes.c_void_p(sink.data_ptr()), h) == 0
+            us = _median_launch_us(torch, launch_read, reps)
+            res[f"read_grid{grid}"] = round(nbytes / (us * 1e-6) / 1e9, 1)
+        res["hbm_GBps"] = res["stream_lds_grid256_inflight2_nt"]
+        del buf
+    for name, fp8, iters, per_op in (("bf16", 0, 8192, 16384), ("fp8", 1, 4096, 65536)):
+        if name not in which:
+            continue
+        grid = 1024   # four workgroups of four waves per CU: four waves per SIMD
+        sink = torch.zeros(grid, dtype=torch.float32, device=dev)
+
+        def launch_mfma(f=fp8, it=iters):
+            assert lib.peaks_mfma(f, grid, it, ctypes.c_void_p(sink.data_ptr()), h) == 0
+        us = _median_launch_us(torch, launch_mfma, reps)
+        flops = grid * 4 * 4 * iters * per_op
+        res[f"mfma_{name}_TFLOPs"] = round(flops / (us * 1e-6) / 1e12, 1)
+    return res
+
+
+def bench_peaks(torch, dev) -> int:
+    res = measure_peaks(torch, dev, full=True)
+    res.update({"spec_hbm_GBps": PEAK_HBM_GBPS, "spec_mfma_TFLOPs": PEAK_MFMA_TFLOPS,
+                "kernel_source": "mla_paged_attention_amd/csrc/peaks.hip"})
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def time_queued(torch, fn, steps: int, warmup: int):
     """GPU time of calls fn(i) that are shorter than their own host-side
     launch cost. The stream is held by a bounded spin kernel while the host
@@ -347,6 +439,8 @@ def main(argv=None) -> int:
     ap.add_argument("--graph", action="store_true",
                     help="also time the call replayed from a captured HIP graph")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-measured-peak", action="store_true",
+                    help="skip the calibration kernels (measured peak beside the spec peak)")
     ap.add_argument("--gemm", type=int, default=0, metavar="M",
                     help="instead of decoding, time the block-scaled E4M3 projection at "
                          "decode batch M (n = 2112, k = 7168 unless --gemm-nk)")
@@ -355,6 +449,9 @@ def main(argv=None) -> int:
                     help="instead of decoding, time the per-head absorption products at "
                          "decode batch B (heads from --absorb-heads)")
     ap.add_argument("--absorb-heads", type=int, default=16)
+    ap.add_argument("--peaks", action="store_true",
+                    help="instead of decoding, measure this GPU's HBM stream and matrix-core "
+                         "peaks with the calibration kernels (libmla_peaks.so)")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="instead of decoding, run plain device copies and reductions of "
                          "MIB MiB (HBM counter calibration and practical bandwidth)")
@@ -378,6 +475,8 @@ def main(argv=None) -> int:
     dev = torch.device("cuda:0")
     if args.calib_copy:
         return calib_copy(torch, dev, args.calib_copy << 20, max(args.steps, 1))
+    if args.peaks:
+        return bench_peaks(torch, dev)
     if args.absorb:
         return bench_absorb(torch, mla, workloads, dev, args.absorb, args.absorb_heads,
                             args.steps, args.warmup)
@@ -420,6 +519,13 @@ def main(argv=None) -> int:
                    kv_scale=wl.kv_scale, out=out, lse=lse, workspace=ws, stream=on,
                    events=events)
 
+    mp = None
+    if not args.no_measured_peak:
+        # The calibration kernels run before the warmup: they are measurement
+        # work of their own, and they bring the GPU out of the idle state of
+        # the host-side set-up before the timed calls.
+        log("measuring this GPU's HBM and matrix-core peaks")
+        mp = measure_peaks(torch, dev)
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -531,6 +637,16 @@ def main(argv=None) -> int:
     else:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS,
                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBPS, 4)}
+    if mp is not None:
+        measured = mp["hbm_GBps"] if roofline["bound"] == "hbm" else \
+            mp[f"mfma_{'fp8' if wl.kv_dtype == 'fp8' else 'bf16'}_TFLOPs"]
+        which = ("bf16",) if wl.kv_dtype != "fp8" else ("fp8",)
+        roofline["measured_peak"] = measured
+        roofline["frac_of_measured_peak"] = round(roofline["achieved"] / measured, 4)
+        roofline["measured_peak_kernel"] = (
+            "2 GiB through LDS in 36 KB direct-to-LDS tiles, non-temporal, 256 workgroups, "
+            "2 tiles in flight" if roofline["bound"] == "hbm" else
+            f"dense {which[0]} matrix-op loop, 4 waves per SIMD")
     roofline.update({
         "traffic": traffic, "kernel": kernel_name,
         "kernel_us_avg": round(attn_avg * 1e3, 2),
@@ -580,6 +696,7 @@ def main(argv=None) -> int:
                        "attention_p10_p90": [pct(sorted(x * 1e3 for x in attn_ms), 0.1),
                                              pct(sorted(x * 1e3 for x in attn_ms), 0.9)]},
         "roofline": roofline,
+        "measured_peaks": mp,
         "cpu_baseline": None,
         "parity": None,
     }

@@ -15,6 +15,10 @@ CSRC = os.path.join(HERE, "csrc")
 SOURCES = [os.path.join(CSRC, f)
            for f in ("mla_kernels.hip", "gemm_fp8.hip", "absorb.hip", "mla_api.hip")]
 LIBRARY = os.path.join(HERE, "libmla_mi355x.so")
+# Calibration kernels (measured HBM and matrix-core peaks), a library of
+# their own: the decode library does not contain them.
+PEAKS_SOURCES = [os.path.join(CSRC, "peaks.hip")]
+PEAKS_LIBRARY = os.path.join(HERE, "libmla_peaks.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -30,9 +34,9 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False, extra_flags=None) -> str:
-    tmp = LIBRARY + ".tmp"
-    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-o", tmp, *SOURCES]
+def _hipcc(sources, library, verbose, extra_flags):
+    tmp = library + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(extra_flags or []), "-o", tmp, *sources]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -42,8 +46,15 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIBRARY)
-    return LIBRARY
+    os.replace(tmp, library)
+    return library
+
+
+def build(verbose: bool = False, extra_flags=None) -> str:
+    """Build the decode library and the calibration library; returns the
+    decode library's path."""
+    _hipcc(PEAKS_SOURCES, PEAKS_LIBRARY, verbose, extra_flags)
+    return _hipcc(SOURCES, LIBRARY, verbose, extra_flags)
 
 
 if __name__ == "__main__":
