@@ -42,6 +42,19 @@
  *    workspace-size symbol broke import on other GPUs).
  *  - Unsupported configurations are reported, never silently changed.
  *  - No C++ exception crosses this boundary.
+ *  - Device-side inputs are clamped, never trusted: a block-table entry outside
+ *    [0, num_blocks) is read as block 0 and a seq_lens entry outside
+ *    [0, max_blocks_per_seq * block_size] is clamped into that range (no
+ *    out-of-bounds access; the result is not meaningful). The bounds-check
+ *    build of this library (libmla_mi355x_checked.so, compiled with
+ *    MLA_BOUNDS_CHECK=1) also reports each clamp: every decode call with a
+ *    workspace first zeroes the 32-bit word at byte offset
+ *    MLA_BOUNDS_WORD_OFFSET of the workspace, then ORs MLA_BOUNDS_BAD_BLOCK
+ *    and/or MLA_BOUNDS_BAD_SEQ_LEN into it; the host reads it after the call
+ *    has run (e.g. after a stream sync). A sparse list entry outside
+ *    [0, seq_len) is not an error (it is skipped by definition), but its
+ *    request's seq_len and the block ids it maps through are checked.
+ *    mla_decode_noalloc reports nothing.
  */
 #ifndef MLA_MI355X_H
 #define MLA_MI355X_H
@@ -63,6 +76,10 @@ extern "C" {
 #define MLA_GEMM_MAX_M 65536   /* tokens per mla_gemm_fp8_blockscale call */
 #define MLA_GEMM_MAX_N 65536
 #define MLA_GEMM_MAX_K 65536
+/* Bounds-check build: the error word's byte offset in the workspace, and its bits. */
+#define MLA_BOUNDS_WORD_OFFSET 32
+#define MLA_BOUNDS_BAD_BLOCK 1
+#define MLA_BOUNDS_BAD_SEQ_LEN 2
 /* Bytes of the device scratch array behind mla_decode_noalloc (one per GPU). */
 #define MLA_NOALLOC_SCRATCH_BYTES (96ull << 20)
 

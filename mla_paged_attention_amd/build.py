@@ -19,6 +19,9 @@ LIBRARY = os.path.join(HERE, "libmla_mi355x.so")
 # their own: the decode library does not contain them.
 PEAKS_SOURCES = [os.path.join(CSRC, "peaks.hip")]
 PEAKS_LIBRARY = os.path.join(HERE, "libmla_peaks.so")
+# Bounds-check build of the decode library: every clamp of a corrupt input
+# (block id, seq_len) is also reported in an error word of the workspace.
+CHECKED_LIBRARY = os.path.join(HERE, "libmla_mi355x_checked.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
@@ -51,9 +54,10 @@ def _hipcc(sources, library, verbose, extra_flags):
 
 
 def build(verbose: bool = False, extra_flags=None) -> str:
-    """Build the decode library and the calibration library; returns the
-    decode library's path."""
+    """Build the decode library, its bounds-check build and the calibration
+    library; returns the decode library's path."""
     _hipcc(PEAKS_SOURCES, PEAKS_LIBRARY, verbose, extra_flags)
+    _hipcc(SOURCES, CHECKED_LIBRARY, verbose, [*(extra_flags or []), "-DMLA_BOUNDS_CHECK=1"])
     return _hipcc(SOURCES, LIBRARY, verbose, extra_flags)
 
 

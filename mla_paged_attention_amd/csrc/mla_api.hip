@@ -254,6 +254,12 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   };
 
   if (!rec(0)) return MLA_ERR_HIP;
+  // Bounds-check build: this call's error word, zeroed first.
+  int32_t* err_word = nullptr;
+  if (MLA_BOUNDS_CHECK) {
+    err_word = header + mla::kBoundsWordIndex;
+    if (mla::launch_clear_word(err_word, s) != hipSuccess) return MLA_ERR_HIP;
+  }
   // The plan sees every sparse request as topk tokens long.
   const int32_t* lens = a.seq_lens;
   if (sparse) {
@@ -262,7 +268,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
                                 a.max_blocks, a.num_blocks, bs_log2_of(a.block_size),
                                 int32_t(cache_cap), int32_t(mla::sparse_stride(a.topk)),
                                 reinterpret_cast<int32_t*>(ws + w.sp_rows), sp_len,
-                                ws + w.zero_row, s) != hipSuccess)
+                                ws + w.zero_row, err_word, s) != hipSuccess)
       return MLA_ERR_HIP;
     lens = sp_len;
   }
@@ -313,6 +319,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   args.wr_row_ptr = row_ptr;
   args.wr_split = split;
   args.wr_header = header;
+  args.err_word = err_word;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
   int64_t parts_launched = (parts + 7) / 8 * 8;
   if (parts_launched * args.head_tiles > INT32_MAX) return MLA_ERR_INVALID_ARG;

@@ -6,7 +6,18 @@
 #include <stddef.h>
 #include <stdint.h>
 
+// Bounds-check build (-DMLA_BOUNDS_CHECK=1, libmla_mi355x_checked.so): every
+// clamp of a corrupt input is also reported in an error word of the
+// workspace. The release build compiles the reports away.
+#ifndef MLA_BOUNDS_CHECK
+#define MLA_BOUNDS_CHECK 0
+#endif
+
 namespace mla {
+
+constexpr int kBoundsBadBlock = 1;   // a block-table entry outside [0, num_blocks)
+constexpr int kBoundsBadSeqLen = 2;  // a seq_lens entry outside [0, max_blocks * block_size]
+constexpr int kBoundsWordIndex = 8;  // int32 index of the error word in the workspace header
 
 constexpr int kDK = 576;        // key width (512 kv_c + 64 rope)
 constexpr int kDV = 512;        // value width (kv_c)
@@ -146,6 +157,8 @@ struct AttnArgs {
   int32_t* wr_row_ptr;
   int32_t* wr_split;
   int32_t* wr_header;
+  // Bounds-check build: the error word (null otherwise).
+  int32_t* err_word;
 };
 
 constexpr int kInlinePlanBatch = 64;  // one request per lane of a wave
@@ -171,7 +184,10 @@ hipError_t launch_sparse_rows(const int32_t* indices, int32_t topk, const int32_
                               const int32_t* seq_lens, int32_t batch, int32_t max_blocks,
                               int32_t num_blocks, int32_t bs_log2, int32_t cap_tokens,
                               int32_t stride, int32_t* rows, int32_t* eff_len, void* zero_row,
-                              hipStream_t stream);
+                              int32_t* err_word, hipStream_t stream);
+
+// Bounds-check build: zeroes the error word at the start of a call.
+hipError_t launch_clear_word(int32_t* word, hipStream_t stream);
 
 // Block-scaled E4M3 projection (gemm_fp8.hip): bf16 -> E4M3 codes with one
 // scale per token and 128-wide group, and c[m][n] = A[m][k] B[n][k]^T with

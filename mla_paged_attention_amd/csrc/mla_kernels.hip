@@ -146,6 +146,22 @@ __device__ __forceinline__ int piece_start(int j, int units, int k) {
 
 __device__ __forceinline__ int clamp_len(int n, int cap) { return n < 0 ? 0 : (n > cap ? cap : n); }
 
+// Bounds-check build: reports a clamped input in the call's error word.
+__device__ __forceinline__ void report_bounds(int32_t* word, int bit) {
+#if MLA_BOUNDS_CHECK
+  if (word) atomicOr(word, bit);
+#else
+  (void)word;
+  (void)bit;
+#endif
+}
+
+// seq_lens[b] clamped to [0, cap]; a value outside is reported.
+__device__ __forceinline__ int checked_len(int n, int cap, int32_t* word) {
+  if (n < 0 || n > cap) report_bounds(word, kBoundsBadSeqLen);
+  return clamp_len(n, cap);
+}
+
 __device__ __forceinline__ int units_of(int n) {
   int u = (n + kUnit - 1) / kUnit;
   return u < 1 ? 1 : u;  // an empty request still owns one (empty) unit
@@ -680,7 +696,7 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
   const int bs_mask = (1 << a.bs_log2) - 1;
 
   for_each_piece(a, part, [&](int b, int u0, int u1, int out_row) {
-    const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
+    const int n = checked_len(a.seq_lens[b], a.cap_tokens, a.err_word);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
     const int ntiles = u_end > u0 ? (u_end - u0 + 1) / 2 : 0;
     const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
@@ -694,7 +710,10 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
     auto unit_rows = [&](int u, bool valid) -> const uint8_t* {
       const int t0 = u * kUnit;
       int blk = valid ? scalar_load_i32(bt_row + (t0 >> a.bs_log2)) : 0;
-      if (blk < 0 || blk >= a.num_blocks) blk = 0;
+      if (blk < 0 || blk >= a.num_blocks) {
+        report_bounds(a.err_word, kBoundsBadBlock);
+        blk = 0;
+      }
       return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowBytes;
     };
     auto issue_tile = [&](int k) {
@@ -1211,7 +1230,7 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
   static_assert(sizeof(ebuf[0]) == 64, "scale stride");
 
   for_each_piece(a, part, [&](int b, int u0, int u1, int out_row) {
-    const int n = clamp_len(a.seq_lens[b], a.cap_tokens);
+    const int n = checked_len(a.seq_lens[b], a.cap_tokens, a.err_word);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
     const int ntiles = u_end > u0 ? (u_end - u0 + kUnits - 1) / kUnits : 0;
     const int32_t* bt_row = a.block_table + size_t(b) * a.max_blocks;
@@ -1225,7 +1244,10 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
     auto unit_rows = [&](int u) -> const uint8_t* {
       const int t0 = u * kUnit;
       int blk = scalar_load_i32(bt_row + (t0 >> a.bs_log2));
-      if (blk < 0 || blk >= a.num_blocks) blk = 0;
+      if (blk < 0 || blk >= a.num_blocks) {
+        report_bounds(a.err_word, kBoundsBadBlock);
+        blk = 0;
+      }
       return a.kv + (size_t(blk) * (size_t(1) << a.bs_log2) + size_t(t0 & bs_mask)) * kRowB;
     };
     auto issue_tile = [&](int k) {
@@ -1880,7 +1902,7 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
 __global__ void __launch_bounds__(256) sparse_rows_kernel(
     const int32_t* indices, int32_t topk, const int32_t* block_table, const int32_t* seq_lens,
     int32_t batch, int32_t max_blocks, int32_t num_blocks, int32_t bs_log2, int32_t cap_tokens,
-    int32_t stride, int32_t* rows, int32_t* eff_len, uint32_t* zero_row) {
+    int32_t stride, int32_t* rows, int32_t* eff_len, uint32_t* zero_row, int32_t* err_word) {
   const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < kDK * 2 / 4) zero_row[i] = 0u;
   if (i >= int64_t(batch) * stride) return;
@@ -1889,10 +1911,13 @@ __global__ void __launch_bounds__(256) sparse_rows_kernel(
   int row = -1;
   if (k < topk) {
     const int t = indices[size_t(b) * topk + k];
-    const int n = clamp_len(seq_lens[b], cap_tokens);
+    const int n = checked_len(seq_lens[b], cap_tokens, err_word);
     if (t >= 0 && t < n) {
       const int blk = block_table[size_t(b) * max_blocks + (t >> bs_log2)];
-      if (blk >= 0 && blk < num_blocks) row = (blk << bs_log2) + (t & ((1 << bs_log2) - 1));
+      if (blk >= 0 && blk < num_blocks)
+        row = (blk << bs_log2) + (t & ((1 << bs_log2) - 1));
+      else
+        report_bounds(err_word, kBoundsBadBlock);
     }
   }
   rows[i] = row;
@@ -1902,12 +1927,19 @@ hipError_t launch_sparse_rows(const int32_t* indices, int32_t topk, const int32_
                               const int32_t* seq_lens, int32_t batch, int32_t max_blocks,
                               int32_t num_blocks, int32_t bs_log2, int32_t cap_tokens,
                               int32_t stride, int32_t* rows, int32_t* eff_len, void* zero_row,
-                              hipStream_t stream) {
+                              int32_t* err_word, hipStream_t stream) {
   const int64_t n = int64_t(batch) * stride;
   const int64_t nb = (n > kDK * 2 / 4 ? n : kDK * 2 / 4) + 255;
   hipLaunchKernelGGL(sparse_rows_kernel, dim3(unsigned(nb / 256)), dim3(256), 0, stream, indices,
                      topk, block_table, seq_lens, batch, max_blocks, num_blocks, bs_log2,
-                     cap_tokens, stride, rows, eff_len, static_cast<uint32_t*>(zero_row));
+                     cap_tokens, stride, rows, eff_len, static_cast<uint32_t*>(zero_row), err_word);
+  return hipGetLastError();
+}
+
+__global__ void clear_word_kernel(int32_t* word) { *word = 0; }
+
+hipError_t launch_clear_word(int32_t* word, hipStream_t stream) {
+  hipLaunchKernelGGL(clear_word_kernel, dim3(1), dim3(1), 0, stream, word);
   return hipGetLastError();
 }
 

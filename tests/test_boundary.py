@@ -416,3 +416,23 @@ def test_decode_noalloc_scratch_size_in_header():
 def test_decode_noalloc_without_device():
     assert _decode_noalloc() == mla.MLA_ERR_NO_DEVICE
     assert _decode_noalloc(q_len=3, splits=16, batch=300, heads=128) == mla.MLA_ERR_NO_DEVICE
+
+
+def test_bounds_check_build_matches_header():
+    # The checked build exports the same ABI, and its error-word location and
+    # bits in the internal launch header agree with include/mla.h.
+    from mla_paged_attention_amd import build as hip_build
+    text = open(HEADER).read()
+    internal = open(os.path.join(ROOT, "mla_paged_attention_amd", "csrc",
+                                 "mla_internal.h")).read()
+    off = int(re.search(r"#define MLA_BOUNDS_WORD_OFFSET (\d+)", text).group(1))
+    idx = int(re.search(r"kBoundsWordIndex = (\d+);", internal).group(1))
+    assert off == 4 * idx
+    assert int(re.search(r"#define MLA_BOUNDS_BAD_BLOCK (\d+)", text).group(1)) == \
+        int(re.search(r"kBoundsBadBlock = (\d+);", internal).group(1))
+    assert int(re.search(r"#define MLA_BOUNDS_BAD_SEQ_LEN (\d+)", text).group(1)) == \
+        int(re.search(r"kBoundsBadSeqLen = (\d+);", internal).group(1))
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_build.CHECKED_LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (mla_\w+)", out))
+    assert set(declared_functions()) <= exported
