@@ -272,12 +272,21 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
       return MLA_ERR_HIP;
     lens = sp_len;
   }
-  // Small batches on the contiguous plan work it out inside the attention
-  // kernel, and forced splits need no plan (piece k of request b is
-  // partition b * S + k, its partial row too): one launch fewer.
-  const bool inline_plan = a.num_splits == 0 && a.batch <= mla::kInlinePlanBatch &&
-                           a.batch < 2 * max_parts;
-  if (!inline_plan && a.num_splits == 0 &&
+  // The attention kernel works the automatic plan out itself (one launch
+  // fewer) for small batches on the contiguous plan, and for batches on the
+  // snake plan (at least two requests per partition) up to
+  // kInlineSnakeBatch requests whose pieces fill at most 64 rounds of the
+  // deal. Forced splits need no plan: piece k of request b is partition
+  // b * S + k, its partial row too.
+  int inline_plan = mla::kInlineNone;
+  if (a.num_splits == 0) {
+    if (a.batch <= mla::kInlinePlanBatch && a.batch < 2 * max_parts)
+      inline_plan = mla::kInlineContiguous;
+    else if (a.batch >= 2 * max_parts && a.batch <= mla::kInlineSnakeBatch &&
+             a.batch + max_parts <= 64 * max_parts)
+      inline_plan = mla::kInlineSnake;
+  }
+  if (inline_plan == mla::kInlineNone && a.num_splits == 0 &&
       mla::launch_plan(lens, a.batch, int32_t(cap), int32_t(max_parts), w, a.workspace, s) !=
           hipSuccess)
     return MLA_ERR_HIP;
@@ -315,7 +324,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   args.sparse_rows = sparse ? reinterpret_cast<const int32_t*>(ws + w.sp_rows) : nullptr;
   args.sparse_stride = sparse ? int32_t(mla::sparse_stride(a.topk)) : 0;
   args.zero_row = sparse ? ws + w.zero_row : nullptr;
-  args.inline_plan = inline_plan ? 1 : 0;
+  args.inline_plan = inline_plan;
   args.wr_row_ptr = row_ptr;
   args.wr_split = split;
   args.wr_header = header;

@@ -162,6 +162,13 @@ struct AttnArgs {
 };
 
 constexpr int kInlinePlanBatch = 64;  // one request per lane of a wave
+// inline_plan modes: none (plan kernel, or forced splits), the contiguous
+// plan worked out by one wave (at most kInlinePlanBatch requests), or the
+// snake plan worked out by every workgroup (at most kInlineSnakeBatch).
+constexpr int kInlineNone = 0;
+constexpr int kInlineContiguous = 1;
+constexpr int kInlineSnake = 2;
+constexpr int kInlineSnakeBatch = 1024;
 
 // Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
 // only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.

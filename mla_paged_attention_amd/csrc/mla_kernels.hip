@@ -424,21 +424,158 @@ __global__ void __launch_bounds__(NT) plan_kernel(
   }
 }
 
+// The snake plan of plan_kernel, worked out by every workgroup of the
+// attention kernel itself (batches of at most kInlineSnakeBatch requests),
+// so that no plan kernel runs. Every workgroup must derive the same plan, so
+// the ranking is deterministic: pieces are ordered by an 8-bit cost bucket,
+// largest first, ties in piece order (a stable LSD radix sort of one bit per
+// pass), where plan_kernel ranks equal costs in atomic order. Scratch lives
+// in `scr` (the attention kernel's still-empty LDS ring). The partition-0
+// workgroups write row_ptr, split and header for the combine. This
+// partition's items (in rank order) land in items[0..*n_items).
+template <int NT>
+__device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* items,
+                                  int* n_items) {
+  __shared__ int s_wave[48];
+  constexpr int kMaxPieces = kInlineSnakeBatch + kMaxPlanParts;
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  int* units = scr;                           // [B]
+  int* kb = units + B;                        // [B] pieces per request
+  int* pk = kb + B;                           // [B + 1] first piece of each request
+  int* rb = pk + B + 1;                       // [B + 1] first partial row
+  int* preq = rb + B + 1;                     // [N] request of each piece
+  int* keyA = preq + kMaxPieces;
+  int* keyB = keyA + kMaxPieces;
+  int* idxA = keyB + kMaxPieces;
+  int* idxB = idxA + kMaxPieces;
+  // Units and costs; their total and maximum.
+  int csum = 0, cmax = 0;
+  for (int b = tid; b < B; b += NT) {
+    const int u = units_of(clamp_len(a.seq_lens[b], a.cap_tokens));
+    units[b] = u;
+    csum += kOverheadUnits + u;
+    cmax = max(cmax, kOverheadUnits + u);
+  }
+  int tot;
+  (void)block_exclusive_scan<NT>(csum, s_wave, &tot);
+  cmax = block_max<NT>(cmax, s_wave);  // also orders the units[] stores
+  int P = (tot + a.parts_cap - 1) / a.parts_cap;
+  if (P < kMinPartUnits) P = kMinPartUnits;
+  // Pieces per request (requests above the target are cut) and the bases of
+  // pieces, partial rows and split requests, over contiguous chunks.
+  const int C = (B + NT - 1) / NT;
+  const int b0 = min(B, tid * C), b1 = min(B, b0 + C);
+  int3 mine = make_int3(0, 0, 0);
+  for (int b = b0; b < b1; ++b) {
+    const int cost = kOverheadUnits + units[b];
+    const int k = cost > P ? (cost + P - 1) / P : 1;
+    kb[b] = k;
+    mine.x += k;
+    mine.y += k > 1 ? k : 0;
+    mine.z += k > 1 ? 1 : 0;
+  }
+  int3 tot3;
+  int3 ex3 = block_exclusive_scan3<NT>(mine, s_wave, &tot3);
+  const int N = tot3.x;
+  const int parts = min(a.parts_cap, N);
+  int shift = 0;
+  while ((cmax >> shift) > 255) ++shift;
+  for (int b = b0; b < b1; ++b) {
+    const int k = kb[b];
+    pk[b] = ex3.x;
+    rb[b] = ex3.y;
+    if (part == 0 && k > 1) a.wr_split[ex3.z] = b;
+    const int q = units[b] / k, r = units[b] - q * k;
+    for (int j = 0; j < k; ++j) {
+      const int len = q + (j < r ? 1 : 0);
+      keyA[ex3.x + j] = 255 - min(255, (kOverheadUnits + len) >> shift);
+      idxA[ex3.x + j] = ex3.x + j;
+      preq[ex3.x + j] = b;
+    }
+    ex3.x += k;
+    ex3.y += k > 1 ? k : 0;
+    ex3.z += k > 1 ? 1 : 0;
+  }
+  if (part == 0) {
+    for (int b = b0; b < b1; ++b) a.wr_row_ptr[b] = rb[b];
+    if (tid == 0) {
+      a.wr_row_ptr[B] = tot3.y;
+      a.wr_header[0] = parts;
+      a.wr_header[1] = P;
+      a.wr_header[2] = tot3.z;
+      a.wr_header[3] = kPlanSnake;
+    }
+  }
+  __syncthreads();
+  // Stable LSD radix sort of (key, piece) by one key bit per pass: each
+  // thread keeps its contiguous chunk's order, zeros before ones.
+  const int E = (N + NT - 1) / NT;
+  const int e0 = min(N, tid * E), e1 = min(N, e0 + E);
+  int* kin = keyA;
+  int* iin = idxA;
+  int* kout = keyB;
+  int* iout = idxB;
+  for (int bit = 0; bit < 8; ++bit) {
+    int z = 0;
+    for (int e = e0; e < e1; ++e) z += ((kin[e] >> bit) & 1) ? 0 : 1;
+    int zt;
+    int zb = block_exclusive_scan<NT>(z, s_wave, &zt);
+    if (zt == 0 || zt == N) continue;  // every key has this bit alike: order unchanged
+    for (int e = e0; e < e1; ++e) {
+      const int key = kin[e];
+      const bool one = (key >> bit) & 1;
+      const int dst = one ? zt + (e - zb) : zb;
+      zb += one ? 0 : 1;
+      kout[dst] = key;
+      iout[dst] = iin[e];
+    }
+    __syncthreads();
+    int* t0 = kin;
+    kin = kout;
+    kout = t0;
+    int* t1 = iin;
+    iin = iout;
+    iout = t1;
+  }
+  // This partition's pieces: ranks r * parts + (r odd ? parts - 1 - part : part).
+  if (tid < 64) {
+    const int r = tid;
+    const int i = r * parts + ((r & 1) ? parts - 1 - part : part);
+    const bool live = part < parts && i < N;
+    const uint64_t m = __ballot(live);
+    if (live) {
+      const int p = iin[i];
+      const int b = preq[p];
+      const int j = p - pk[b];
+      const int k = kb[b];
+      items[r] = make_int4(b, piece_start(j, units[b], k), piece_start(j + 1, units[b], k),
+                           k > 1 ? rb[b] + j : -1);
+    }
+    if (tid == 0) *n_items = __popcll(m);
+  }
+  __syncthreads();
+}
+
 // Partition -> work items. Calls fn(b, u0, u1, row) for every piece of
 // partition `part`: units [u0, u1) of request b, written as the final output
 // when row < 0, else as partial row `row`. Uniform across the workgroup.
-template <typename Fn>
-__device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, Fn&& fn) {
-  // The item list of the three modes, then one loop with the only call of
+template <int NT, typename Fn>
+__device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int* scratch,
+                                               Fn&& fn) {
+  // The item list of the four modes, then one loop with the only call of
   // fn (the whole attention body is inlined there).
   __shared__ int4 s_items[kInlinePlanBatch];
   __shared__ int s_nitems;
   int n = 0, i0 = 0;
-  if (a.num_splits > 0) {
+  if (a.inline_plan == kInlineSnake) {
+    inline_snake_plan<NT>(a, part, scratch, s_items, &s_nitems);
+    n = __builtin_amdgcn_readfirstlane(s_nitems);
+  } else if (a.num_splits > 0) {
     // Forced split k of request b; an empty split still writes its
     // (zero, -inf) partial because the combine reads every row.
     n = part < a.batch * a.num_splits ? 1 : 0;
-  } else if (a.inline_plan) {
+  } else if (a.inline_plan == kInlineContiguous) {
     // The contiguous plan of plan_kernel, worked out by the first wave from
     // seq_lens (request = lane): costs, their prefix, the per-partition
     // target P, the pieces k of each request and the partial rows of split
@@ -695,7 +832,8 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
       (void __attribute__((address_space(3)))*)(&ring[0][0])));
   const int bs_mask = (1 << a.bs_log2) - 1;
 
-  for_each_piece(a, part, [&](int b, int u0, int u1, int out_row) {
+  for_each_piece<kWsThreads>(a, part, reinterpret_cast<int*>(&ring[0][0]),
+                             [&](int b, int u0, int u1, int out_row) {
     const int n = checked_len(a.seq_lens[b], a.cap_tokens, a.err_word);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
     const int ntiles = u_end > u0 ? (u_end - u0 + 1) / 2 : 0;
@@ -1229,7 +1367,8 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
   static_assert(!KV_FP8 || sizeof(pbuf[0]) == 2048, "P operand stride");
   static_assert(sizeof(ebuf[0]) == 64, "scale stride");
 
-  for_each_piece(a, part, [&](int b, int u0, int u1, int out_row) {
+  for_each_piece<kMhThreads>(a, part, reinterpret_cast<int*>(&ring[0][0]),
+                             [&](int b, int u0, int u1, int out_row) {
     const int n = checked_len(a.seq_lens[b], a.cap_tokens, a.err_word);
     const int u_end = min(u1, (n + kUnit - 1) / kUnit);
     const int ntiles = u_end > u0 ? (u_end - u0 + kUnits - 1) / kUnits : 0;
