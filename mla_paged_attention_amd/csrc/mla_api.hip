@@ -273,11 +273,11 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
     lens = sp_len;
   }
   // The attention kernel works the automatic plan out itself (one launch
-  // fewer) for small batches on the contiguous plan, and for batches on the
-  // snake plan (at least two requests per partition) up to
-  // kInlineSnakeBatch requests whose pieces fill at most 64 rounds of the
-  // deal. Forced splits need no plan: piece k of request b is partition
-  // b * S + k, its partial row too.
+  // fewer): the contiguous plan by one wave for small batches or by every
+  // workgroup up to kInlineContigBatch requests, and the snake plan (at
+  // least two requests per partition) up to kInlineSnakeBatch requests whose
+  // pieces fill at most 64 rounds of the deal. Forced splits need no plan:
+  // piece k of request b is partition b * S + k, its partial row too.
   int inline_plan = mla::kInlineNone;
   if (a.num_splits == 0) {
     if (a.batch <= mla::kInlinePlanBatch && a.batch < 2 * max_parts)
@@ -285,6 +285,8 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
     else if (a.batch >= 2 * max_parts && a.batch <= mla::kInlineSnakeBatch &&
              a.batch + max_parts <= 64 * max_parts)
       inline_plan = mla::kInlineSnake;
+    else if (a.batch < 2 * max_parts && a.batch <= mla::kInlineContigBatch)
+      inline_plan = mla::kInlineContiguousWide;
   }
   if (inline_plan == mla::kInlineNone && a.num_splits == 0 &&
       mla::launch_plan(lens, a.batch, int32_t(cap), int32_t(max_parts), w, a.workspace, s) !=

@@ -168,7 +168,9 @@ constexpr int kInlinePlanBatch = 64;  // one request per lane of a wave
 constexpr int kInlineNone = 0;
 constexpr int kInlineContiguous = 1;
 constexpr int kInlineSnake = 2;
+constexpr int kInlineContiguousWide = 3;  // the contiguous plan, worked out by every workgroup
 constexpr int kInlineSnakeBatch = 1024;
+constexpr int kInlineContigBatch = 4096;
 
 // Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
 // only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.

@@ -167,6 +167,14 @@ __device__ __forceinline__ int units_of(int n) {
   return u < 1 ? 1 : u;  // an empty request still owns one (empty) unit
 }
 
+// Wave-uniform load through the scalar unit (counted by lgkmcnt, not vmcnt,
+// so it does not disturb the vector-memory pipeline of the KV ring).
+__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
+  int32_t v;
+  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
+  return v;
+}
+
 // Automatic plan modes (header[3]).
 constexpr int kPlanContiguous = 0;
 constexpr int kPlanSnake = 1;
@@ -557,6 +565,74 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
   __syncthreads();
 }
 
+// The contiguous plan of plan_kernel, worked out by every workgroup of the
+// attention kernel (kInlinePlanBatch < batch <= kInlineContigBatch): costs
+// laid end to end, cut into partitions of P units. A partition's pieces are
+// one run of consecutive requests, so the workgroup keeps only where its run
+// starts (request, its cost prefix and its first partial row) and walks it.
+// Partition 0 writes row_ptr, split and header for the combine. `scr` is the
+// still-empty LDS ring.
+struct ContigWalk {
+  int b, cum, rb, P, parts;
+};
+
+template <int NT>
+__device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, ContigWalk* walk) {
+  __shared__ int s_wave[48];
+  const int tid = threadIdx.x;
+  const int B = a.batch;
+  int* cost = scr;  // [B]
+  const int C = (B + NT - 1) / NT;
+  const int b0 = min(B, tid * C), b1 = min(B, b0 + C);
+  int csum = 0;
+  for (int b = b0; b < b1; ++b) {
+    cost[b] = kOverheadUnits + units_of(clamp_len(a.seq_lens[b], a.cap_tokens));
+    csum += cost[b];
+  }
+  int total;
+  const int cex = block_exclusive_scan<NT>(csum, s_wave, &total);
+  int P = (total + a.parts_cap - 1) / a.parts_cap;
+  if (P < kMinPartUnits) P = kMinPartUnits;
+  const int parts = (total + P - 1) / P;
+  // Pieces per request and the bases of partial rows and split requests.
+  int c0 = cex;
+  int3 mine = make_int3(0, 0, 0);
+  for (int b = b0; b < b1; ++b) {
+    const int ub = c0 + kOverheadUnits, ue = c0 + cost[b];
+    const int k = (ue - 1) / P - ub / P + 1;
+    mine.y += k > 1 ? k : 0;
+    mine.z += k > 1 ? 1 : 0;
+    c0 = ue;
+  }
+  int3 tot3;
+  const int3 ex3 = block_exclusive_scan3<NT>(mine, s_wave, &tot3);
+  c0 = cex;
+  int rb = ex3.y, sb = ex3.z;
+  const int lo = part * P;
+  for (int b = b0; b < b1; ++b) {
+    const int ub = c0 + kOverheadUnits, ue = c0 + cost[b];
+    const int k = (ue - 1) / P - ub / P + 1;
+    // The first request reaching into this partition starts the walk.
+    if (part < parts && ue > lo && c0 <= lo) *walk = ContigWalk{b, c0, rb, P, parts};
+    if (part == 0) {
+      a.wr_row_ptr[b] = rb;
+      if (k > 1) a.wr_split[sb] = b;
+    }
+    rb += k > 1 ? k : 0;
+    sb += k > 1 ? 1 : 0;
+    c0 = ue;
+  }
+  if (part == 0 && tid == 0) {
+    a.wr_row_ptr[B] = tot3.y;
+    a.wr_header[0] = parts;
+    a.wr_header[1] = P;
+    a.wr_header[2] = tot3.z;
+    a.wr_header[3] = kPlanContiguous;
+  }
+  if (tid == 0 && part >= parts) *walk = ContigWalk{B, 0, 0, P, parts};
+  __syncthreads();
+}
+
 // Partition -> work items. Calls fn(b, u0, u1, row) for every piece of
 // partition `part`: units [u0, u1) of request b, written as the final output
 // when row < 0, else as partial row `row`. Uniform across the workgroup.
@@ -567,8 +643,20 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
   // fn (the whole attention body is inlined there).
   __shared__ int4 s_items[kInlinePlanBatch];
   __shared__ int s_nitems;
+  __shared__ ContigWalk s_walk;
   int n = 0, i0 = 0;
-  if (a.inline_plan == kInlineSnake) {
+  // Wide contiguous plan: this partition's run of requests (uniform across
+  // the workgroup), walked from its first request.
+  const bool walk = a.inline_plan == kInlineContiguousWide;
+  int wb = 0, wcum = 0, wrb = 0, wP = 1;
+  if (walk) {
+    inline_contiguous_plan<NT>(a, part, scratch, &s_walk);
+    wb = __builtin_amdgcn_readfirstlane(s_walk.b);
+    wcum = __builtin_amdgcn_readfirstlane(s_walk.cum);
+    wrb = __builtin_amdgcn_readfirstlane(s_walk.rb);
+    wP = __builtin_amdgcn_readfirstlane(s_walk.P);
+    n = a.batch;  // at most one piece per request of the run
+  } else if (a.inline_plan == kInlineSnake) {
     inline_snake_plan<NT>(a, part, scratch, s_items, &s_nitems);
     n = __builtin_amdgcn_readfirstlane(s_nitems);
   } else if (a.num_splits > 0) {
@@ -627,7 +715,22 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
   }
   for (int i = 0; i < n; ++i) {
     int b, u0, u1, row;
-    if (a.num_splits > 0) {
+    if (walk) {
+      const int lo = part * wP, hi = lo + wP;
+      const int ub = wcum + kOverheadUnits;
+      if (wb >= a.batch || ub >= hi) break;
+      const int ue = wcum + kOverheadUnits +
+                     units_of(clamp_len(scalar_load_i32(a.seq_lens + wb), a.cap_tokens));
+      const int first = ub / wP;
+      const int k = (ue - 1) / wP - first + 1;
+      b = wb;
+      u0 = max(ub, lo) - ub;
+      u1 = min(ue, hi) - ub;
+      row = k > 1 ? wrb + (part - first) : -1;
+      wrb += k > 1 ? k : 0;
+      wcum = ue;
+      ++wb;
+    } else if (a.num_splits > 0) {
       const int S = a.num_splits;
       b = part / S;
       const int k = part - b * S;
@@ -771,13 +874,6 @@ __device__ __forceinline__ void lds_read_tr8(const uint32_t (&vb)[4], u32x2_t (&
 #undef MLA_TR8
 #undef MLA_DSTR
 
-// Wave-uniform load through the scalar unit (counted by lgkmcnt, not vmcnt,
-// so it does not disturb the vector-memory pipeline of the KV ring).
-__device__ __forceinline__ int32_t scalar_load_i32(const int32_t* p) {
-  int32_t v;
-  asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(p) : "memory");
-  return v;
-}
 
 // Wave-specialised variant of the tile stream. Waves 0..3 issue the ring's
 // loads and own 128 output features each for P.V; wave 4 (the logit wave)
