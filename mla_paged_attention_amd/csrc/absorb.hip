@@ -24,9 +24,9 @@
 // consecutive output columns of one batch row and stores them as 8 bytes.
 // W_UK's A operand is read with gfx950's transposing LDS read
 // ds_read_b64_tr_b16 (k runs down its rows); W_UV's with 16-byte reads along
-// its rows. The workgroups of one weight slice sit a multiple of the head
-// count apart in launch order, so for head counts that are multiples of 8
-// they run on one XCD and share its L2 copy of the slice.
+// its rows. With a head count that is a multiple of 8, each XCD keeps whole
+// heads (absorb_task), so a head's activations and weight slices are fetched
+// into one L2 only.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -55,6 +55,30 @@ __device__ __forceinline__ a_u32x2_t pack4(a_f32x4_t v) {
   return a_u32x2_t{lo, hi};  // nearest even
 }
 
+// Workgroup -> (head, column slice, batch group) of a one-dimensional launch
+// of heads * slices * groups workgroups. Workgroups are dispatched round-robin
+// over the eight XCDs (each with its own L2), so with a head count that is a
+// multiple of 8 the XCD of launch index L (L mod 8) keeps the heads h = L mod 8
+// (mod 8): the slices of one batch group (which read the same activation rows)
+// and the groups of one slice (which read the same weight slice) then share
+// one L2. Other head counts keep the plain order (head and slice fastest).
+struct AbsorbTask {
+  int h, slice, group;
+};
+
+__device__ __forceinline__ AbsorbTask absorb_task(int L, int heads, int slices, int groups) {
+  (void)groups;
+  if ((heads & 7) == 0) {
+    const int x = L & 7, local = L >> 3;
+    const int per_head = slices * groups;
+    const int hh = local / per_head, rem = local - hh * per_head;
+    return AbsorbTask{8 * hh + x, rem % slices, rem / slices};
+  }
+  const int hs = heads * slices;
+  const int g = L / hs, r = L - g * hs;
+  return AbsorbTask{r / slices, r % slices, g};
+}
+
 // Copy a ROWS x COLS bf16 block (source row stride `stride` elements) into
 // LDS rows of COLS + 8: every load of the thread is issued before its first
 // LDS store.
@@ -76,8 +100,8 @@ __device__ __forceinline__ void stage(const uint16_t* src, size_t stride, uint16
   }
 }
 
-// q[b][h] = [q_nope[b][h] . W_UK[h], q_rope[b][h]]; blockIdx.x = h * (512 /
-// NS) + slice, blockIdx.y = group of 64 TW batch rows, TW 16-row tiles per
+// q[b][h] = [q_nope[b][h] . W_UK[h], q_rope[b][h]] for the (head, slice of NS
+// columns, group of 64 TW batch rows) of absorb_task, TW 16-row tiles per
 // wave. Slice 0 also copies the rope part of its rows.
 template <int NS, int TW>
 __global__ void __launch_bounds__(kAbsorbThreads) absorb_q_kernel(const uint16_t* x,
@@ -91,8 +115,10 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_q_kernel(const uint16_t
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cc = lane & 15, g = lane >> 4;
-  const int h = blockIdx.x / kSplit, n0 = (blockIdx.x % kSplit) * NS;
-  const int b0 = blockIdx.y * kRows;
+  const AbsorbTask task =
+      absorb_task(blockIdx.x, heads, kSplit, (batch + kRows - 1) / kRows);
+  const int h = task.h, n0 = task.slice * NS;
+  const int b0 = task.group * kRows;
   const int bt = b0 + 16 * TW * wave;  // this wave's first batch row
 
   // B operand: batch row bt + 16 t + cc, k = 32 s + 8 g .. + 7 (a row past
@@ -161,8 +187,8 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_q_kernel(const uint16_t
   }
 }
 
-// o[b][h] = o_latent[b][h] . W_UV[h]^T; blockIdx.x = h * (128 / NS) + slice
-// of NS value columns, blockIdx.y = 64-row batch group.
+// o[b][h] = o_latent[b][h] . W_UV[h]^T for the (head, slice of NS value
+// columns, 64-row batch group) of absorb_task.
 template <int NS>
 __global__ void __launch_bounds__(kAbsorbThreads) absorb_out_kernel(const uint16_t* x,
                                                                     const uint16_t* w,
@@ -174,8 +200,10 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_out_kernel(const uint16
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int cc = lane & 15, g = lane >> 4;
-  const int h = blockIdx.x / kSplit, n0 = (blockIdx.x % kSplit) * NS;
-  const int bt = blockIdx.y * kAbsorbRows + 16 * wave;
+  const AbsorbTask task =
+      absorb_task(blockIdx.x, heads, kSplit, (batch + kAbsorbRows - 1) / kAbsorbRows);
+  const int h = task.h, n0 = task.slice * NS;
+  const int bt = task.group * kAbsorbRows + 16 * wave;
 
   a_u32x4_t xf[K / 32];
   {
@@ -242,7 +270,7 @@ hipError_t launch_absorb_q(const uint16_t* q_nope, const uint16_t* w_uk, const u
     if (i == 0 || v < best_bytes) best = i, best_bytes = v;
   }
   const int ns = kShapes[best].ns, rows = kAbsorbRows * kShapes[best].tw;
-  const dim3 grid(unsigned(heads) * unsigned(kLatent / ns), unsigned((batch + rows - 1) / rows));
+  const dim3 grid(unsigned(heads) * unsigned(kLatent / ns) * unsigned((batch + rows - 1) / rows));
   const dim3 block(kAbsorbThreads);
   switch (best) {
     case 0:
@@ -271,10 +299,10 @@ hipError_t launch_absorb_out(const uint16_t* o_latent, const uint16_t* w_uv, uin
                              int32_t batch, int32_t heads, hipStream_t stream) {
   const unsigned groups = unsigned((batch + kAbsorbRows - 1) / kAbsorbRows);
   if (long(heads) * (kNope / 32) * groups >= 256)
-    hipLaunchKernelGGL(absorb_out_kernel<32>, dim3(unsigned(heads) * (kNope / 32), groups),
+    hipLaunchKernelGGL(absorb_out_kernel<32>, dim3(unsigned(heads) * (kNope / 32) * groups),
                        dim3(kAbsorbThreads), 0, stream, o_latent, w_uv, o, batch, heads);
   else
-    hipLaunchKernelGGL(absorb_out_kernel<16>, dim3(unsigned(heads) * (kNope / 16), groups),
+    hipLaunchKernelGGL(absorb_out_kernel<16>, dim3(unsigned(heads) * (kNope / 16) * groups),
                        dim3(kAbsorbThreads), 0, stream, o_latent, w_uv, o, batch, heads);
   return hipGetLastError();
 }
