@@ -229,9 +229,12 @@ def _peaks_lib():
     lib = ctypes.CDLL(hip_build.PEAKS_LIBRARY)
     vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
     lib.peaks_stream_lds.argtypes = [vp, i64, i32, i32, i32, vp]
+    lib.peaks_stream_perm.argtypes = [vp, i64, i64, i32, i32, vp]
+    lib.peaks_gather_rows.argtypes = [vp, i64, i32, i32, i32, vp]
     lib.peaks_read.argtypes = [vp, i64, i32, vp, vp]
     lib.peaks_mfma.argtypes = [i32, i32, i32, vp, vp]
-    for f in (lib.peaks_stream_lds, lib.peaks_read, lib.peaks_mfma):
+    for f in (lib.peaks_stream_lds, lib.peaks_stream_perm, lib.peaks_gather_rows, lib.peaks_read,
+              lib.peaks_mfma):
         f.restype = i32
     return lib
 
@@ -254,13 +257,22 @@ def _median_launch_us(torch, launch, reps: int) -> float:
 TILE_BYTES = 36864          # one ring stage of the attention kernels
 
 
+PATTERN_KERNELS = {
+    "tiles": "the same ring over 36 KB tiles in scattered order (a paged cache's blocks)",
+    "rows1152": "the same ring gathering single 1152-byte rows at hashed positions",
+    "rows576": "the same ring gathering single 576-byte rows at hashed positions",
+}
+
+
 def measure_peaks(torch, dev, which=("hbm", "bf16", "fp8"), full: bool = False,
-                  reps: int = 10) -> dict:
+                  reps: int = 10, patterns=()) -> dict:
     """What this GPU delivers, measured by libmla_peaks.so's calibration
     kernels (HBM: 2 GiB streamed through LDS as 36 KB direct-to-LDS tiles
     with the non-temporal bit, one workgroup per CU and two tiles in flight
-    as in the attention ring; matrix cores: dense loops of the bf16 16x16x32
-    and scaled E4M3 16x16x128 ops on every SIMD)."""
+    as in the attention ring; with `patterns` (or `full`) the same ring over
+    scattered tiles and over gathered single rows, the access patterns of the
+    paged and the sparse decode; matrix cores: dense loops of the bf16
+    16x16x32 and scaled E4M3 16x16x128 ops on every SIMD)."""
     import ctypes
     lib = _peaks_lib()
     h = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
@@ -289,6 +301,26 @@ def measure_peaks(torch, dev, which=("hbm", "bf16", "fp8"), full: bool = False,
             us = _median_launch_us(torch, launch_read, reps)
             res[f"read_grid{grid}"] = round(nbytes / (us * 1e-6) / 1e9, 1)
         res["hbm_GBps"] = res["stream_lds_grid256_inflight2_nt"]
+        grid = 256
+        per_wg = ntiles // grid
+        pattern_bytes = grid * per_wg * TILE_BYTES
+        for pat in (tuple(PATTERN_KERNELS) if full else tuple(patterns)):
+            if pat == "tiles":
+                stride = 7919                      # prime, coprime to the tile count
+                while math.gcd(stride, ntiles) != 1:
+                    stride += 2
+
+                def launch_pat(st=stride):
+                    assert lib.peaks_stream_perm(ctypes.c_void_p(buf.data_ptr()), ntiles, st, grid,
+                                                 per_wg, h) == 0
+            else:
+                row_bytes = int(pat[4:])
+
+                def launch_pat(rb=row_bytes):
+                    assert lib.peaks_gather_rows(ctypes.c_void_p(buf.data_ptr()), nbytes // rb, rb,
+                                                 grid, per_wg, h) == 0
+            us = _median_launch_us(torch, launch_pat, reps)
+            res[f"pattern_{pat}_GBps"] = round(pattern_bytes / (us * 1e-6) / 1e9, 1)
         del buf
     for name, fp8, iters, per_op in (("bf16", 0, 8192, 16384), ("fp8", 1, 4096, 65536)):
         if name not in which:
@@ -527,7 +559,9 @@ def main(argv=None) -> int:
         # timed calls. The matrix-core loops, which heat the chip, run after
         # the timed regions.
         log("measuring this GPU's HBM peak")
-        mp = measure_peaks(torch, dev, which=("hbm",), reps=150)
+        pattern = ("rows576" if wl.kv_dtype == "fp8" else "rows1152") if wl.indices is not None \
+            else "tiles"
+        mp = measure_peaks(torch, dev, which=("hbm",), reps=150, patterns=(pattern,))
     for i in range(args.warmup):
         call(i)
     torch.cuda.synchronize()
@@ -653,6 +687,12 @@ def main(argv=None) -> int:
             "2 GiB through LDS in 36 KB direct-to-LDS tiles, non-temporal, 256 workgroups, "
             "2 tiles in flight" if roofline["bound"] == "hbm" else
             f"dense {which[0]} matrix-op loop, 4 waves per SIMD")
+        pat_keys = [k for k in mp if k.startswith("pattern_")]
+        if roofline["bound"] == "hbm" and pat_keys:
+            pat = pat_keys[0][len("pattern_"):-len("_GBps")]
+            roofline["pattern_peak"] = mp[pat_keys[0]]
+            roofline["frac_of_pattern_peak"] = round(roofline["achieved"] / mp[pat_keys[0]], 4)
+            roofline["pattern_peak_kernel"] = PATTERN_KERNELS[pat]
     roofline.update({
         "traffic": traffic, "kernel": kernel_name,
         "kernel_us_avg": round(attn_avg * 1e3, 2),

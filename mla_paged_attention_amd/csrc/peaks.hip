@@ -1,7 +1,9 @@
 // peaks.hip -- calibration kernels that measure what this MI355X actually
 // delivers, as denominators beside the vendor peaks: HBM read bandwidth
 // (a direct-to-LDS stream of 36 KB tiles shaped like the attention kernels'
-// KV ring, and a plain vector read) and dense matrix-core throughput
+// KV ring, in order and in scattered order as a paged cache places its
+// blocks, a gather of single rows as sparse decode reads them, and a plain
+// vector read) and dense matrix-core throughput
 // (v_mfma_f32_16x16x32_bf16 and v_mfma_scale_f32_16x16x128_f8f6f4 in E4M3).
 // Measurement only: built into libmla_peaks.so, never into the decode
 // library. The caller times the launches with events on `stream`.
@@ -48,6 +50,71 @@ __global__ void __launch_bounds__(kStreamThreads) stream_lds_kernel(const uint8_
     ++issued;
   }
   wait_vmem<0>();
+}
+
+// The same ring over tiles in scattered order, as a paged cache reads its
+// blocks: workgroup w's k-th tile is tile ((w * per_wg + k) * stride) % ntiles
+// (stride coprime to ntiles, so every tile is read once), two tiles in
+// flight, non-temporal loads.
+__global__ void __launch_bounds__(kStreamThreads) stream_perm_kernel(const uint8_t* src,
+                                                                   int64_t ntiles, int64_t stride,
+                                                                   int per_wg) {
+  __shared__ uint8_t ring[kStages][kTileBytes];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  auto issue = [&](int k) {
+    const int64_t t = ((int64_t(blockIdx.x) * per_wg + k) * stride) % ntiles;
+    const uint8_t* base = src + t * kTileBytes + tid * 16;
+    uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i)
+      __builtin_amdgcn_global_load_lds(
+          base + i * kStreamThreads * 16,
+          (void __attribute__((address_space(3)))*)(dst + i * kStreamThreads * 16), 16, 0, 2);
+  };
+  issue(0);
+  if (per_wg > 1) issue(1);
+  for (int k = 0; k < per_wg; ++k) {
+    if (k + 1 < per_wg) wait_vmem<kLoadsPerTile>(); else wait_vmem<0>();
+    __syncthreads();
+    if (k + 2 < per_wg) issue(k + 2);
+  }
+}
+
+// Row gather, as sparse decode reads its listed tokens: every 36 KB tile is
+// 36864 / row_bytes rows taken from hashed positions among nrows rows of
+// row_bytes bytes, two tiles in flight, non-temporal loads.
+__global__ void __launch_bounds__(kStreamThreads) gather_rows_kernel(const uint8_t* src,
+                                                                   int64_t nrows, int row_bytes,
+                                                                   int per_wg) {
+  __shared__ uint8_t ring[kStages][kTileBytes];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int chunks = row_bytes / 16;
+  auto issue = [&](int k) {
+    uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
+#pragma unroll
+    for (int i = 0; i < kLoadsPerTile; ++i) {
+      const int pos = i * kStreamThreads + tid;
+      const int t = pos / chunks, ch = pos - (pos / chunks) * chunks;
+      uint32_t h = uint32_t(blockIdx.x) * 2654435761u ^ uint32_t(k) * 40503u ^
+                   uint32_t(t) * 2246822519u;
+      h ^= h >> 15;
+      h *= 2654435761u;
+      h ^= h >> 13;
+      const int64_t row = int64_t(h % uint64_t(nrows));
+      __builtin_amdgcn_global_load_lds(
+          src + row * row_bytes + ch * 16,
+          (void __attribute__((address_space(3)))*)(dst + i * kStreamThreads * 16), 16, 0, 2);
+    }
+  };
+  issue(0);
+  if (per_wg > 1) issue(1);
+  for (int k = 0; k < per_wg; ++k) {
+    if (k + 1 < per_wg) wait_vmem<kLoadsPerTile>(); else wait_vmem<0>();
+    __syncthreads();
+    if (k + 2 < per_wg) issue(k + 2);
+  }
 }
 
 // Plain read: 16-byte vector loads, eight in flight per thread, folded into
@@ -133,6 +200,32 @@ int peaks_stream_lds(const void* src, int64_t ntiles, int grid, int in_flight, i
     else if (in_flight == 2) hipLaunchKernelGGL((stream_lds_kernel<2, 0>), g, b, 0, s, p, ntiles);
     else hipLaunchKernelGGL((stream_lds_kernel<3, 0>), g, b, 0, s, p, ntiles);
   }
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Streams grid * per_wg 36,864-byte tiles of src in scattered order (tile k
+// of workgroup w is ((w * per_wg + k) * stride) % ntiles; grid * per_wg <=
+// ntiles; ntiles * 36864 bytes must lie in the buffer).
+int peaks_stream_perm(const void* src, int64_t ntiles, int64_t stride, int grid, int per_wg,
+                      void* stream) {
+  if (!src || ntiles <= 0 || stride <= 0 || grid <= 0 || per_wg <= 0 ||
+      int64_t(grid) * per_wg > ntiles)
+    return -1;
+  hipLaunchKernelGGL(stream_perm_kernel, dim3(grid), dim3(kStreamThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src), ntiles,
+                     stride, per_wg);
+  return hipGetLastError() == hipSuccess ? 0 : -2;
+}
+
+// Gathers grid * per_wg tiles of rows of row_bytes (1152 or 576) bytes from
+// hashed rows among the nrows rows of src (nrows * row_bytes bytes).
+int peaks_gather_rows(const void* src, int64_t nrows, int row_bytes, int grid, int per_wg,
+                      void* stream) {
+  if (!src || nrows <= 0 || (row_bytes != 1152 && row_bytes != 576) || grid <= 0 || per_wg <= 0)
+    return -1;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(kStreamThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint8_t*>(src), nrows,
+                     row_bytes, per_wg);
   return hipGetLastError() == hipSuccess ? 0 : -2;
 }
 

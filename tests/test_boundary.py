@@ -436,3 +436,14 @@ def test_bounds_check_build_matches_header():
                          capture_output=True, text=True, check=True).stdout
     exported = set(re.findall(r"\bT (mla_\w+)", out))
     assert set(declared_functions()) <= exported
+
+
+def test_peaks_library_exports_what_the_bench_binds():
+    # The calibration library is separate from the decode library; the bench
+    # binds these five entry points by name.
+    from mla_paged_attention_amd import build as hip_build
+    out = subprocess.run(["nm", "-D", "--defined-only", hip_build.PEAKS_LIBRARY],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (peaks_\w+)", out))
+    assert exported == {"peaks_stream_lds", "peaks_stream_perm", "peaks_gather_rows",
+                        "peaks_read", "peaks_mfma"}
