@@ -678,8 +678,18 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
       int P = (total + a.parts_cap - 1) / a.parts_cap;
       if (P < kMinPartUnits) P = kMinPartUnits;
       const int ub = cinc - cost + kOverheadUnits, ue = cinc;
-      const int first = ub / P;
-      const int k = live ? (ue - 1) / P - first + 1 : 0;
+      // Requests of equal length whose count divides the partitions: each is
+      // cut into S = partitions / batch equal pieces, one partition each, so
+      // that the cuts fall on request boundaries. (The cut at multiples of P
+      // would give most of them a third, small piece: one more partial row
+      // and one more piece start per workgroup.)
+      const int c0 = __builtin_amdgcn_readlane(cost, 0);
+      const int cv = live ? cost : c0;
+      const int S = a.parts_cap / a.batch;
+      const bool aligned = wave_max(cv) == -wave_max(-cv) && a.parts_cap % a.batch == 0 &&
+                           S >= 2 && c0 - kOverheadUnits >= S * kMinPartUnits;
+      const int first = aligned ? lane * S : ub / P;
+      const int k = live ? (aligned ? S : (ue - 1) / P - first + 1) : 0;
       const int nrows = k > 1 ? k : 0;
       const int rinc = wave_inclusive_scan(nrows);
       const int sinc = wave_inclusive_scan(k > 1 ? 1 : 0);
@@ -691,8 +701,8 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
         }
         if (lane == 0) {
           a.wr_row_ptr[a.batch] = __builtin_amdgcn_readlane(rinc, 63);
-          a.wr_header[0] = (total + P - 1) / P;
-          a.wr_header[1] = P;
+          a.wr_header[0] = aligned ? a.batch * S : (total + P - 1) / P;
+          a.wr_header[1] = aligned ? (c0 - kOverheadUnits + S - 1) / S : P;
           a.wr_header[2] = __builtin_amdgcn_readlane(sinc, 63);
           a.wr_header[3] = kPlanContiguous;
         }
@@ -702,8 +712,16 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
       if (mine) {
         const int idx = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32),
                                                   __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0));
-        const int p0 = max(ub, part * P), p1 = min(ue, (part + 1) * P);
-        s_items[idx] = make_int4(lane, p0 - ub, p1 - ub, k > 1 ? rinc - nrows + part - first : -1);
+        int u0, u1;
+        if (aligned) {
+          const int j = part - first;
+          u0 = int((long long)j * units / S);
+          u1 = int((long long)(j + 1) * units / S);
+        } else {
+          u0 = max(ub, part * P) - ub;
+          u1 = min(ue, (part + 1) * P) - ub;
+        }
+        s_items[idx] = make_int4(lane, u0, u1, k > 1 ? rinc - nrows + part - first : -1);
       }
       if (lane == 0) s_nitems = __popcll(m);
     }

@@ -66,6 +66,18 @@ def test_full_size(orc, name):
     _check(orc, wl, 0, what=f"{name} (whole batch)")
 
 
+@pytest.mark.parametrize("kv_dtype,num_heads,batch,length",
+                         [("bf16", 16, 8, 4096), ("bf16", 16, 64, 1000), ("bf16", 128, 4, 4111),
+                          ("fp8", 128, 2, 8192), ("fp8", 16, 32, 2048)])
+def test_equal_lengths_cut_on_request_boundaries(orc, kv_dtype, num_heads, batch, length):
+    # Equal requests whose count divides the partitions are each cut into
+    # equal pieces, one partition apiece (the automatic plan computed in the
+    # attention kernel); poisoned tails and unused blocks must not leak.
+    wl = workloads.make_workload(batch=batch, num_heads=num_heads, seq=("fixed", [length] * batch),
+                                 block_size=64, seed=300 + batch, kv_dtype=kv_dtype, poison=True)
+    _check(orc, wl, 0, what=f"equal {kv_dtype} H={num_heads} B={batch} N={length}")
+
+
 @pytest.mark.parametrize("num_splits", [0, 1, 5])
 def test_fp8_small(orc, num_splits):
     wl = workloads.make_workload(batch=5, num_heads=20, seq=("fixed", [1, 17, 100, 513, 2000]),
