@@ -3,6 +3,8 @@
 // host synchronisation, no exceptions across the boundary.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <math.h>
 #include <mutex>
 #include <string.h>
@@ -151,10 +153,12 @@ mla_status_t validate_decode(const DecodeArgs& a) {
   }
   if (a.batch == 0) return MLA_OK;
   {
-    // The split plan sums per-request costs (1 + 16-token units, at most the
-    // cap) in int32: the largest total, plus a partition of slack, must fit.
+    // The split plan sums per-request costs (overhead + 16-token units, at
+    // most the cap) in int32: the largest total, plus a partition of slack,
+    // must fit.
     const int64_t cap_tokens = a.topk > 0 ? a.topk : int64_t(a.max_blocks) * a.block_size;
-    const int64_t max_cost = mla::kOverheadUnits + (cap_tokens + mla::kUnit - 1) / mla::kUnit;
+    const int64_t max_cost = std::max(mla::kOverheadUnitsWs, mla::kOverheadUnitsMh) +
+                             (cap_tokens + mla::kUnit - 1) / mla::kUnit;
     if (int64_t(a.batch) * max_cost > INT32_MAX / 2) return MLA_ERR_INVALID_ARG;
   }
   if (!a.q || !a.kv_cache || !a.block_table || !a.seq_lens || !a.out)
@@ -239,6 +243,8 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
     w = layout(max_parts);
     if (w.total > a.workspace_bytes) return MLA_ERR_WORKSPACE_TOO_SMALL;
   }
+  const int32_t plan_ovh =
+      mla::plan_overhead_units(rows, a.kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0, sparse);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   int32_t* header = reinterpret_cast<int32_t*>(ws + w.header);
   int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + w.row_ptr);
@@ -289,7 +295,8 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
       inline_plan = mla::kInlineContiguousWide;
   }
   if (inline_plan == mla::kInlineNone && a.num_splits == 0 &&
-      mla::launch_plan(lens, a.batch, int32_t(cap), int32_t(max_parts), w, a.workspace, s) !=
+      mla::launch_plan(lens, a.batch, int32_t(cap), int32_t(max_parts), plan_ovh, w, a.workspace,
+                       s) !=
           hipSuccess)
     return MLA_ERR_HIP;
   if (!rec(1)) return MLA_ERR_HIP;
@@ -331,6 +338,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   args.wr_split = split;
   args.wr_header = header;
   args.err_word = err_word;
+  args.plan_ovh = plan_ovh;
   int64_t parts = a.num_splits > 0 ? int64_t(a.batch) * a.num_splits : max_parts;
   int64_t parts_launched = (parts + 7) / 8 * 8;
   if (parts_launched * args.head_tiles > INT32_MAX) return MLA_ERR_INVALID_ARG;

@@ -25,7 +25,13 @@ constexpr int kUnit = 16;       // tokens per scheduling unit = MFMA tile rows
 constexpr int kHeadTile = 16;   // heads per workgroup (MFMA tile columns)
 constexpr int kWaves = 4;       // waves per attention workgroup
 constexpr int kThreads = 64 * kWaves;
-constexpr int kOverheadUnits = 1;   // per-request fixed cost in the balanced plan
+// Per-request fixed cost of the balanced plan, in 16-token units: what
+// starting a piece costs the attention kernel (the first tile's latency, q,
+// the epilogue). Chosen by measurement, per kernel: the value that balanced
+// the partitions best (v2lite-64 for the 16-head kernel, fullhead for the
+// many-head kernel; 1, 4, 6, 8, 12 and 16 were tried).
+constexpr int kOverheadUnitsWs = 8;
+constexpr int kOverheadUnitsMh = 16;
 constexpr int kMinPartUnits = 8;    // smallest partition (128 tokens): fewer, cheaper merges
 constexpr int kPlanThreads = 1024;
 constexpr int kPlanThreadsSmall = 256;
@@ -96,6 +102,16 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
 
 inline int head_tiles(int num_heads) { return (num_heads + kHeadTile - 1) / kHeadTile; }
 
+// The attention kernel a call runs (launch_attention): the 16-head bf16
+// kernel for one head tile of a dense bf16 cache, the many-head kernel
+// otherwise. Its per-piece cost sets the plan's overhead units.
+inline bool uses_16_head_kernel(int rows, int kv_fp8, bool sparse) {
+  return !sparse && !kv_fp8 && head_tiles(rows) == 1;
+}
+inline int plan_overhead_units(int rows, int kv_fp8, bool sparse) {
+  return uses_16_head_kernel(rows, kv_fp8, sparse) ? kOverheadUnitsWs : kOverheadUnitsMh;
+}
+
 // Workgroups per partition: the many-head kernels (and the E4M3 kernel) put
 // four 16-head tiles in one workgroup; the 16-head bf16 kernel uses one.
 inline int workgroups_per_partition(int num_heads, int kv_fp8) {
@@ -159,6 +175,8 @@ struct AttnArgs {
   int32_t* wr_header;
   // Bounds-check build: the error word (null otherwise).
   int32_t* err_word;
+  // Per-request fixed cost of the automatic plan, in units (plan_overhead_units).
+  int32_t plan_ovh;
 };
 
 constexpr int kInlinePlanBatch = 64;  // one request per lane of a wave
@@ -175,7 +193,7 @@ constexpr int kInlineContigBatch = 4096;
 // Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
 // only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
-                       int32_t max_parts, const WorkspaceLayout& w, void* workspace,
+                       int32_t max_parts, int32_t ovh, const WorkspaceLayout& w, void* workspace,
                        hipStream_t stream);
 
 // kv_fp8: 0 = bf16 cache, 1 = E4M3 cache. `parts_launched` is a multiple of 8.

@@ -230,7 +230,7 @@ __device__ int block_scan_lds(int* s, int n, int* s_wave) {
 //    equal partitions; a request straddling a cut becomes several pieces.
 template <int NT>
 __global__ void __launch_bounds__(NT) plan_kernel(
-    const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t max_parts,
+    const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t max_parts, int32_t ovh,
     int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr, int4* work,
     int32_t* split) {
   __shared__ int s_wave[48];
@@ -246,7 +246,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
     for (int i = 0; i < 4; ++i) {
       const int b = 4 * tid + i;
       units[i] = b < batch ? units_of(clamp_len(seq_lens[b], cap_tokens)) : 0;
-      cost[i] = b < batch ? kOverheadUnits + units[i] : 0;
+      cost[i] = b < batch ? ovh + units[i] : 0;
       c0[i] = csum;
       csum += cost[i];
       cmax = max(cmax, cost[i]);
@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
       const int b = 4 * tid + i;
       if (b < batch) {
         k[i] = snake ? (cost[i] > P ? (cost[i] + P - 1) / P : 1)
-                     : (c0[i] + cost[i] - 1) / P - (c0[i] + kOverheadUnits) / P + 1;
+                     : (c0[i] + cost[i] - 1) / P - (c0[i] + ovh) / P + 1;
       } else {
         k[i] = 0;
       }
@@ -294,7 +294,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
         row_ptr[b] = rb;
         if (k[i] > 1) split[sb++] = b;
         if (!snake) {
-          const int ub = c0[i] + kOverheadUnits, ue = c0[i] + cost[i];
+          const int ub = c0[i] + ovh, ue = c0[i] + cost[i];
           const int first = ub / P;
           for (int j = 0; j < k[i]; ++j) {
             const int q = first + j;
@@ -305,8 +305,8 @@ __global__ void __launch_bounds__(NT) plan_kernel(
         } else {
           // Piece lengths: q + 1 (first r pieces) and q.
           const int q = units[i] / k[i], r = units[i] - q * k[i];
-          if (r > 0) atomicAdd(&s_bucket[(kOverheadUnits + q + 1) >> shift], r);
-          if (k[i] > r) atomicAdd(&s_bucket[(kOverheadUnits + q) >> shift], k[i] - r);
+          if (r > 0) atomicAdd(&s_bucket[(ovh + q + 1) >> shift], r);
+          if (k[i] > r) atomicAdd(&s_bucket[(ovh + q) >> shift], k[i] - r);
         }
       }
       ib += k[i];
@@ -337,7 +337,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
         const int q = units[i] / k[i], r = units[i] - q * k[i];
         for (int j = 0; j < k[i]; ++j) {
           const int len = q + (j < r ? 1 : 0);
-          const int rank = atomicAdd(&s_bucket[(kOverheadUnits + len) >> shift], 1);
+          const int rank = atomicAdd(&s_bucket[(ovh + len) >> shift], 1);
           const int round = rank / parts, pos = rank - round * parts;
           const int q = (round & 1) ? parts - 1 - pos : pos;
           s_pq[ibase[i] + j] = short(q);
@@ -373,7 +373,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
   // Large batches: contiguous plan over the requests in chunks of
   // NT (costs re-read per pass).
   auto cost_of = [&](int b) {
-    return kOverheadUnits + units_of(clamp_len(seq_lens[b], cap_tokens));
+    return ovh + units_of(clamp_len(seq_lens[b], cap_tokens));
   };
   int carry = 0;
   for (int base = 0; base < batch; base += NT) {
@@ -397,7 +397,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
     if (b < batch) {
       cost = cost_of(b);
       c0 = cum[b];
-      k = (c0 + cost - 1) / P - (c0 + kOverheadUnits) / P + 1;
+      k = (c0 + cost - 1) / P - (c0 + ovh) / P + 1;
     }
     int3 tot3;
     const int3 ex3 = block_exclusive_scan3<NT>(make_int3(k, k > 1 ? k : 0, k > 1 ? 1 : 0), s_wave,
@@ -406,7 +406,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
       const int ibase = carry3.x + ex3.x, rbase = carry3.y + ex3.y;
       row_ptr[b] = rbase;
       if (k > 1) split[carry3.z + ex3.z] = b;
-      const int ub = c0 + kOverheadUnits, ue = c0 + cost;
+      const int ub = c0 + ovh, ue = c0 + cost;
       const int first = ub / P;
       for (int j = 0; j < k; ++j) {
         const int q = first + j;
@@ -444,6 +444,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
 template <int NT>
 __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* items,
                                   int* n_items) {
+  const int ovh = a.plan_ovh;
   __shared__ int s_wave[48];
   constexpr int kMaxPieces = kInlineSnakeBatch + kMaxPlanParts;
   const int tid = threadIdx.x;
@@ -462,8 +463,8 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
   for (int b = tid; b < B; b += NT) {
     const int u = units_of(clamp_len(a.seq_lens[b], a.cap_tokens));
     units[b] = u;
-    csum += kOverheadUnits + u;
-    cmax = max(cmax, kOverheadUnits + u);
+    csum += ovh + u;
+    cmax = max(cmax, ovh + u);
   }
   int tot;
   (void)block_exclusive_scan<NT>(csum, s_wave, &tot);
@@ -476,7 +477,7 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
   const int b0 = min(B, tid * C), b1 = min(B, b0 + C);
   int3 mine = make_int3(0, 0, 0);
   for (int b = b0; b < b1; ++b) {
-    const int cost = kOverheadUnits + units[b];
+    const int cost = ovh + units[b];
     const int k = cost > P ? (cost + P - 1) / P : 1;
     kb[b] = k;
     mine.x += k;
@@ -497,7 +498,7 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
     const int q = units[b] / k, r = units[b] - q * k;
     for (int j = 0; j < k; ++j) {
       const int len = q + (j < r ? 1 : 0);
-      keyA[ex3.x + j] = 255 - min(255, (kOverheadUnits + len) >> shift);
+      keyA[ex3.x + j] = 255 - min(255, (ovh + len) >> shift);
       idxA[ex3.x + j] = ex3.x + j;
       preq[ex3.x + j] = b;
     }
@@ -578,6 +579,7 @@ struct ContigWalk {
 
 template <int NT>
 __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, ContigWalk* walk) {
+  const int ovh = a.plan_ovh;
   __shared__ int s_wave[48];
   const int tid = threadIdx.x;
   const int B = a.batch;
@@ -586,7 +588,7 @@ __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, Co
   const int b0 = min(B, tid * C), b1 = min(B, b0 + C);
   int csum = 0;
   for (int b = b0; b < b1; ++b) {
-    cost[b] = kOverheadUnits + units_of(clamp_len(a.seq_lens[b], a.cap_tokens));
+    cost[b] = ovh + units_of(clamp_len(a.seq_lens[b], a.cap_tokens));
     csum += cost[b];
   }
   int total;
@@ -598,7 +600,7 @@ __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, Co
   int c0 = cex;
   int3 mine = make_int3(0, 0, 0);
   for (int b = b0; b < b1; ++b) {
-    const int ub = c0 + kOverheadUnits, ue = c0 + cost[b];
+    const int ub = c0 + ovh, ue = c0 + cost[b];
     const int k = (ue - 1) / P - ub / P + 1;
     mine.y += k > 1 ? k : 0;
     mine.z += k > 1 ? 1 : 0;
@@ -610,7 +612,7 @@ __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, Co
   int rb = ex3.y, sb = ex3.z;
   const int lo = part * P;
   for (int b = b0; b < b1; ++b) {
-    const int ub = c0 + kOverheadUnits, ue = c0 + cost[b];
+    const int ub = c0 + ovh, ue = c0 + cost[b];
     const int k = (ue - 1) / P - ub / P + 1;
     // The first request reaching into this partition starts the walk.
     if (part < parts && ue > lo && c0 <= lo) *walk = ContigWalk{b, c0, rb, P, parts};
@@ -639,6 +641,7 @@ __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, Co
 template <int NT, typename Fn>
 __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int* scratch,
                                                Fn&& fn) {
+  const int ovh = a.plan_ovh;
   // The item list of the four modes, then one loop with the only call of
   // fn (the whole attention body is inlined there).
   __shared__ int4 s_items[kInlinePlanBatch];
@@ -672,12 +675,12 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
       const int lane = threadIdx.x;
       const bool live = lane < a.batch;
       const int units = live ? units_of(clamp_len(a.seq_lens[lane], a.cap_tokens)) : 0;
-      const int cost = live ? kOverheadUnits + units : 0;
+      const int cost = live ? ovh + units : 0;
       const int cinc = wave_inclusive_scan(cost);
       const int total = __builtin_amdgcn_readlane(cinc, 63);
       int P = (total + a.parts_cap - 1) / a.parts_cap;
       if (P < kMinPartUnits) P = kMinPartUnits;
-      const int ub = cinc - cost + kOverheadUnits, ue = cinc;
+      const int ub = cinc - cost + ovh, ue = cinc;
       // Requests of equal length whose count divides the partitions: each is
       // cut into S = partitions / batch equal pieces, one partition each, so
       // that the cuts fall on request boundaries. (The cut at multiples of P
@@ -687,7 +690,7 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
       const int cv = live ? cost : c0;
       const int S = a.parts_cap / a.batch;
       const bool aligned = wave_max(cv) == -wave_max(-cv) && a.parts_cap % a.batch == 0 &&
-                           S >= 2 && c0 - kOverheadUnits >= S * kMinPartUnits;
+                           S >= 2 && c0 - ovh >= S * kMinPartUnits;
       const int first = aligned ? lane * S : ub / P;
       const int k = live ? (aligned ? S : (ue - 1) / P - first + 1) : 0;
       const int nrows = k > 1 ? k : 0;
@@ -702,7 +705,7 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
         if (lane == 0) {
           a.wr_row_ptr[a.batch] = __builtin_amdgcn_readlane(rinc, 63);
           a.wr_header[0] = aligned ? a.batch * S : (total + P - 1) / P;
-          a.wr_header[1] = aligned ? (c0 - kOverheadUnits + S - 1) / S : P;
+          a.wr_header[1] = aligned ? (c0 - ovh + S - 1) / S : P;
           a.wr_header[2] = __builtin_amdgcn_readlane(sinc, 63);
           a.wr_header[3] = kPlanContiguous;
         }
@@ -735,9 +738,9 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
     int b, u0, u1, row;
     if (walk) {
       const int lo = part * wP, hi = lo + wP;
-      const int ub = wcum + kOverheadUnits;
+      const int ub = wcum + ovh;
       if (wb >= a.batch || ub >= hi) break;
-      const int ue = wcum + kOverheadUnits +
+      const int ue = wcum + ovh +
                      units_of(clamp_len(scalar_load_i32(a.seq_lens + wb), a.cap_tokens));
       const int first = ub / wP;
       const int k = (ue - 1) / wP - first + 1;
@@ -2115,14 +2118,14 @@ __global__ void __launch_bounds__(256) combine_split_kernel(
 // Host-side launchers.
 
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
-                       int32_t max_parts, const WorkspaceLayout& w, void* workspace,
+                       int32_t max_parts, int32_t ovh, const WorkspaceLayout& w, void* workspace,
                        hipStream_t stream) {
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   // Small batches and partition counts: a quarter of the threads (cheaper barriers).
   const bool small = batch <= 4 * kPlanThreadsSmall && max_parts < 4 * kPlanThreadsSmall;
   auto kern = small ? plan_kernel<kPlanThreadsSmall> : plan_kernel<kPlanThreads>;
   hipLaunchKernelGGL(kern, dim3(1), dim3(small ? kPlanThreadsSmall : kPlanThreads), 0, stream,
-                     seq_lens, batch, cap_tokens, max_parts,
+                     seq_lens, batch, cap_tokens, max_parts, ovh,
                      reinterpret_cast<int32_t*>(ws + w.header), reinterpret_cast<int32_t*>(ws + w.cum),
                      reinterpret_cast<int32_t*>(ws + w.row_ptr),
                      reinterpret_cast<int32_t*>(ws + w.part_ptr),
@@ -2141,7 +2144,7 @@ hipError_t launch_attention(const AttnArgs& args, int kv_fp8, int32_t parts_laun
       hipLaunchKernelGGL((attn_mh_kernel<0, 1>), grid_mh, dim3(kMhThreads), 0, stream, args);
   } else if (kv_fp8) {
     hipLaunchKernelGGL((attn_mh_kernel<1, 0>), grid_mh, dim3(kMhThreads), 0, stream, args);
-  } else if (args.head_tiles == 1) {
+  } else if (uses_16_head_kernel(args.rows, kv_fp8, false)) {
     hipLaunchKernelGGL(attn_ws_kernel, grid, dim3(kWsThreads), 0, stream, args);
   } else {
     hipLaunchKernelGGL((attn_mh_kernel<0, 0>), grid_mh, dim3(kMhThreads), 0, stream, args);

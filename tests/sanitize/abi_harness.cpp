@@ -14,7 +14,8 @@
 static int g_launches = 0;
 
 namespace mla {
-hipError_t launch_plan(const int32_t*, int32_t, int32_t, int32_t, const WorkspaceLayout&, void*,
+hipError_t launch_plan(const int32_t*, int32_t, int32_t, int32_t, int32_t, const WorkspaceLayout&,
+                       void*,
                        hipStream_t) { ++g_launches; return hipErrorUnknown; }
 hipError_t launch_attention(const AttnArgs&, int, int32_t, hipStream_t) {
   ++g_launches; return hipErrorUnknown;
