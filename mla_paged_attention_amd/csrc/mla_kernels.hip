@@ -1968,21 +1968,28 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
       }
       wave_barrier_lds();  // lbuf complete
       const float out_scale = KV_FP8 ? a.kv_scale * (1.f / 256.f) : 1.f;
+      // The output rows' addresses are formed here from values the compiler
+      // cannot see through, not hoisted to the kernel start (where sixteen
+      // per-lane 64-bit head offsets would stay live across the step loops
+      // and spill).
+      int row_base = final_out ? b : row;
+      int ge = g, ce = c;
+      asm volatile("" : "+s"(row_base), "+v"(ge), "+v"(ce));
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int hh = 4 * g + r;
+          const int hh = 4 * ge + r;
           const int h = (ht0 + t) * kHeadTile + hh;
           const float lh = lbuf[t][hh];
           const float inv = lh > 0.f ? out_scale / lh : 0.f;
           if (h < H) {
             if (final_out) {
-              uint16_t* dst = a.out + (size_t(b) * H + h) * kDV + 128 * wq + c;
+              uint16_t* dst = a.out + (size_t(row_base) * H + h) * kDV + 128 * wq + ce;
 #pragma unroll
               for (int j = 0; j < 8; ++j) dst[16 * j] = bf16_bits(acc[t][j][r] * inv);
             } else {
-              float* dst = a.part_out + (size_t(row) * H + h) * kDV + 128 * wq + c;
+              float* dst = a.part_out + (size_t(row_base) * H + h) * kDV + 128 * wq + ce;
 #pragma unroll
               for (int j = 0; j < 8; ++j) dst[16 * j] = acc[t][j][r] * inv;
             }
