@@ -974,8 +974,15 @@ __global__ void __launch_bounds__(kWsThreads, 1) attn_ws_kernel(AttnArgs a) {
     auto issue_tile = [&](int k) {
       int nv[2];
       tile_nv(k, nv);
+      // A second unit in the same page continues the first unit's rows:
+      // no second block-table lookup (a scalar-load round trip).
+      const int t0 = (u0 + 2 * k) * kUnit;
       const uint8_t* r0 = unit_rows(u0 + 2 * k, true);
-      const uint8_t* r1 = nv[1] > 0 ? unit_rows(u0 + 2 * k + 1, true) : r0;
+      const uint8_t* r1 = r0;
+      if (nv[1] > 0)
+        r1 = ((t0 + kUnit) >> a.bs_log2) == (t0 >> a.bs_log2)
+                 ? r0 + kUnit * kRowBytes
+                 : unit_rows(u0 + 2 * k + 1, true);
       uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
 #pragma unroll
       for (int i = 0; i < kDmaPerThread; ++i) {
@@ -1510,8 +1517,15 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
       const int uk = u0 + kUnits * k;
       const uint8_t* r[4];
       r[0] = unit_rows(uk);
+      // Units in the page of the unit before continue its rows: one
+      // block-table lookup (a scalar-load round trip) per page, not per unit.
 #pragma unroll
-      for (int u = 1; u < 4; ++u) r[u] = (u < kUnits && uk + u < u_end) ? unit_rows(uk + u) : r[0];
+      for (int u = 1; u < 4; ++u) {
+        const int tu = (uk + u) * kUnit;
+        r[u] = !(u < kUnits && uk + u < u_end)           ? r[0]
+               : (tu >> a.bs_log2) == ((tu - kUnit) >> a.bs_log2) ? r[u - 1] + kUnit * kRowB
+                                                                  : unit_rows(uk + u);
+      }
       uint8_t* dst = &ring[k % kStages][0] + wave * 64 * 16;
 #pragma unroll
       for (int i = 0; i < kDmaPerThread; ++i) {
