@@ -398,7 +398,11 @@ def bench_gemm(torch, mla, workloads, dev, m: int, n: int, k: int, steps: int, w
     else:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS,
                 "unit": "GB/s", "frac": round(gbps / PEAK_HBM_GBPS, 4)}
-    roof.update({"kernel": "mla::gemm_fp8_kernel", "algorithmic_bytes_per_launch": alg_bytes,
+    if m <= 16 and k <= 8192:
+        kname = f"mla::gemm_fp8_lds_kernel<{4 if m <= 4 else 0}>"
+    else:
+        kname = "mla::gemm_fp8_kernel"
+    roof.update({"kernel": kname, "algorithmic_bytes_per_launch": alg_bytes,
                  "algorithmic_flops_per_launch": flops, "traffic": None})
     print(json.dumps({
         "metric": "block-fp8 projection us/call at decode batch", "value": round(avg, 2),

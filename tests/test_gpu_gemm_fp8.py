@@ -47,7 +47,9 @@ def check_gemm(orc, m, n, k, seed, rows=None):
 
 @pytest.mark.parametrize("m,n,k", [(1, 2112, 7168), (4, 2112, 7168), (16, 576, 7168),
                                    (17, 576, 1024), (33, 16, 128), (64, 2112, 2048),
-                                   (100, 576, 1152), (2, 48, 384)])
+                                   (100, 576, 1152), (2, 48, 384), (1, 16, 128),
+                                   (3, 32, 16384), (16, 2112, 9088), (4, 32, 8192),
+                                   (5, 64, 8192)])
 def test_gemm_matches_oracle(orc, m, n, k):
     check_gemm(orc, m, n, k, seed=m + n + k)
 
