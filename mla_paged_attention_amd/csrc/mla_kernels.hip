@@ -2016,124 +2016,144 @@ __global__ void __launch_bounds__(kMhThreads, 1) attn_mh_kernel(AttnArgs a) {
 
 // ----------------------------------------------------------------------------
 // LSE combine: one workgroup per (request, 16-head tile, feature chunk);
-// thread (head hh, sub) merges kCombineF features of the chunk from
-// kCombineUnroll partial rows in flight.
-constexpr int kCombineF = 8;                          // features per thread
-constexpr int kCombineChunk = 16 * kCombineF;         // features per workgroup
-constexpr int kCombineChunks = kDV / kCombineChunk;
-constexpr int kCombineUnroll = 64 / kCombineF;        // rows per batch of loads
+// thread (head hh, sub) merges F features of the chunk from 64 / F partial
+// rows in flight. F = 8 (four 128-feature chunks per head tile) when there
+// are many (request, tile) pairs; fewer features per thread, and so more
+// workgroups, when there are few: each workgroup then reads a smaller share
+// of a request's rows, which bounds small batches (a request split into many
+// pieces at batch 8 gives 32 workgroups at F = 8, 128 at F = 2).
 constexpr int kCombineGrid = 1 << 30;  // no cap: one workgroup per (request, tile, chunk)
 
+template <int F>
+__device__ __forceinline__ void load_features(const float* src, float (&v)[F]) {
+  if constexpr (F == 2) {
+    const f32x2_t x = *reinterpret_cast<const f32x2_t*>(src);
+    v[0] = x[0];
+    v[1] = x[1];
+  } else {
+#pragma unroll
+    for (int i = 0; i < F / 4; ++i) {
+      const f32x4_t x = reinterpret_cast<const f32x4_t*>(src)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * i + e] = x[e];
+    }
+  }
+}
+
 // Merge rows r0 .. r0 + nr - 1 of request b for head tile ht and feature
-// chunk `chunk`: thread (head tid / 16, features kCombineF (tid % 16) ..) of 256.
+// chunk `chunk` (16 F features): thread (head tid / 16, features F (tid % 16)
+// ..) of 256.
+template <int F>
 __device__ __forceinline__ void combine_rows(const float* part_out, const float* part_lse, int r0,
                                              int nr, uint16_t* out, float* lse, int b, int H,
                                              int ht, int chunk) {
-  constexpr int V = kCombineF / 4;
+  constexpr int U = 64 / F;  // rows per batch of loads
   const int tid = threadIdx.x;
   const int h = ht * kHeadTile + (tid >> 4);
   if (h >= H) return;
-  const int d = chunk * kCombineChunk + kCombineF * (tid & 15);
-  // One pass with a running maximum, kCombineUnroll rows in flight:
-  // acc and W are kept relative to M and rescaled when M rises.
+  const int d = chunk * 16 * F + F * (tid & 15);
+  // One pass with a running maximum, U rows in flight: acc and W are kept
+  // relative to M and rescaled when M rises.
   float M = -INFINITY;
-  f32x4_t acc[V];
+  float acc[F];
 #pragma unroll
-  for (int i = 0; i < V; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < F; ++i) acc[i] = 0.f;
   float W = 0.f;
-  for (int s0 = 0; s0 < nr; s0 += kCombineUnroll) {
+  for (int s0 = 0; s0 < nr; s0 += U) {
     // Rows past the request's last are not loaded (the count is uniform
     // across the workgroup, so the skipped loads are branched over).
-    const int cnt = min(nr - s0, kCombineUnroll);
-    f32x4_t v[kCombineUnroll][V];
-    float ls[kCombineUnroll];
+    const int cnt = min(nr - s0, U);
+    float v[U][F];
+    float ls[U];
 #pragma unroll
-    for (int k = 0; k < kCombineUnroll; ++k) {
+    for (int k = 0; k < U; ++k) {
       if (k < cnt) {
         ls[k] = part_lse[size_t(r0 + s0 + k) * H + h];
-        const f32x4_t* src =
-            reinterpret_cast<const f32x4_t*>(part_out + (size_t(r0 + s0 + k) * H + h) * kDV + d);
-#pragma unroll
-        for (int i = 0; i < V; ++i) v[k][i] = src[i];
+        load_features<F>(part_out + (size_t(r0 + s0 + k) * H + h) * kDV + d, v[k]);
       } else {
         ls[k] = -INFINITY;
 #pragma unroll
-        for (int i = 0; i < V; ++i) v[k][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < F; ++i) v[k][i] = 0.f;
       }
     }
     float mb = ls[0];
 #pragma unroll
-    for (int k = 1; k < kCombineUnroll; ++k) mb = fmaxf(mb, ls[k]);
+    for (int k = 1; k < U; ++k) mb = fmaxf(mb, ls[k]);
     if (mb == -INFINITY) continue;  // only empty rows in this batch
     const float Mn = fmaxf(M, mb);
     const float a = M == -INFINITY ? 0.f : fast_exp2((M - Mn) * kLog2e);
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] *= a;
+    for (int i = 0; i < F; ++i) acc[i] *= a;
     W *= a;
     M = Mn;
 #pragma unroll
-    for (int k = 0; k < kCombineUnroll; ++k) {
+    for (int k = 0; k < U; ++k) {
       const float w = ls[k] != -INFINITY ? fast_exp2((ls[k] - M) * kLog2e) : 0.f;
       if (w != 0.f) {  // an empty row's values are never used
 #pragma unroll
-        for (int i = 0; i < V; ++i) acc[i] += w * v[k][i];
+        for (int i = 0; i < F; ++i) acc[i] += w * v[k][i];
       }
       W += w;
     }
   }
   const float inv = W > 0.f ? 1.f / W : 0.f;
-  u32x2_t pk[V];
+  unsigned pk[F / 2];
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    const f32x4_t o = acc[i] * inv;
-    pk[i][0] = unsigned(bf16_bits(o[0])) | (unsigned(bf16_bits(o[1])) << 16);
-    pk[i][1] = unsigned(bf16_bits(o[2])) | (unsigned(bf16_bits(o[3])) << 16);
-  }
+  for (int i = 0; i < F / 2; ++i)
+    pk[i] = unsigned(bf16_bits(acc[2 * i] * inv)) | (unsigned(bf16_bits(acc[2 * i + 1] * inv)) << 16);
   uint16_t* dst = out + (size_t(b) * H + h) * kDV + d;
-  if constexpr (V == 2) {
-    *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0][0], pk[0][1], pk[1][0], pk[1][1]};
+  if constexpr (F == 8) {
+    *reinterpret_cast<u32x4_t*>(dst) = u32x4_t{pk[0], pk[1], pk[2], pk[3]};
+  } else if constexpr (F == 4) {
+    *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{pk[0], pk[1]};
   } else {
-#pragma unroll
-    for (int i = 0; i < V; ++i) *reinterpret_cast<u32x2_t*>(dst + 4 * i) = pk[i];
+    *reinterpret_cast<unsigned*>(dst) = pk[0];
   }
   if (chunk == 0 && (tid & 15) == 0 && lse) lse[size_t(b) * H + h] = W > 0.f ? M + __logf(W) : -INFINITY;
 }
 
 // Rows of request b: row_ptr[b] .. row_ptr[b + 1] - 1, or with uniform > 0
 // (forced splits, no plan launched) b * uniform .. b * uniform + uniform - 1.
+template <int F>
 __global__ void __launch_bounds__(256) combine_kernel(const float* part_out, const float* part_lse,
                                                       const int32_t* row_ptr, uint16_t* out,
                                                       float* lse, int32_t batch, int32_t H,
                                                       int32_t tiles, int zero_empty,
                                                       int32_t uniform) {
+  constexpr int kChunks = kDV / (16 * F);
   const int blk = blockIdx.x;
-  const int chunk = blk % kCombineChunks;
-  const int bt = blk / kCombineChunks;
+  const int chunk = blk % kChunks;
+  const int bt = blk / kChunks;
   const int b = bt / tiles, ht = bt - (bt / tiles) * tiles;
   const int r0 = uniform > 0 ? b * uniform : row_ptr[b];
   const int nr = uniform > 0 ? uniform : row_ptr[b + 1] - r0;
   if (nr <= 0 && !zero_empty) return;
-  combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+  combine_rows<F>(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
 }
 
 // The automatic plan's combine: block k merges request split[k] (header[2]
 // such requests); the rest exit at once.
+template <int F>
 __global__ void __launch_bounds__(256) combine_split_kernel(
     const float* part_out, const float* part_lse, const int32_t* row_ptr, const int32_t* split,
     const int32_t* header, uint16_t* out, float* lse, int32_t H, int32_t tiles) {
   // Grid-stride over (split request, head tile, chunk): a plan without
   // split requests costs one small launch.
-  const int per = tiles * kCombineChunks;
+  constexpr int kChunks = kDV / (16 * F);
+  const int per = tiles * kChunks;
   const int n = header[2] * per;
   for (int w = blockIdx.x; w < n; w += gridDim.x) {
     const int k = w / per;
     const int rest = w - k * per;
     const int b = split[k];
-    const int chunk = rest % kCombineChunks, ht = rest / kCombineChunks;
+    const int chunk = rest % kChunks, ht = rest / kChunks;
     const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
-    combine_rows(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+    combine_rows<F>(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
   }
 }
+
+// Features per combine thread for `pairs` (request, head tile) pairs.
+int combine_features(int64_t pairs) { return pairs >= 128 ? 8 : pairs >= 32 ? 4 : 2; }
 
 // ----------------------------------------------------------------------------
 // Host-side launchers.
@@ -2225,9 +2245,17 @@ hipError_t launch_combine(const float* part_out, const float* part_lse,
                           int32_t num_heads, int zero_empty, int32_t uniform,
                           hipStream_t stream) {
   const int tiles = head_tiles(num_heads);
-  hipLaunchKernelGGL(combine_kernel, dim3(unsigned(batch) * unsigned(tiles) * kCombineChunks),
-                     dim3(256), 0, stream, part_out, part_lse, row_ptr, out, lse, batch,
-                     num_heads, tiles, zero_empty, uniform);
+  const int64_t pairs = int64_t(batch) * tiles;
+  auto go = [&](auto kern, int f) {
+    hipLaunchKernelGGL(kern, dim3(unsigned(pairs * (kDV / (16 * f)))), dim3(256), 0, stream,
+                       part_out, part_lse, row_ptr, out, lse, batch, num_heads, tiles, zero_empty,
+                       uniform);
+  };
+  switch (combine_features(pairs)) {
+    case 8: go(combine_kernel<8>, 8); break;
+    case 4: go(combine_kernel<4>, 4); break;
+    default: go(combine_kernel<2>, 2); break;
+  }
   return hipGetLastError();
 }
 
@@ -2237,10 +2265,18 @@ hipError_t launch_combine_split(const float* part_out, const float* part_lse,
                                 int32_t max_split, int32_t num_heads, hipStream_t stream) {
   const int tiles = head_tiles(num_heads);
   if (max_split <= 0) return hipSuccess;
-  const int64_t tuples = int64_t(max_split) * tiles * kCombineChunks;
-  const unsigned grid = unsigned(tuples < kCombineGrid ? tuples : kCombineGrid);
-  hipLaunchKernelGGL(combine_split_kernel, dim3(grid), dim3(256), 0, stream, part_out, part_lse,
-                     row_ptr, split, header, out, lse, num_heads, tiles);
+  const int64_t pairs = int64_t(max_split) * tiles;
+  auto go = [&](auto kern, int f) {
+    const int64_t tuples = pairs * (kDV / (16 * f));
+    const unsigned grid = unsigned(tuples < kCombineGrid ? tuples : kCombineGrid);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, part_out, part_lse, row_ptr, split,
+                       header, out, lse, num_heads, tiles);
+  };
+  switch (combine_features(pairs)) {
+    case 8: go(combine_split_kernel<8>, 8); break;
+    case 4: go(combine_split_kernel<4>, 4); break;
+    default: go(combine_split_kernel<2>, 2); break;
+  }
   return hipGetLastError();
 }
 
