@@ -441,6 +441,10 @@ __global__ void __launch_bounds__(NT) plan_kernel(
 // in `scr` (the attention kernel's still-empty LDS ring). The partition-0
 // workgroups write row_ptr, split and header for the combine. This
 // partition's items (in rank order) land in items[0..*n_items).
+// Ints of LDS the plans may use before the ring fills: the four-stage ring
+// of 36,864-byte tiles (checked where the ring is declared).
+constexpr int kPlanScratchInts = 4 * 36864 / 4;
+
 template <int NT>
 __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* items,
                                   int* n_items) {
@@ -454,17 +458,29 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
   int* pk = kb + B;                           // [B + 1] first piece of each request
   int* rb = pk + B + 1;                       // [B + 1] first partial row
   int* preq = rb + B + 1;                     // [N] request of each piece
-  int* keyA = preq + kMaxPieces;
-  int* keyB = keyA + kMaxPieces;
-  int* idxA = keyB + kMaxPieces;
-  int* idxB = idxA + kMaxPieces;
-  // Units and costs; their total and maximum.
+  int* keyA = preq + kMaxPieces;              // [N] sort key of each piece
+  int* keyB = keyA + kMaxPieces;              // per-wave key histograms
+  int* idxB = keyB + kMaxPieces;              // [N] pieces by rank
+  // Units and costs; their total and maximum. Every length this thread needs
+  // is requested before the first is used (one round trip, not one per
+  // request).
+  constexpr int kLensPerThread = (kInlineSnakeBatch + NT - 1) / NT;
+  int lens[kLensPerThread];
+#pragma unroll
+  for (int i = 0; i < kLensPerThread; ++i) {
+    const int b = tid + i * NT;
+    lens[i] = b < B ? a.seq_lens[b] : 0;
+  }
   int csum = 0, cmax = 0;
-  for (int b = tid; b < B; b += NT) {
-    const int u = units_of(clamp_len(a.seq_lens[b], a.cap_tokens));
-    units[b] = u;
-    csum += ovh + u;
-    cmax = max(cmax, ovh + u);
+#pragma unroll
+  for (int i = 0; i < kLensPerThread; ++i) {
+    const int b = tid + i * NT;
+    if (b < B) {
+      const int u = units_of(clamp_len(lens[i], a.cap_tokens));
+      units[b] = u;
+      csum += ovh + u;
+      cmax = max(cmax, ovh + u);
+    }
   }
   int tot;
   (void)block_exclusive_scan<NT>(csum, s_wave, &tot);
@@ -499,7 +515,6 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
     for (int j = 0; j < k; ++j) {
       const int len = q + (j < r ? 1 : 0);
       keyA[ex3.x + j] = 255 - min(255, (ovh + len) >> shift);
-      idxA[ex3.x + j] = ex3.x + j;
       preq[ex3.x + j] = b;
     }
     ex3.x += k;
@@ -517,36 +532,75 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
     }
   }
   __syncthreads();
-  // Stable LSD radix sort of (key, piece) by one key bit per pass: each
-  // thread keeps its contiguous chunk's order, zeros before ones.
-  const int E = (N + NT - 1) / NT;
-  const int e0 = min(N, tid * E), e1 = min(N, e0 + E);
-  int* kin = keyA;
-  int* iin = idxA;
-  int* kout = keyB;
-  int* iout = idxB;
-  for (int bit = 0; bit < 8; ++bit) {
-    int z = 0;
-    for (int e = e0; e < e1; ++e) z += ((kin[e] >> bit) & 1) ? 0 : 1;
-    int zt;
-    int zb = block_exclusive_scan<NT>(z, s_wave, &zt);
-    if (zt == 0 || zt == N) continue;  // every key has this bit alike: order unchanged
-    for (int e = e0; e < e1; ++e) {
-      const int key = kin[e];
-      const bool one = (key >> bit) & 1;
-      const int dst = one ? zt + (e - zb) : zb;
-      zb += one ? 0 : 1;
-      kout[dst] = key;
-      iout[dst] = iin[e];
+  // Stable counting sort of the pieces by their 8-bit keys, in one pass.
+  // Wave w owns a contiguous chunk of pieces and walks it 64 at a time; the
+  // lanes holding equal keys in a batch find each other with eight ballots
+  // (one per key bit), which ranks them among themselves in lane order. Its
+  // per-key counts hist[w][key] become, after one scan over keys and waves,
+  // the first output slot of each (wave, key); a second walk scatters. Every
+  // workgroup reaches the same permutation (the stable order is unique).
+  constexpr int kW = NT / 64;
+  int* hist = keyB;        // [kW][256]
+  int* order = idxB;       // [N] pieces by rank
+  static_assert(4 * kInlineSnakeBatch + 2 + 4 * kMaxPieces <= kPlanScratchInts,
+                "snake plan scratch exceeds the ring");
+  static_assert(kW * 256 <= kMaxPieces && NT >= 256, "histogram layout");
+  const int lane = tid & 63, wave = tid >> 6;
+  const int chunk = (N + kW - 1) / kW;
+  const int c0 = min(N, wave * chunk), c1 = min(N, c0 + chunk);
+  for (int k = lane; k < 256; k += 64) hist[wave * 256 + k] = 0;
+  // Lanes of the batch with this lane's key (all 64 lanes take part in the
+  // ballots; lanes past the chunk are masked out).
+  auto peers = [&](int key, bool live) -> uint64_t {
+    uint64_t m = __ballot(live);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const uint64_t ones = __ballot(live && ((key >> bit) & 1));
+      m &= ((key >> bit) & 1) ? ones : ~ones;
     }
-    __syncthreads();
-    int* t0 = kin;
-    kin = kout;
-    kout = t0;
-    int* t1 = iin;
-    iin = iout;
-    iout = t1;
+    return m;
+  };
+  const uint64_t below = (uint64_t(1) << lane) - 1;
+  for (int e = c0; e < c1; e += 64) {
+    const bool live = e + lane < c1;
+    const int key = live ? keyA[e + lane] : 0;
+    const uint64_t m = peers(key, live);
+    if (live && (m & below) == 0) hist[wave * 256 + key] += __popcll(m);  // the key's first lane
   }
+  __syncthreads();
+  // Slot bases: keys in ascending order, waves in order within a key.
+  {
+    int tot = 0;
+    int h[kW];
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        h[w] = hist[w * 256 + tid];
+        tot += h[w];
+      }
+    }
+    int all;
+    int base = block_exclusive_scan<NT>(tid < 256 ? tot : 0, s_wave, &all);
+    if (tid < 256) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) {
+        hist[w * 256 + tid] = base;
+        base += h[w];
+      }
+    }
+  }
+  __syncthreads();
+  for (int e = c0; e < c1; e += 64) {
+    const bool live = e + lane < c1;
+    const int key = live ? keyA[e + lane] : 0;
+    const uint64_t m = peers(key, live);
+    if (live) order[hist[wave * 256 + key] + __popcll(m & below)] = e + lane;
+    // The key's first lane moves the base past this batch (after every lane
+    // of the wave has read it: a wave's LDS operations run in order).
+    if (live && (m & below) == 0) hist[wave * 256 + key] += __popcll(m);
+  }
+  __syncthreads();
+  const int* iin = order;
   // This partition's pieces: ranks r * parts + (r odd ? parts - 1 - part : part).
   if (tid < 64) {
     const int r = tid;
@@ -796,6 +850,7 @@ constexpr int kTile = 2 * kUnit;                      // tokens per LDS tile
 constexpr int kStages = 4;                            // LDS ring depth
 constexpr int kRowChunks = kRowBytes / 16;            // 72 chunks per cached row
 constexpr int kTileBytesBf16 = kTile * kRowBytes;     // 36864
+static_assert(kStages * kTileBytesBf16 == 4 * kPlanScratchInts, "plan scratch is the ring");
 constexpr int kDmaPerThread = kTile * kRowChunks / kThreads;  // 9
 static_assert(kTile * kRowChunks == kDmaPerThread * kThreads, "tile must split evenly");
 
