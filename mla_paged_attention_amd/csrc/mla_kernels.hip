@@ -733,7 +733,12 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
       const int cinc = wave_inclusive_scan(cost);
       const int total = __builtin_amdgcn_readlane(cinc, 63);
       int P = (total + a.parts_cap - 1) / a.parts_cap;
-      if (P < kMinPartUnits) P = kMinPartUnits;
+      // Few and short requests (pieces of kMinPartUnits would keep under a
+      // quarter of the partitions busy) take smaller pieces: such a call is
+      // bound by each piece's latency, not by its bytes.
+      const int pmin =
+          4 * total < a.parts_cap * kMinPartUnits ? kMinPartUnitsFew : kMinPartUnits;
+      if (P < pmin) P = pmin;
       const int ub = cinc - cost + ovh, ue = cinc;
       // Requests of equal length whose count divides the partitions: each is
       // cut into S = partitions / batch equal pieces, one partition each, so
