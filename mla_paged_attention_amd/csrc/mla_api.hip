@@ -250,7 +250,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + w.row_ptr);
   int32_t* part_ptr = reinterpret_cast<int32_t*>(ws + w.part_ptr);
   int4* work = reinterpret_cast<int4*>(ws + w.work);
-  int32_t* split = reinterpret_cast<int32_t*>(ws + w.split);
+  int4* split = reinterpret_cast<int4*>(ws + w.split);
   float* part_lse = reinterpret_cast<float*>(ws + w.part_lse);
   float* part_out = reinterpret_cast<float*>(ws + w.part_out);
 
@@ -355,7 +355,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
     // Split requests are fewer than the partitions (each is costlier than
     // a partition's share, or straddles one of the parts - 1 cuts).
     const int64_t max_split = a.batch < max_parts ? a.batch : max_parts;
-    if (mla::launch_combine_split(part_out, part_lse, row_ptr, split, header,
+    if (mla::launch_combine_split(part_out, part_lse, split, header,
                                   static_cast<uint16_t*>(a.out), a.lse, int32_t(max_split),
                                   rows, s) != hipSuccess)
       return MLA_ERR_HIP;

@@ -51,7 +51,7 @@ struct WorkspaceLayout {
   size_t row_ptr;   // int32[batch + 1]: first partial row of each request
   size_t part_ptr;  // int32[parts + 1]: first work item of each partition
   size_t work;      // int32x4[batch + parts]: (request, unit begin, unit end, row or -1)
-  size_t split;     // int32[parts]: requests with partial rows
+  size_t split;     // int4[parts]: (request, first partial row, rows, 0) per split request
   size_t part_lse;  // float[rows][num_heads]
   size_t part_out;  // float[rows][num_heads][512]
   size_t sp_rows;   // sparse: int32[batch][sparse_stride] physical row ids
@@ -84,7 +84,7 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
   w.work = off;
   off += align256(size_t(batch + parts) * 16);
   w.split = off;
-  off += align256(size_t(parts) * 4);
+  off += align256(size_t(parts) * 16);
   w.part_lse = off;
   off += align256(size_t(rows) * size_t(num_heads) * 4);
   w.part_out = off;
@@ -175,7 +175,7 @@ struct AttnArgs {
   // combine.
   int32_t inline_plan;
   int32_t* wr_row_ptr;
-  int32_t* wr_split;
+  int4* wr_split;
   int32_t* wr_header;
   // Bounds-check build: the error word (null otherwise).
   int32_t* err_word;
@@ -239,7 +239,7 @@ hipError_t launch_absorb_out(const uint16_t* o_latent, const uint16_t* w_uv, uin
 // Combine of the automatic plan: only the requests listed in `split`
 // (header[2] of them, at most `max_split`).
 hipError_t launch_combine_split(const float* part_out, const float* part_lse,
-                                const int32_t* row_ptr, const int32_t* split,
+                                const int4* split,
                                 const int32_t* header, uint16_t* out, float* lse,
                                 int32_t max_split, int32_t num_heads, hipStream_t stream);
 

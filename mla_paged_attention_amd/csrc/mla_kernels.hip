@@ -232,7 +232,7 @@ template <int NT>
 __global__ void __launch_bounds__(NT) plan_kernel(
     const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t max_parts, int32_t ovh,
     int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr, int4* work,
-    int32_t* split) {
+    int4* split) {
   __shared__ int s_wave[48];
   __shared__ int s_cnt[kMaxPlanParts + 1];
   __shared__ int s_bucket[4 * NT];
@@ -292,7 +292,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
       if (b < batch) {
         cum[b] = c0[i];
         row_ptr[b] = rb;
-        if (k[i] > 1) split[sb++] = b;
+        if (k[i] > 1) split[sb++] = make_int4(b, rb, k[i], 0);
         if (!snake) {
           const int ub = c0[i] + ovh, ue = c0[i] + cost[i];
           const int first = ub / P;
@@ -405,7 +405,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
     if (b < batch) {
       const int ibase = carry3.x + ex3.x, rbase = carry3.y + ex3.y;
       row_ptr[b] = rbase;
-      if (k > 1) split[carry3.z + ex3.z] = b;
+      if (k > 1) split[carry3.z + ex3.z] = make_int4(b, rbase, k, 0);
       const int ub = c0 + ovh, ue = c0 + cost;
       const int first = ub / P;
       for (int j = 0; j < k; ++j) {
@@ -510,7 +510,7 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
     const int k = kb[b];
     pk[b] = ex3.x;
     rb[b] = ex3.y;
-    if (part == 0 && k > 1) a.wr_split[ex3.z] = b;
+    if (part == 0 && k > 1) a.wr_split[ex3.z] = make_int4(b, ex3.y, k, 0);
     const int q = units[b] / k, r = units[b] - q * k;
     for (int j = 0; j < k; ++j) {
       const int len = q + (j < r ? 1 : 0);
@@ -672,7 +672,7 @@ __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, Co
     if (part < parts && ue > lo && c0 <= lo) *walk = ContigWalk{b, c0, rb, P, parts};
     if (part == 0) {
       a.wr_row_ptr[b] = rb;
-      if (k > 1) a.wr_split[sb] = b;
+      if (k > 1) a.wr_split[sb] = make_int4(b, rb, k, 0);
     }
     rb += k > 1 ? k : 0;
     sb += k > 1 ? 1 : 0;
@@ -759,7 +759,7 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
         // Same values from every partition-0 workgroup (one per head tile).
         if (live) {
           a.wr_row_ptr[lane] = rinc - nrows;
-          if (k > 1) a.wr_split[sinc - 1] = lane;
+          if (k > 1) a.wr_split[sinc - 1] = make_int4(lane, rinc - nrows, k, 0);
         }
         if (lane == 0) {
           a.wr_row_ptr[a.batch] = __builtin_amdgcn_readlane(rinc, 63);
@@ -2191,24 +2191,27 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* part_out, con
   combine_rows<F>(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
 }
 
-// The automatic plan's combine: block k merges request split[k] (header[2]
-// such requests); the rest exit at once.
+// The automatic plan's combine: block k merges the split request of record
+// split[k] = (request, first partial row, rows), header[2] such records; the
+// rest exit at once. The first record a block needs is requested together
+// with header[2] (one round trip before the rows, not two).
 template <int F>
 __global__ void __launch_bounds__(256) combine_split_kernel(
-    const float* part_out, const float* part_lse, const int32_t* row_ptr, const int32_t* split,
-    const int32_t* header, uint16_t* out, float* lse, int32_t H, int32_t tiles) {
+    const float* part_out, const float* part_lse, const int4* split, const int32_t* header,
+    uint16_t* out, float* lse, int32_t H, int32_t tiles, int32_t max_split) {
   // Grid-stride over (split request, head tile, chunk): a plan without
   // split requests costs one small launch.
   constexpr int kChunks = kDV / (16 * F);
   const int per = tiles * kChunks;
+  const int k0 = blockIdx.x / per;
+  const int4 rec0 = k0 < max_split ? split[k0] : make_int4(0, 0, 0, 0);
   const int n = header[2] * per;
   for (int w = blockIdx.x; w < n; w += gridDim.x) {
     const int k = w / per;
+    const int4 rec = w == int(blockIdx.x) ? rec0 : split[k];
     const int rest = w - k * per;
-    const int b = split[k];
     const int chunk = rest % kChunks, ht = rest / kChunks;
-    const int r0 = row_ptr[b], nr = row_ptr[b + 1] - r0;
-    combine_rows<F>(part_out, part_lse, r0, nr, out, lse, b, H, ht, chunk);
+    combine_rows<F>(part_out, part_lse, rec.y, rec.z, out, lse, rec.x, H, ht, chunk);
   }
 }
 
@@ -2230,7 +2233,7 @@ hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_token
                      reinterpret_cast<int32_t*>(ws + w.header), reinterpret_cast<int32_t*>(ws + w.cum),
                      reinterpret_cast<int32_t*>(ws + w.row_ptr),
                      reinterpret_cast<int32_t*>(ws + w.part_ptr),
-                     reinterpret_cast<int4*>(ws + w.work), reinterpret_cast<int32_t*>(ws + w.split));
+                     reinterpret_cast<int4*>(ws + w.work), reinterpret_cast<int4*>(ws + w.split));
   return hipGetLastError();
 }
 
@@ -2320,7 +2323,7 @@ hipError_t launch_combine(const float* part_out, const float* part_lse,
 }
 
 hipError_t launch_combine_split(const float* part_out, const float* part_lse,
-                                const int32_t* row_ptr, const int32_t* split,
+                                const int4* split,
                                 const int32_t* header, uint16_t* out, float* lse,
                                 int32_t max_split, int32_t num_heads, hipStream_t stream) {
   const int tiles = head_tiles(num_heads);
@@ -2329,8 +2332,8 @@ hipError_t launch_combine_split(const float* part_out, const float* part_lse,
   auto go = [&](auto kern, int f) {
     const int64_t tuples = pairs * (kDV / (16 * f));
     const unsigned grid = unsigned(tuples < kCombineGrid ? tuples : kCombineGrid);
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, part_out, part_lse, row_ptr, split,
-                       header, out, lse, num_heads, tiles);
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(256), 0, stream, part_out, part_lse, split, header,
+                       out, lse, num_heads, tiles, max_split);
   };
   switch (combine_features(pairs)) {
     case 8: go(combine_split_kernel<8>, 8); break;

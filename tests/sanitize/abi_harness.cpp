@@ -34,8 +34,8 @@ hipError_t launch_absorb_q(const uint16_t*, const uint16_t*, const uint16_t*, ui
                            int32_t, hipStream_t) { ++g_launches; return hipErrorUnknown; }
 hipError_t launch_absorb_out(const uint16_t*, const uint16_t*, uint16_t*, int32_t, int32_t,
                              hipStream_t) { ++g_launches; return hipErrorUnknown; }
-hipError_t launch_combine_split(const float*, const float*, const int32_t*, const int32_t*,
-                                const int32_t*, uint16_t*, float*, int32_t, int32_t, hipStream_t) {
+hipError_t launch_combine_split(const float*, const float*, const int4*, const int32_t*,
+                                uint16_t*, float*, int32_t, int32_t, hipStream_t) {
   ++g_launches; return hipErrorUnknown;
 }
 }  // namespace mla
