@@ -117,6 +117,19 @@ def test_large_batch_with_long_requests(orc):
     _check(orc, wl, 0, what="large batch with long requests")
 
 
+@pytest.mark.parametrize("num_heads", [16, 128])
+def test_snake_plan_largest_batch(orc, num_heads):
+    # The in-kernel snake plan at its largest batch (1024 requests): every
+    # workgroup ranks the pieces itself, so the ranking must agree across
+    # workgroups. A few very long requests are cut into many pieces, and
+    # many short ones share a cost (equal sort keys); all rows are checked.
+    gen = np.random.default_rng(71)
+    lens = gen.integers(1, 400, size=1016).tolist() + [0, 1, 16, 17, 12000, 20000, 7000, 33]
+    wl = workloads.make_workload(batch=len(lens), num_heads=num_heads, seq=("fixed", lens),
+                                 block_size=32, seed=72, poison=True)
+    _check(orc, wl, 0, what=f"snake plan, 1024 requests, {num_heads} heads")
+
+
 @pytest.mark.parametrize("num_heads,kv_dtype,splits",
                          [(16, "bf16", (0, 1)), (128, "bf16", (0, 1)), (32, "fp8", (0, 1))])
 def test_long_context(orc, num_heads, kv_dtype, splits):
