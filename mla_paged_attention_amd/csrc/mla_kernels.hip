@@ -194,6 +194,26 @@ __device__ __forceinline__ int block_max(int v, int* s_wave) {
   return r;
 }
 
+// Block-wide total and maximum in one exchange (two barriers).
+template <int NT>
+__device__ __forceinline__ int2 block_sum_max(int sum, int mx, int* s_wave) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int ws = __builtin_amdgcn_readlane(wave_inclusive_scan(sum), 63);
+  const int wm = wave_max(mx);
+  if (lane == 0) {
+    s_wave[wave] = ws;
+    s_wave[16 + wave] = wm;
+  }
+  __syncthreads();
+  int t = 0, m = s_wave[16];
+  for (int i = 0; i < NT / 64; ++i) {
+    t += s_wave[i];
+    m = max(m, s_wave[16 + i]);
+  }
+  __syncthreads();
+  return make_int2(t, m);
+}
+
 // Exclusive scan of s[0..n) in place (n <= NT * 4), returns the total.
 template <int NT>
 __device__ int block_scan_lds(int* s, int n, int* s_wave) {
@@ -482,54 +502,75 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
       cmax = max(cmax, ovh + u);
     }
   }
-  int tot;
-  (void)block_exclusive_scan<NT>(csum, s_wave, &tot);
-  cmax = block_max<NT>(cmax, s_wave);  // also orders the units[] stores
+  const int2 sm = block_sum_max<NT>(csum, cmax, s_wave);  // also orders the units[] stores
+  const int tot = sm.x;
+  cmax = sm.y;
   int P = (tot + a.parts_cap - 1) / a.parts_cap;
   if (P < kMinPartUnits) P = kMinPartUnits;
-  // Pieces per request (requests above the target are cut) and the bases of
-  // pieces, partial rows and split requests, over contiguous chunks.
-  const int C = (B + NT - 1) / NT;
-  const int b0 = min(B, tid * C), b1 = min(B, b0 + C);
-  int3 mine = make_int3(0, 0, 0);
-  for (int b = b0; b < b1; ++b) {
-    const int cost = ovh + units[b];
-    const int k = cost > P ? (cost + P - 1) / P : 1;
-    kb[b] = k;
-    mine.x += k;
-    mine.y += k > 1 ? k : 0;
-    mine.z += k > 1 ? 1 : 0;
-  }
-  int3 tot3;
-  int3 ex3 = block_exclusive_scan3<NT>(mine, s_wave, &tot3);
-  const int N = tot3.x;
-  const int parts = min(a.parts_cap, N);
   int shift = 0;
   while ((cmax >> shift) > 255) ++shift;
-  for (int b = b0; b < b1; ++b) {
-    const int k = kb[b];
-    pk[b] = ex3.x;
-    rb[b] = ex3.y;
-    if (part == 0 && k > 1) a.wr_split[ex3.z] = make_int4(b, ex3.y, k, 0);
-    const int q = units[b] / k, r = units[b] - q * k;
-    for (int j = 0; j < k; ++j) {
-      const int len = q + (j < r ? 1 : 0);
-      keyA[ex3.x + j] = 255 - min(255, (ovh + len) >> shift);
-      preq[ex3.x + j] = b;
+  int N, n_rows = 0, n_split = 0;
+  if (cmax <= P) {
+    // No request costs more than the target, so none is cut: piece b is
+    // request b and no partial row exists.
+    N = B;
+#pragma unroll
+    for (int i = 0; i < kLensPerThread; ++i) {
+      const int b = tid + i * NT;
+      if (b < B) {
+        const int u = units_of(clamp_len(lens[i], a.cap_tokens));
+        kb[b] = 1;
+        pk[b] = b;
+        rb[b] = 0;
+        keyA[b] = 255 - min(255, (ovh + u) >> shift);
+        preq[b] = b;
+        if (part == 0) a.wr_row_ptr[b] = 0;
+      }
     }
-    ex3.x += k;
-    ex3.y += k > 1 ? k : 0;
-    ex3.z += k > 1 ? 1 : 0;
+  } else {
+    // Pieces per request (requests above the target are cut) and the bases
+    // of pieces, partial rows and split requests, over contiguous chunks.
+    const int C = (B + NT - 1) / NT;
+    const int b0 = min(B, tid * C), b1 = min(B, b0 + C);
+    int3 mine = make_int3(0, 0, 0);
+    for (int b = b0; b < b1; ++b) {
+      const int cost = ovh + units[b];
+      const int k = cost > P ? (cost + P - 1) / P : 1;
+      kb[b] = k;
+      mine.x += k;
+      mine.y += k > 1 ? k : 0;
+      mine.z += k > 1 ? 1 : 0;
+    }
+    int3 tot3;
+    int3 ex3 = block_exclusive_scan3<NT>(mine, s_wave, &tot3);
+    N = tot3.x;
+    n_rows = tot3.y;
+    n_split = tot3.z;
+    for (int b = b0; b < b1; ++b) {
+      const int k = kb[b];
+      pk[b] = ex3.x;
+      rb[b] = ex3.y;
+      if (part == 0 && k > 1) a.wr_split[ex3.z] = make_int4(b, ex3.y, k, 0);
+      const int q = units[b] / k, r = units[b] - q * k;
+      for (int j = 0; j < k; ++j) {
+        const int len = q + (j < r ? 1 : 0);
+        keyA[ex3.x + j] = 255 - min(255, (ovh + len) >> shift);
+        preq[ex3.x + j] = b;
+      }
+      ex3.x += k;
+      ex3.y += k > 1 ? k : 0;
+      ex3.z += k > 1 ? 1 : 0;
+    }
+    if (part == 0)
+      for (int b = b0; b < b1; ++b) a.wr_row_ptr[b] = rb[b];
   }
-  if (part == 0) {
-    for (int b = b0; b < b1; ++b) a.wr_row_ptr[b] = rb[b];
-    if (tid == 0) {
-      a.wr_row_ptr[B] = tot3.y;
-      a.wr_header[0] = parts;
-      a.wr_header[1] = P;
-      a.wr_header[2] = tot3.z;
-      a.wr_header[3] = kPlanSnake;
-    }
+  const int parts = min(a.parts_cap, N);
+  if (part == 0 && tid == 0) {
+    a.wr_row_ptr[B] = n_rows;
+    a.wr_header[0] = parts;
+    a.wr_header[1] = P;
+    a.wr_header[2] = n_split;
+    a.wr_header[3] = kPlanSnake;
   }
   __syncthreads();
   // Stable counting sort of the pieces by their 8-bit keys, in one pass.
