@@ -574,12 +574,13 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
   }
   __syncthreads();
   // Stable counting sort of the pieces by their 8-bit keys, in one pass.
-  // Wave w owns a contiguous chunk of pieces and walks it 64 at a time; the
-  // lanes holding equal keys in a batch find each other with eight ballots
-  // (one per key bit), which ranks them among themselves in lane order. Its
-  // per-key counts hist[w][key] become, after one scan over keys and waves,
-  // the first output slot of each (wave, key); a second walk scatters. Every
-  // workgroup reaches the same permutation (the stable order is unique).
+  // Wave w owns a contiguous chunk of pieces and counts its keys into
+  // hist[w][key]; one scan over keys and waves turns the counts into the
+  // first output slot of each (wave, key). A second walk, 64 pieces at a
+  // time, scatters: the lanes holding equal keys in a batch find each other
+  // with eight ballots (one per key bit), which ranks them among themselves
+  // in lane order. Every workgroup reaches the same permutation (the stable
+  // order is unique).
   constexpr int kW = NT / 64;
   int* hist = keyB;        // [kW][256]
   int* order = idxB;       // [N] pieces by rank
@@ -602,12 +603,8 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
     return m;
   };
   const uint64_t below = (uint64_t(1) << lane) - 1;
-  for (int e = c0; e < c1; e += 64) {
-    const bool live = e + lane < c1;
-    const int key = live ? keyA[e + lane] : 0;
-    const uint64_t m = peers(key, live);
-    if (live && (m & below) == 0) hist[wave * 256 + key] += __popcll(m);  // the key's first lane
-  }
+  // Counts only: LDS atomic adds (the totals do not depend on their order).
+  for (int e = c0 + lane; e < c1; e += 64) atomicAdd(&hist[wave * 256 + keyA[e]], 1);
   __syncthreads();
   // Slot bases: keys in ascending order, waves in order within a key.
   {
