@@ -86,7 +86,7 @@ extern "C" {
 typedef enum {
   MLA_OK = 0,
   MLA_ERR_INVALID_ARG = -1,        /* null/misaligned pointer, out-of-range size */
-  MLA_ERR_UNSUPPORTED = -2,        /* valid request this build does not serve */
+  MLA_ERR_UNSUPPORTED = -2,        /* valid request the library does not serve (device not gfx950) */
   MLA_ERR_WORKSPACE_TOO_SMALL = -3,
   MLA_ERR_NO_DEVICE = -4,
   MLA_ERR_HIP = -5                 /* a HIP runtime call or launch failed */
