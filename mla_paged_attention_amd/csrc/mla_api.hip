@@ -247,7 +247,6 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
       mla::plan_overhead_units(rows, a.kv_dtype == MLA_KV_FP8_E4M3 ? 1 : 0, sparse);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
   int32_t* header = reinterpret_cast<int32_t*>(ws + w.header);
-  int32_t* row_ptr = reinterpret_cast<int32_t*>(ws + w.row_ptr);
   int32_t* part_ptr = reinterpret_cast<int32_t*>(ws + w.part_ptr);
   int4* work = reinterpret_cast<int4*>(ws + w.work);
   int4* split = reinterpret_cast<int4*>(ws + w.split);
@@ -313,7 +312,6 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   args.header = header;
   args.part_ptr = part_ptr;
   args.work = work;
-  args.row_ptr = row_ptr;
   args.scale_log2 = a.scale * 1.4426950408889634f;
   args.kv_scale = a.kv_scale;
   args.rows = rows;
@@ -334,7 +332,6 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   args.sparse_stride = sparse ? int32_t(mla::sparse_stride(a.topk)) : 0;
   args.zero_row = sparse ? ws + w.zero_row : nullptr;
   args.inline_plan = inline_plan;
-  args.wr_row_ptr = row_ptr;
   args.wr_split = split;
   args.wr_header = header;
   args.err_word = err_word;
@@ -348,7 +345,7 @@ mla_status_t run_decode(const DecodeArgs& call, void* const* events) {
   if (!rec(2)) return MLA_ERR_HIP;
 
   if (a.num_splits > 1) {
-    if (mla::launch_combine(part_out, part_lse, row_ptr, static_cast<uint16_t*>(a.out), a.lse,
+    if (mla::launch_combine(part_out, part_lse, nullptr, static_cast<uint16_t*>(a.out), a.lse,
                             a.batch, rows, 0, a.num_splits, s) != hipSuccess)
       return MLA_ERR_HIP;
   } else if (a.num_splits == 0 && max_parts > 1 && w.rows > 0) {

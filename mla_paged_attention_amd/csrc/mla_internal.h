@@ -48,7 +48,6 @@ struct WorkspaceLayout {
   size_t header;    // int32[64]: [0] partitions, [1] cost units per partition,
                     // [2] split requests, [3] plan mode
   size_t cum;       // int32[batch + 1]: exclusive prefix of per-request costs
-  size_t row_ptr;   // int32[batch + 1]: first partial row of each request
   size_t part_ptr;  // int32[parts + 1]: first work item of each partition
   size_t work;      // int32x4[batch + parts]: (request, unit begin, unit end, row or -1)
   size_t split;     // int4[parts]: (request, first partial row, rows, 0) per split request
@@ -76,8 +75,6 @@ inline WorkspaceLayout workspace_layout(int64_t batch, int64_t num_heads, int64_
   w.header = off;
   off += 256;
   w.cum = off;
-  off += align256(size_t(batch + 1) * 4);
-  w.row_ptr = off;
   off += align256(size_t(batch + 1) * 4);
   w.part_ptr = off;
   off += align256(size_t(parts + 1) * 4);
@@ -147,7 +144,6 @@ struct AttnArgs {
   const int32_t* header;
   const int32_t* part_ptr;   // automatic plan: work items of each partition
   const int4* work;
-  const int32_t* row_ptr;
   float scale_log2;          // logit scale * log2(e)
   float kv_scale;            // fp8 dequantisation scale (1 for bf16)
   int32_t rows;              // q_len * heads
@@ -171,10 +167,8 @@ struct AttnArgs {
   const uint8_t* zero_row;
   // Automatic plan worked out inside the attention kernel (batches of at
   // most kInlinePlanBatch requests with a contiguous plan): no plan launch;
-  // the partition-0 workgroups write row_ptr, split and header for the
-  // combine.
+  // the partition-0 workgroups write split and header for the combine.
   int32_t inline_plan;
-  int32_t* wr_row_ptr;
   int4* wr_split;
   int32_t* wr_header;
   // Bounds-check build: the error word (null otherwise).
@@ -194,8 +188,8 @@ constexpr int kInlineContiguousWide = 3;  // the contiguous plan, worked out by 
 constexpr int kInlineSnakeBatch = 1024;
 constexpr int kInlineContigBatch = 4096;
 
-// Split plan (one workgroup). Forced mode (num_splits > 0) writes row_ptr
-// only; the automatic plan fills header, cum, row_ptr, part_ptr, work and split.
+// Split plan (one workgroup) for the automatic plan when the attention kernel
+// does not work it out itself: fills header, cum, part_ptr, work and split.
 hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_tokens,
                        int32_t max_parts, int32_t ovh, const WorkspaceLayout& w, void* workspace,
                        hipStream_t stream);

@@ -251,7 +251,7 @@ __device__ int block_scan_lds(int* s, int n, int* s_wave) {
 template <int NT>
 __global__ void __launch_bounds__(NT) plan_kernel(
     const int32_t* seq_lens, int32_t batch, int32_t cap_tokens, int32_t max_parts, int32_t ovh,
-    int32_t* header, int32_t* cum, int32_t* row_ptr, int32_t* part_ptr, int4* work,
+    int32_t* header, int32_t* cum, int32_t* part_ptr, int4* work,
     int4* split) {
   __shared__ int s_wave[48];
   __shared__ int s_cnt[kMaxPlanParts + 1];
@@ -311,7 +311,6 @@ __global__ void __launch_bounds__(NT) plan_kernel(
       rbase[i] = rb;
       if (b < batch) {
         cum[b] = c0[i];
-        row_ptr[b] = rb;
         if (k[i] > 1) split[sb++] = make_int4(b, rb, k[i], 0);
         if (!snake) {
           const int ub = c0[i] + ovh, ue = c0[i] + cost[i];
@@ -382,7 +381,6 @@ __global__ void __launch_bounds__(NT) plan_kernel(
     }
     if (tid == 0) {
       cum[batch] = total;
-      row_ptr[batch] = tot3.y;
       header[0] = parts;
       header[1] = P;
       header[2] = tot3.z;
@@ -424,7 +422,6 @@ __global__ void __launch_bounds__(NT) plan_kernel(
                                            &tot3);
     if (b < batch) {
       const int ibase = carry3.x + ex3.x, rbase = carry3.y + ex3.y;
-      row_ptr[b] = rbase;
       if (k > 1) split[carry3.z + ex3.z] = make_int4(b, rbase, k, 0);
       const int ub = c0 + ovh, ue = c0 + cost;
       const int first = ub / P;
@@ -444,7 +441,6 @@ __global__ void __launch_bounds__(NT) plan_kernel(
   for (int q = tid; q <= max_parts; q += NT) part_ptr[q] = s_cnt[q];
   if (tid == 0) {
     cum[batch] = total;
-    row_ptr[batch] = carry3.y;
     header[0] = parts;
     header[1] = P;
     header[2] = carry3.z;
@@ -459,7 +455,7 @@ __global__ void __launch_bounds__(NT) plan_kernel(
 // largest first, ties in piece order (a stable LSD radix sort of one bit per
 // pass), where plan_kernel ranks equal costs in atomic order. Scratch lives
 // in `scr` (the attention kernel's still-empty LDS ring). The partition-0
-// workgroups write row_ptr, split and header for the combine. This
+// workgroups write split and header for the combine. This
 // partition's items (in rank order) land in items[0..*n_items).
 // Ints of LDS the plans may use before the ring fills: the four-stage ring
 // of 36,864-byte tiles (checked where the ring is declared).
@@ -509,7 +505,7 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
   if (P < kMinPartUnits) P = kMinPartUnits;
   int shift = 0;
   while ((cmax >> shift) > 255) ++shift;
-  int N, n_rows = 0, n_split = 0;
+  int N, n_split = 0;
   if (cmax <= P) {
     // No request costs more than the target, so none is cut: piece b is
     // request b and no partial row exists.
@@ -524,7 +520,6 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
         rb[b] = 0;
         keyA[b] = 255 - min(255, (ovh + u) >> shift);
         preq[b] = b;
-        if (part == 0) a.wr_row_ptr[b] = 0;
       }
     }
   } else {
@@ -544,7 +539,6 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
     int3 tot3;
     int3 ex3 = block_exclusive_scan3<NT>(mine, s_wave, &tot3);
     N = tot3.x;
-    n_rows = tot3.y;
     n_split = tot3.z;
     for (int b = b0; b < b1; ++b) {
       const int k = kb[b];
@@ -561,12 +555,9 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
       ex3.y += k > 1 ? k : 0;
       ex3.z += k > 1 ? 1 : 0;
     }
-    if (part == 0)
-      for (int b = b0; b < b1; ++b) a.wr_row_ptr[b] = rb[b];
   }
   const int parts = min(a.parts_cap, N);
   if (part == 0 && tid == 0) {
-    a.wr_row_ptr[B] = n_rows;
     a.wr_header[0] = parts;
     a.wr_header[1] = P;
     a.wr_header[2] = n_split;
@@ -663,7 +654,7 @@ __device__ void inline_snake_plan(const AttnArgs& a, int part, int* scr, int4* i
 // laid end to end, cut into partitions of P units. A partition's pieces are
 // one run of consecutive requests, so the workgroup keeps only where its run
 // starts (request, its cost prefix and its first partial row) and walks it.
-// Partition 0 writes row_ptr, split and header for the combine. `scr` is the
+// Partition 0 writes split and header for the combine. `scr` is the
 // still-empty LDS ring.
 struct ContigWalk {
   int b, cum, rb, P, parts;
@@ -708,16 +699,12 @@ __device__ void inline_contiguous_plan(const AttnArgs& a, int part, int* scr, Co
     const int k = (ue - 1) / P - ub / P + 1;
     // The first request reaching into this partition starts the walk.
     if (part < parts && ue > lo && c0 <= lo) *walk = ContigWalk{b, c0, rb, P, parts};
-    if (part == 0) {
-      a.wr_row_ptr[b] = rb;
-      if (k > 1) a.wr_split[sb] = make_int4(b, rb, k, 0);
-    }
+    if (part == 0 && k > 1) a.wr_split[sb] = make_int4(b, rb, k, 0);
     rb += k > 1 ? k : 0;
     sb += k > 1 ? 1 : 0;
     c0 = ue;
   }
   if (part == 0 && tid == 0) {
-    a.wr_row_ptr[B] = tot3.y;
     a.wr_header[0] = parts;
     a.wr_header[1] = P;
     a.wr_header[2] = tot3.z;
@@ -795,12 +782,8 @@ __device__ __forceinline__ void for_each_piece(const AttnArgs& a, int part, int*
       const int sinc = wave_inclusive_scan(k > 1 ? 1 : 0);
       if (part == 0) {
         // Same values from every partition-0 workgroup (one per head tile).
-        if (live) {
-          a.wr_row_ptr[lane] = rinc - nrows;
-          if (k > 1) a.wr_split[sinc - 1] = make_int4(lane, rinc - nrows, k, 0);
-        }
+        if (live && k > 1) a.wr_split[sinc - 1] = make_int4(lane, rinc - nrows, k, 0);
         if (lane == 0) {
-          a.wr_row_ptr[a.batch] = __builtin_amdgcn_readlane(rinc, 63);
           a.wr_header[0] = aligned ? a.batch * S : (total + P - 1) / P;
           a.wr_header[1] = aligned ? (c0 - ovh + S - 1) / S : P;
           a.wr_header[2] = __builtin_amdgcn_readlane(sinc, 63);
@@ -2269,7 +2252,6 @@ hipError_t launch_plan(const int32_t* seq_lens, int32_t batch, int32_t cap_token
   hipLaunchKernelGGL(kern, dim3(1), dim3(small ? kPlanThreadsSmall : kPlanThreads), 0, stream,
                      seq_lens, batch, cap_tokens, max_parts, ovh,
                      reinterpret_cast<int32_t*>(ws + w.header), reinterpret_cast<int32_t*>(ws + w.cum),
-                     reinterpret_cast<int32_t*>(ws + w.row_ptr),
                      reinterpret_cast<int32_t*>(ws + w.part_ptr),
                      reinterpret_cast<int4*>(ws + w.work), reinterpret_cast<int4*>(ws + w.split));
   return hipGetLastError();

@@ -76,7 +76,7 @@ def test_status_strings_and_version():
 
 def _layout(batch, heads, rows, parts=1):
     a = lambda x: (x + 255) // 256 * 256  # noqa: E731
-    return (256 + 2 * a((batch + 1) * 4) + a((parts + 1) * 4) + a((batch + parts) * 16)
+    return (256 + a((batch + 1) * 4) + a((parts + 1) * 4) + a((batch + parts) * 16)
             + a(parts * 16) + a(rows * heads * 4) + a(rows * heads * 512 * 4))
 
 
