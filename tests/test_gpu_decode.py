@@ -232,6 +232,17 @@ def test_head_padding_to_128(orc):
         np.testing.assert_allclose(lse128[b, 16:], np.log(n), atol=1e-3)
 
 
+@pytest.mark.parametrize("batch", [40, 160])
+def test_forced_splits_larger_batches(orc, batch):
+    # Forced splits merge every request: 40 and 160 (request, head tile)
+    # pairs run the merge with 4 and 8 features per thread.
+    gen = np.random.default_rng(batch)
+    lens = [0, 1, 17] + gen.integers(1, 700, size=batch - 3).tolist()
+    wl = workloads.make_workload(batch=batch, num_heads=16, seq=("fixed", lens), block_size=32,
+                                 seed=batch + 5, poison=True)
+    _check(orc, wl, 3, what=f"forced 3 splits, batch {batch}")
+
+
 @pytest.mark.parametrize("kv_dtype,num_heads", [("bf16", 16), ("bf16", 64), ("fp8", 48)])
 def test_split_counts_agree(orc, kv_dtype, num_heads):
     wl = workloads.make_workload(batch=3, num_heads=num_heads, seq=("fixed", [2000, 37, 4097]),
@@ -322,10 +333,12 @@ def test_batch_zero():
 
 # ---------------------------------------------------------------- combine
 
-def test_combine_matches_oracle_merge(orc):
-    gen = torch.Generator().manual_seed(31)
-    H = 20
-    counts = [0, 1, 2, 5, 16, 3]
+@pytest.mark.parametrize("nreq,H", [(6, 20), (40, 16), (70, 32)])
+def test_combine_matches_oracle_merge(orc, nreq, H):
+    # (request, 16-head tile) pairs: 12, 40 and 140, so the merge runs with
+    # 2, 4 and 8 features per thread.
+    gen = torch.Generator().manual_seed(31 + nreq)
+    counts = ([0, 1, 2, 5, 16, 3] * ((nreq + 5) // 6))[:nreq]
     indptr = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     rows = int(indptr[-1])
     part_out = torch.randn((rows, H, 512), generator=gen, dtype=torch.float32)
