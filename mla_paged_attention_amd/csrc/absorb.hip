@@ -131,15 +131,30 @@ __global__ void __launch_bounds__(kAbsorbThreads) absorb_q_kernel(const uint16_t
 #pragma unroll
     for (int s = 0; s < K / 32; ++s) xf[t][s] = *reinterpret_cast<const a_u32x4_t*>(p + 32 * s);
   }
+  // The rope columns (slice 0 only) are requested with the other operands and
+  // stored after the barrier, so their round trip overlaps the weights'.
+  constexpr int kRopeIters = (kRows * kRope / 8 + kAbsorbThreads - 1) / kAbsorbThreads;
+  a_u32x4_t rv[kRopeIters];
+  if (n0 == 0) {
+#pragma unroll
+    for (int it = 0; it < kRopeIters; ++it) {
+      const int i = tid + it * kAbsorbThreads;
+      const int b = b0 + i / (kRope / 8), q = i % (kRope / 8);
+      if (i < kRows * kRope / 8 && b < batch)
+        rv[it] = *reinterpret_cast<const a_u32x4_t*>(rope + (size_t(b) * heads + h) * kRope + 8 * q);
+    }
+  }
   stage<K, NS>(w + size_t(h) * K * kLatent + n0, kLatent, sw, tid);
   __syncthreads();
 
   if (n0 == 0) {
-    for (int i = tid; i < kRows * kRope / 8; i += kAbsorbThreads) {
+#pragma unroll
+    for (int it = 0; it < kRopeIters; ++it) {
+      const int i = tid + it * kAbsorbThreads;
       const int b = b0 + i / (kRope / 8), q = i % (kRope / 8);
-      if (b < batch)
+      if (i < kRows * kRope / 8 && b < batch)
         *reinterpret_cast<a_u32x4_t*>(c + (size_t(b) * heads + h) * kOut + kLatent + 8 * q) =
-            *reinterpret_cast<const a_u32x4_t*>(rope + (size_t(b) * heads + h) * kRope + 8 * q);
+            rv[it];
     }
   }
   if (bt >= batch) return;  // no rows in this wave's tiles
