@@ -111,3 +111,14 @@ def test_r1tp8_multi_token_full(orc, q_len):
     out, lse = to_np(*run_gpu(wl, 0))
     ref_out, ref_lse = run_oracle(orc, wl)
     compare(out, lse, ref_out, ref_lse, "bf16", f"r1tp8 q_len={q_len} (whole batch)")
+
+
+def test_fp8_multi_token_full(orc):
+    # The fp8 configuration (64 requests of 8192 tokens, 128 heads, E4M3
+    # cache) with two query tokens per request: 256 query rows per request in
+    # the many-head E4M3 kernel, in the automatic plan the benchmark times;
+    # every request against the oracle fed the dequantised cache.
+    wl = workloads.make_config("fp8", q_len=2)
+    out, lse = to_np(*run_gpu(wl, 0))
+    ref_out, ref_lse = run_oracle(orc, wl)
+    compare(out, lse, ref_out, ref_lse, "fp8", "fp8 q_len=2 (whole batch)")
